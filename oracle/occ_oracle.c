@@ -1,0 +1,598 @@
+/*
+ * occ_oracle.c -- plain, slow CPU oracle for Occult's MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This code is loaded by the tests, by the smoke
+ * check and by the benchmark's CPU-baseline leg, and by nothing else; the
+ * product path never calls it.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * Source: "Occult: Optimizing Collaborative Communication across Experts for
+ * Accelerated Parallel MoE Training and Inference" (Luo et al., ICML 2025,
+ * arXiv 2505.13345).  Each function names the passage it follows.  Floating
+ * point is fp64 unless the passage (or a stated reading) fixes the precision.
+ *
+ * Readings taken where the paper is silent or garbled (each one is listed in
+ * the design notes of the repository):
+ *   - top-k order is (logit descending, expert index ascending), on the fp32
+ *     logits; the k weights are the full softmax probabilities, not
+ *     renormalised (Eq. 2 only zeroes the entries outside the top k);
+ *   - the expert FFN is SwiGLU: E(x) = W_down (silu(W_gate x) * (W_up x));
+ *   - shared experts are dense, ungated, weight 1;
+ *   - BRIM entries equal to -1 are skipped;
+ *   - the co-activation graph C keeps its diagonal (the expert loads); P uses
+ *     the largest off-diagonal entry as its maximum and has a zero diagonal;
+ *   - CT is the mean number of distinct groups per token;
+ *   - Algorithm 1 runs on the integer counts C (the 1/|L| and 1/max factors
+ *     do not change any argmax or argmin), ties go to the lowest index, and
+ *     a group grows while it holds fewer than Ne/Nd experts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_PRUNE_OFF = 0, ORC_PRUNE_TRAVERSE = 1, ORC_PRUNE_GROUPSUM = 2 };
+enum { ORC_OK = 0, ORC_BAD = 1 };
+
+/* One element of an fp32 or bf16 array, exactly, as a double.  A bf16 value
+ * is the upper half of an fp32 bit pattern. */
+static double elem(const void *p, int dtype, size_t i)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Group (device) and position inside the group of every expert, from the
+ * placement L: Nd lists of n = Ne/Nd experts (section 3.2).  Returns ORC_BAD
+ * unless L is a permutation of 0..Ne-1. */
+static int group_table(int Ne, int Nd, const int32_t *L, int *grp, int *slot)
+{
+    if (Nd <= 0 || Ne % Nd != 0)
+        return ORC_BAD;
+    int n = Ne / Nd;
+    for (int e = 0; e < Ne; e++)
+        grp[e] = -1;
+    for (int g = 0; g < Nd; g++)
+        for (int j = 0; j < n; j++) {
+            int e = L[g * n + j];
+            if (e < 0 || e >= Ne || grp[e] != -1)
+                return ORC_BAD;
+            grp[e] = g;
+            if (slot)
+                slot[e] = j;
+        }
+    return ORC_OK;
+}
+
+/* Does expert a come before expert b in routing-score order? */
+static int ranks_before(const float *l, int a, int b)
+{
+    return l[a] > l[b] || (l[a] == l[b] && a < b);
+}
+
+/* All Ne experts in routing-score order (a plain insertion sort). */
+static void score_order(const float *l, int Ne, int *ord)
+{
+    for (int i = 0; i < Ne; i++) {
+        int e = i, q = i;
+        while (q > 0 && ranks_before(l, e, ord[q - 1])) {
+            ord[q] = ord[q - 1];
+            q--;
+        }
+        ord[q] = e;
+    }
+}
+
+/*
+ * Router, Eq. 2 (section 2.1): R(x) = Top-K(Softmax(g(x)), k).  The logits
+ * g(x) are given.  Softmax is monotone, so the top k of the probabilities are
+ * the top k of the logits.
+ *
+ * Collaboration pruning (section 3.3, routing-score-based): the token's
+ * experts are restricted to G groups, then the top k experts inside those
+ * groups are taken in descending score order.  The groups are found
+ *   TRAVERSE: by walking the token's k routed experts in descending score
+ *             and collecting their groups until G are reached;
+ *   GROUPSUM: by ranking the groups that hold at least one of the k routed
+ *             experts by the fp32 sum (taken in top-k order) of those
+ *             experts' logits, ties to the lower group, and keeping G.
+ * Weights stay the full-softmax probabilities.
+ *
+ * ids[t*k + j] is the j-th chosen expert, w the matching probability.
+ */
+int orc_route(int T, int Ne, int k, const float *logits, int Nd, const int32_t *L,
+              int prune_rule, int G, int32_t *ids, double *w)
+{
+    if (T < 0 || k < 1 || k > Ne)
+        return ORC_BAD;
+    int *grp = malloc(sizeof(int) * Ne), *ord = malloc(sizeof(int) * Ne);
+    int *chosen = malloc(sizeof(int) * Nd), *elig = malloc(sizeof(int) * Nd);
+    float *score = malloc(sizeof(float) * Nd);
+    int rc = group_table(Ne, Nd, L, grp, NULL);
+    int prune = prune_rule != ORC_PRUNE_OFF && G < Nd;
+    if (prune && (G < 1 || G * (Ne / Nd) < k))
+        rc = ORC_BAD;
+    for (int t = 0; t < T && rc == ORC_OK; t++) {
+        const float *l = logits + (size_t)t * Ne;
+        score_order(l, Ne, ord);
+
+        double m = l[ord[0]], s = 0.0;
+        for (int e = 0; e < Ne; e++)
+            s += exp((double)l[e] - m);
+
+        for (int g = 0; g < Nd; g++)
+            chosen[g] = !prune;
+        if (prune && prune_rule == ORC_PRUNE_TRAVERSE) {
+            int have = 0;
+            for (int j = 0; j < k && have < G; j++) {
+                int g = grp[ord[j]];
+                if (!chosen[g]) {
+                    chosen[g] = 1;
+                    have++;
+                }
+            }
+        } else if (prune && prune_rule == ORC_PRUNE_GROUPSUM) {
+            for (int g = 0; g < Nd; g++) {
+                score[g] = 0.0f;
+                elig[g] = 0;
+            }
+            for (int j = 0; j < k; j++) {
+                int g = grp[ord[j]];
+                score[g] = score[g] + l[ord[j]];
+                elig[g] = 1;
+            }
+            for (int r = 0; r < G; r++) {
+                int best = -1;
+                for (int g = 0; g < Nd; g++)
+                    if (elig[g] && !chosen[g] && (best < 0 || score[g] > score[best]))
+                        best = g;
+                if (best < 0)
+                    break;
+                chosen[best] = 1;
+            }
+        } else if (prune) {
+            rc = ORC_BAD;
+        }
+
+        int j = 0;
+        for (int q = 0; q < Ne && j < k; q++) {
+            int e = ord[q];
+            if (!chosen[grp[e]])
+                continue;
+            ids[(size_t)t * k + j] = e;
+            w[(size_t)t * k + j] = exp((double)l[e] - m) / s;
+            j++;
+        }
+        if (j != k)
+            rc = ORC_BAD;
+    }
+    free(grp); free(ord); free(chosen); free(elig); free(score);
+    return rc;
+}
+
+/* Does token t route to an expert kept on group g? */
+static int token_uses_group(const int32_t *ids_t, int k, const int *grp, int g)
+{
+    for (int j = 0; j < k; j++)
+        if (grp[ids_t[j]] == g)
+            return 1;
+    return 0;
+}
+
+/*
+ * BRIM_0, Algorithm 3 (appendix A.2): one counter, devices outer, tokens
+ * inner; entry [g, t] is the SFD row holding token t's replica for group g,
+ * or -1.  sfd_off[g] is the counter when row g starts; sfd_off[Nd] = N_sfd.
+ */
+int orc_brim0(int T, int k, const int32_t *ids, int Ne, int Nd, const int32_t *L,
+              int32_t *brim0, int64_t *sfd_off)
+{
+    int *grp = malloc(sizeof(int) * Ne);
+    int rc = group_table(Ne, Nd, L, grp, NULL);
+    int64_t ctr = 0;
+    for (int g = 0; g < Nd && rc == ORC_OK; g++) {
+        sfd_off[g] = ctr;
+        for (int t = 0; t < T; t++)
+            brim0[(size_t)g * T + t] =
+                token_uses_group(ids + (size_t)t * k, k, grp, g) ? (int32_t)ctr++ : -1;
+    }
+    sfd_off[Nd] = ctr;
+    free(grp);
+    return rc;
+}
+
+/*
+ * BRIM_1, Algorithm 5 (appendix A.2), built per group g (each device builds
+ * its own): the group's SFD tokens are t' = 0..N_g-1 in SFD order; a counter
+ * that restarts for each group runs over local experts outer (placement
+ * order) and SFD tokens inner; entry [j, t'] is the local EPD row of
+ * (t', L[g][j]), or -1.
+ *
+ * brim1 holds group g's N_g-wide block at offset n * sfd_off[g].  Also
+ * written, as a condensed form of the same matrix: epd_off (Ne+1, in
+ * placement order) where the global EPD rows of position g*n+j start (the
+ * groups' EPD blocks laid end to end), and for each EPD row its SFD row
+ * (epd_src) and routing weight (epd_w).
+ */
+int orc_brim1(int T, int k, const int32_t *ids, const double *w, int Ne, int Nd,
+              const int32_t *L, const int32_t *brim0, const int64_t *sfd_off,
+              int32_t *brim1, int64_t *epd_off, int64_t *epd_src, double *epd_w)
+{
+    int *grp = malloc(sizeof(int) * Ne);
+    int rc = group_table(Ne, Nd, L, grp, NULL);
+    int n = Ne / Nd;
+    int64_t glob = 0;
+    for (int g = 0; g < Nd && rc == ORC_OK; g++) {
+        int64_t Ng = sfd_off[g + 1] - sfd_off[g];
+        int64_t *tok = malloc(sizeof(int64_t) * (Ng > 0 ? Ng : 1));
+        for (int t = 0; t < T; t++) {
+            int32_t r = brim0[(size_t)g * T + t];
+            if (r >= 0)
+                tok[r - sfd_off[g]] = t;
+        }
+        int32_t *B = brim1 + (size_t)n * sfd_off[g];
+        int64_t ctr = 0;
+        for (int j = 0; j < n; j++) {
+            int e = L[g * n + j];
+            epd_off[g * n + j] = glob + ctr;
+            for (int64_t tp = 0; tp < Ng; tp++) {
+                const int32_t *ids_t = ids + (size_t)tok[tp] * k;
+                int jj = -1;
+                for (int q = 0; q < k; q++)
+                    if (ids_t[q] == e)
+                        jj = q;
+                if (jj < 0) {
+                    B[(size_t)j * Ng + tp] = -1;
+                    continue;
+                }
+                B[(size_t)j * Ng + tp] = (int32_t)ctr;
+                epd_src[glob + ctr] = sfd_off[g] + tp;
+                epd_w[glob + ctr] = w[(size_t)tok[tp] * k + jj];
+                ctr++;
+            }
+        }
+        glob += ctr;
+        free(tok);
+    }
+    epd_off[Ne] = glob;
+    free(grp);
+    return rc;
+}
+
+/* SwiGLU hidden state of one expert for one token, in fp64:
+ * h[f] = silu(W_gate[f,:] . x) * (W_up[f,:] . x), silu(z) = z / (1 + e^-z).
+ * base indexes the expert's (F x d) matrices inside Wg and Wu. */
+static void swiglu_hidden(const double *x, const void *Wg, const void *Wu, int dtype,
+                          size_t base, int F, int d, double *h)
+{
+    for (int f = 0; f < F; f++) {
+        double g = 0.0, u = 0.0;
+        for (int c = 0; c < d; c++) {
+            g += elem(Wg, dtype, base + (size_t)f * d + c) * x[c];
+            u += elem(Wu, dtype, base + (size_t)f * d + c) * x[c];
+        }
+        h[f] = g / (1.0 + exp(-g)) * u;
+    }
+}
+
+/* out += scale * (W_down h); base indexes the expert's (d x F) matrix. */
+static void down_add(const double *h, const void *Wd, int dtype, size_t base, int F, int d,
+                     double scale, double *out)
+{
+    for (int c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int f = 0; f < F; f++)
+            s += elem(Wd, dtype, base + (size_t)c * F + f) * h[f];
+        out[c] += scale * s;
+    }
+}
+
+/* Shared experts, added with weight 1 (a reading: the paper names them only
+ * in section 5, for DeepSeek-MoE). */
+static void shared_add(const double *x, int n_sh, int F_sh, int d, int dtype, const void *Wsg,
+                       const void *Wsu, const void *Wsd, double *h, double *out)
+{
+    for (int s = 0; s < n_sh; s++) {
+        swiglu_hidden(x, Wsg, Wsu, dtype, (size_t)s * F_sh * d, F_sh, d, h);
+        down_add(h, Wsd, dtype, (size_t)s * d * F_sh, F_sh, d, 1.0, out);
+    }
+}
+
+/*
+ * Layer output, Eq. 1 (section 2.1): MoE(x) = sum_i R(x)_i E_i(x), the sum
+ * running over the k routed experts of the token (the other entries of R are
+ * zero), plus the shared experts.  One row per requested token, in fp64.
+ */
+int orc_moe_rows(int nrows, const int64_t *rows, int d, int k, int F, int n_sh, int F_sh,
+                 int dtype, const void *x, const int32_t *ids, const double *w, const void *Wg,
+                 const void *Wu, const void *Wd, const void *Wsg, const void *Wsu,
+                 const void *Wsd, int nthreads, double *y)
+{
+    int Fmax = F > F_sh ? F : F_sh;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *xt = malloc(sizeof(double) * d), *h = malloc(sizeof(double) * Fmax);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int i = 0; i < nrows; i++) {
+            int64_t t = rows[i];
+            double *yt = y + (size_t)i * d;
+            for (int c = 0; c < d; c++) {
+                xt[c] = elem(x, dtype, (size_t)t * d + c);
+                yt[c] = 0.0;
+            }
+            for (int j = 0; j < k; j++) {
+                int e = ids[(size_t)t * k + j];
+                swiglu_hidden(xt, Wg, Wu, dtype, (size_t)e * F * d, F, d, h);
+                down_add(h, Wd, dtype, (size_t)e * d * F, F, d, w[(size_t)t * k + j], yt);
+            }
+            shared_add(xt, n_sh, F_sh, d, dtype, Wsg, Wsu, Wsd, h, yt);
+        }
+        free(xt);
+        free(h);
+    }
+    return ORC_OK;
+}
+
+/* Number of threads orc_moe_rows runs with when asked for nthreads. */
+int orc_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    int used = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+    }
+    return used;
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * The Occult pipeline of Algorithm 2 (appendix A.1) in fp64, on one host,
+ * the Nd groups standing in for the devices and the two all-to-alls being
+ * identities:
+ *   Dispatch (Alg. 4): x_sfd[BRIM_0[g, t]] = x[t];
+ *   SMM scattering (Alg. 6) and weight modulation (Alg. 7): for every
+ *     BRIM_1 entry v >= 0 of group g at (j, t'), x_epd[v] = w * h where h is
+ *     the SwiGLU hidden state of x_sfd row t' for expert L[g][j] -- the
+ *     routing weight scales the hidden state after the activation;
+ *   SMM merging (Alg. 8): sfd_out[t'] += W_down x_epd[v], zero-initialised;
+ *   Combine (Alg. 9): y[t] = sum over g of sfd_out[BRIM_0[g, t]].
+ * Shared experts are added at the end.  Used on small inputs to check that
+ * the two-stage split reproduces Eq. 1.
+ */
+int orc_occult_replay(int T, int d, int Ne, int k, int Nd, int F, int n_sh, int F_sh, int dtype,
+                      const void *x, const int32_t *ids, const double *w, const int32_t *L,
+                      const void *Wg, const void *Wu, const void *Wd, const void *Wsg,
+                      const void *Wsu, const void *Wsd, double *y)
+{
+    int n = Ne / Nd;
+    int32_t *brim0 = malloc(sizeof(int32_t) * (size_t)Nd * T);
+    int64_t *sfd_off = malloc(sizeof(int64_t) * (Nd + 1));
+    int rc = orc_brim0(T, k, ids, Ne, Nd, L, brim0, sfd_off);
+    if (rc != ORC_OK) {
+        free(brim0); free(sfd_off);
+        return rc;
+    }
+    int64_t N_sfd = sfd_off[Nd], N_epd = (int64_t)T * k;
+    int32_t *brim1 = malloc(sizeof(int32_t) * (size_t)(n * N_sfd + 1));
+    int64_t *epd_off = malloc(sizeof(int64_t) * (Ne + 1));
+    int64_t *epd_src = malloc(sizeof(int64_t) * (N_epd + 1));
+    double *epd_w = malloc(sizeof(double) * (N_epd + 1));
+    rc = orc_brim1(T, k, ids, w, Ne, Nd, L, brim0, sfd_off, brim1, epd_off, epd_src, epd_w);
+
+    double *x_sfd = calloc((size_t)(N_sfd + 1) * d, sizeof(double));
+    double *sfd_out = calloc((size_t)(N_sfd + 1) * d, sizeof(double));
+    double *xt = malloc(sizeof(double) * d);
+    int Fmax = F > F_sh ? F : F_sh;
+    double *h = malloc(sizeof(double) * Fmax);
+
+    for (int g = 0; g < Nd; g++)
+        for (int t = 0; t < T; t++) {
+            int32_t r = brim0[(size_t)g * T + t];
+            if (r >= 0)
+                for (int c = 0; c < d; c++)
+                    x_sfd[(size_t)r * d + c] = elem(x, dtype, (size_t)t * d + c);
+        }
+
+    for (int g = 0; g < Nd && rc == ORC_OK; g++) {
+        int64_t Ng = sfd_off[g + 1] - sfd_off[g];
+        int64_t *tok = malloc(sizeof(int64_t) * (Ng > 0 ? Ng : 1));
+        for (int t = 0; t < T; t++) {
+            int32_t r = brim0[(size_t)g * T + t];
+            if (r >= 0)
+                tok[r - sfd_off[g]] = t;
+        }
+        const int32_t *B = brim1 + (size_t)n * sfd_off[g];
+        int64_t n_loc = 0;
+        for (int j = 0; j < n; j++)
+            for (int64_t tp = 0; tp < Ng; tp++)
+                n_loc += B[(size_t)j * Ng + tp] >= 0;
+        double *x_epd = malloc(sizeof(double) * (size_t)(n_loc + 1) * F);
+        for (int j = 0; j < n; j++) {
+            int e = L[g * n + j];
+            for (int64_t tp = 0; tp < Ng; tp++) {
+                int32_t v = B[(size_t)j * Ng + tp];
+                if (v < 0)
+                    continue;
+                const int32_t *ids_t = ids + (size_t)tok[tp] * k;
+                double wt = 0.0;
+                for (int q = 0; q < k; q++)
+                    if (ids_t[q] == e)
+                        wt = w[(size_t)tok[tp] * k + q];
+                swiglu_hidden(x_sfd + (size_t)(sfd_off[g] + tp) * d, Wg, Wu, dtype,
+                              (size_t)e * F * d, F, d, h);
+                for (int f = 0; f < F; f++)
+                    x_epd[(size_t)v * F + f] = wt * h[f];
+            }
+        }
+        for (int j = 0; j < n; j++) {
+            int e = L[g * n + j];
+            for (int64_t tp = 0; tp < Ng; tp++) {
+                int32_t v = B[(size_t)j * Ng + tp];
+                if (v >= 0)
+                    down_add(x_epd + (size_t)v * F, Wd, dtype, (size_t)e * d * F, F, d, 1.0,
+                             sfd_out + (size_t)(sfd_off[g] + tp) * d);
+            }
+        }
+        free(x_epd);
+        free(tok);
+    }
+
+    for (int t = 0; t < T && rc == ORC_OK; t++) {
+        double *yt = y + (size_t)t * d;
+        for (int c = 0; c < d; c++)
+            yt[c] = 0.0;
+        for (int g = 0; g < Nd; g++) {
+            int32_t r = brim0[(size_t)g * T + t];
+            if (r >= 0)
+                for (int c = 0; c < d; c++)
+                    yt[c] += sfd_out[(size_t)r * d + c];
+        }
+        for (int c = 0; c < d; c++)
+            xt[c] = elem(x, dtype, (size_t)t * d + c);
+        shared_add(xt, n_sh, F_sh, d, dtype, Wsg, Wsu, Wsd, h, yt);
+    }
+    free(brim0); free(sfd_off); free(brim1); free(epd_off); free(epd_src); free(epd_w);
+    free(x_sfd); free(sfd_out); free(xt); free(h);
+    return rc;
+}
+
+/*
+ * Co-activation statistics.  Eq. 3 (section 2.1): C[i][j] counts the tokens
+ * of the batch that activate both i and j, over every ordered pair of the
+ * token's k experts (so C[i][i] is expert i's load).  Eq. 4: P = C / max C,
+ * the max taken over i != j, P[i][i] = 0, one fp32 division per entry
+ * (P = 0 when no pair exists).  Section 2.2: CT is the mean number of
+ * replicas per token, i.e. distinct groups among the token's experts; n_sfd
+ * is their sum.  intra is the share of off-diagonal co-activations whose two
+ * experts sit in one group (the Intra / Inter row of Table 1).
+ */
+int orc_coact(int T, int k, const int32_t *ids, int Ne, int Nd, const int32_t *L, int64_t *C,
+              float *P, int64_t *n_sfd, double *ct, double *intra)
+{
+    int *grp = malloc(sizeof(int) * Ne);
+    int rc = group_table(Ne, Nd, L, grp, NULL);
+    memset(C, 0, sizeof(int64_t) * (size_t)Ne * Ne);
+    int64_t nsfd = 0;
+    for (int t = 0; t < T && rc == ORC_OK; t++) {
+        const int32_t *ids_t = ids + (size_t)t * k;
+        for (int a = 0; a < k; a++)
+            for (int b = 0; b < k; b++)
+                C[(size_t)ids_t[a] * Ne + ids_t[b]] += 1;
+        for (int g = 0; g < Nd; g++)
+            nsfd += token_uses_group(ids_t, k, grp, g);
+    }
+    int64_t mx = 0, same = 0, all = 0;
+    for (int i = 0; i < Ne; i++)
+        for (int j = 0; j < Ne; j++)
+            if (i != j) {
+                int64_t c = C[(size_t)i * Ne + j];
+                if (c > mx)
+                    mx = c;
+                all += c;
+                if (grp[i] == grp[j])
+                    same += c;
+            }
+    for (int i = 0; i < Ne; i++)
+        for (int j = 0; j < Ne; j++)
+            P[(size_t)i * Ne + j] =
+                (i == j || mx == 0) ? 0.0f : (float)C[(size_t)i * Ne + j] / (float)mx;
+    *n_sfd = nsfd;
+    *ct = T > 0 ? (double)nsfd / (double)T : 0.0;
+    *intra = all > 0 ? (double)same / (double)all : 0.0;
+    free(grp);
+    return rc;
+}
+
+/*
+ * Expert placement rescheduling, Algorithm 1 (section 3.2), a greedy
+ * clustering in the manner of farthest point sampling.  Group 0 is seeded
+ * with the most collaborative pair (i < j); every later group with the
+ * unused expert least collaborative with all placed experts; each group then
+ * grows, while it holds fewer than n experts, by the unused expert most
+ * collaborative with the group's members.  With n = 1 there is no pair and
+ * group 0 starts empty (its first pick, over all-zero scores, is expert 0).
+ * L receives Nd lists of n experts in push order.
+ */
+int orc_placement(int Ne, int Nd, const int64_t *C, int32_t *L)
+{
+    if (Nd <= 0 || Ne % Nd != 0)
+        return ORC_BAD;
+    int n = Ne / Nd;
+    int *used = calloc(Ne, sizeof(int));
+    for (int g = 0; g < Nd; g++) {
+        int len = 0;
+        int32_t *Lg = L + g * n;
+        if (g == 0 && n >= 2) {
+            int bi = -1, bj = -1;
+            for (int i = 0; i < Ne; i++)
+                for (int j = i + 1; j < Ne; j++)
+                    if (bi < 0 || C[(size_t)i * Ne + j] > C[(size_t)bi * Ne + bj]) {
+                        bi = i;
+                        bj = j;
+                    }
+            Lg[len++] = bi;
+            Lg[len++] = bj;
+            used[bi] = used[bj] = 1;
+
+        } else if (g > 0) {
+            int best = -1;
+            int64_t bsum = 0;
+            for (int e = 0; e < Ne; e++) {
+                if (used[e])
+                    continue;
+                int64_t s = 0;
+                for (int gg = 0; gg < g; gg++)
+                    for (int q = 0; q < n; q++)
+                        s += C[(size_t)L[gg * n + q] * Ne + e];
+                if (best < 0 || s < bsum) {
+                    best = e;
+                    bsum = s;
+                }
+            }
+            Lg[len++] = best;
+            used[best] = 1;
+
+        }
+        while (len < n) {
+            int best = -1;
+            int64_t bsum = 0;
+            for (int e = 0; e < Ne; e++) {
+                if (used[e])
+                    continue;
+                int64_t s = 0;
+                for (int q = 0; q < len; q++)
+                    s += C[(size_t)Lg[q] * Ne + e];
+                if (best < 0 || s > bsum) {
+                    best = e;
+                    bsum = s;
+                }
+            }
+            Lg[len++] = best;
+            used[best] = 1;
+
+        }
+    }
+    free(used);
+    return ORC_OK;
+}
