@@ -1,0 +1,206 @@
+"""Benchmark of the Occult MoE layer on one MI355X.
+
+One step = one occ_moe_forward call (route -> BRIM -> dispatch -> SwiGLU
+grouped GEMM -> intra-group merge -> cross-group combine) over one batch of
+the OLMoE-shaped workload (T = 8192 tokens, d = 2048, 64 experts, top-8,
+8 groups, F = 1024, bf16), inputs resident in HBM.  The expert placement is
+the rescheduled one (Algorithm 1 on the batch's co-activation counts, built
+with the library's own calls, untimed); the contiguous placement is timed
+too and reported beside it.
+
+Prints one JSON line.  The roofline entry is for the dominant kernel (the
+SwiGLU up-projection GEMM): algorithmic FLOPs per launch over its average
+duration, measured with HIP events recorded around it on the layer's stream
+during the timed steps.  The CPU baseline times the oracle on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU + % of bf16 MFMA / HBM roofline; CT"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="olmoe_t8192")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-contiguous", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "expert groups stand in for devices on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from expert_token_routing_amd import occ, profiling, synth, workloads as W
+
+    wl = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {wl.name}: generating inputs")
+    inp = synth.make_all(wl)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    desc = occ.desc_of(wl)
+    ws = occ.alloc_workspace(desc, dev)
+    dt = synth.torch_dtype(wl)
+    y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # --- placement (offline step, untimed): Algorithm 1 on this batch's counts
+    L_contig = inp["placement"]
+    ids = torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev)
+    wts = torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev)
+    occ.occ_route(desc, g["logits"], L_contig, ids, wts)
+    C = torch.empty(wl.Ne, wl.Ne, dtype=torch.int32, device=dev)
+    P = torch.empty(wl.Ne, wl.Ne, dtype=torch.float32, device=dev)
+    n_sfd = torch.empty(1, dtype=torch.int64, device=dev)
+    ct = torch.empty(1, dtype=torch.float64, device=dev)
+    intra = torch.empty(1, dtype=torch.float64, device=dev)
+    occ.occ_coactivation_stats(desc, ids, L_contig, C, P, n_sfd, ct, intra)
+    torch.cuda.synchronize()
+    ct_contig, intra_contig = float(ct.item()), float(intra.item())
+    L_alg1 = occ.occ_place_experts(C.cpu().numpy(), wl.Nd)
+    occ.occ_coactivation_stats(desc, ids, L_alg1, C, P, n_sfd, ct, intra)
+    torch.cuda.synchronize()
+    ct_alg1, nsfd_alg1, intra_alg1 = float(ct.item()), int(n_sfd.item()), float(intra.item())
+
+    def run(L, steps, events=None):
+        for i in range(steps):
+            ev = events[i].handles if events is not None else None
+            occ.occ_moe_forward(desc, g["x"], g["logits"], L, g["w_gate"], g["w_up"], g["w_down"],
+                                g["ws_gate"], g["ws_up"], g["ws_down"], y, ws, stage_events=ev)
+
+    def timed(L, label):
+        log(f"[bench] {label}: warmup {args.warmup}")
+        run(L, args.warmup)
+        torch.cuda.synchronize()
+        events = [occ.StageEvents() for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        run(L, args.steps, events)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = start.elapsed_time(stop) / args.steps
+        stages = np.array([e.elapsed_ms() for e in events])  # steps x stages
+        for e in events:
+            e.close()
+        log(f"[bench] {label}: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+        return ms, stages.mean(0)
+
+    ms, stages = timed(L_alg1, "alg1 placement")
+    tokens_per_s = wl.T / (ms / 1e3)
+    res_contig = None
+    if not args.no_contiguous:
+        ms_c, stages_c = timed(L_contig, "contiguous placement")
+        res_contig = {"value": wl.T / (ms_c / 1e3), "ms_per_step": ms_c, "ct": ct_contig,
+                      "intra": intra_contig,
+                      "stages_ms": {s: float(v) for s, v in zip(occ.STAGES, stages_c)}}
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # --- roofline of the dominant kernel: the up-projection grouped GEMM
+    up_ms = float(stages[occ.STAGES.index("gemm_up")])
+    flops_up = 2.0 * wl.T * wl.k * wl.d * 2 * wl.F
+    achieved = flops_up / (up_ms / 1e3) / 1e12
+    traffic = profiling.traffic_bytes("k_gemm_up", wl.name, "gemm_bf16.hip")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "k_gemm_up", "avg_ms": round(up_ms, 5),
+                "flops_per_launch": flops_up}
+
+    # --- CPU baseline: the oracle on a bounded sample of this workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, L_alg1, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == W.DTYPE_BF16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "Ne": wl.Ne, "k": wl.k,
+                   "Nd": wl.Nd, "F": wl.F, "placement": "alg1"},
+        "ct": ct_alg1, "n_sfd": nsfd_alg1, "intra": intra_alg1,
+        "ct_bounds": [-(-wl.k * wl.Nd // wl.Ne), min(wl.k, wl.Nd)],
+        "roofline": roofline, "cpu_baseline": cpu,
+        "stages_ms": {s: round(float(v), 5) for s, v in zip(occ.STAGES, stages)},
+        "contiguous": res_contig,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, placement, seconds):
+    """Time the oracle (route, BRIM, stats on the full batch; Eq. 1 rows on a
+    sample sized to about `seconds`) and scale to tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from expert_token_routing_amd import synth
+
+    log("[bench] cpu baseline: oracle route/BRIM/stats on the full batch")
+    t0 = time.perf_counter()
+    ids, w = oracle.route(inp["logits"].numpy(), wl.k, placement, wl.prune_rule, wl.prune_groups)
+    oracle.brim1(ids, w, wl.Ne, placement)
+    oracle.coact(ids, wl.Ne, placement)
+    t_index = time.perf_counter() - t0
+
+    bits = lambda t: None if t is None else t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    args = (bits(inp["x"]), ids, w, bits(inp["w_gate"]), bits(inp["w_up"]), bits(inp["w_down"]),
+            bits(inp["ws_gate"]), bits(inp["ws_up"]), bits(inp["ws_down"]))
+    threads = oracle.threads(0)
+    probe = synth.sample_rows(wl.T, max(threads, 4), seed=5)
+    t0 = time.perf_counter()
+    oracle.moe_rows(probe, *args)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(wl.T, max(len(probe), seconds / max(per_row, 1e-9))))
+    rows = synth.sample_rows(wl.T, n, seed=6)
+    log(f"[bench] cpu baseline: Eq. 1 on {len(rows)} sampled rows with {threads} threads")
+    t0 = time.perf_counter()
+    oracle.moe_rows(rows, *args)
+    t_rows = time.perf_counter() - t0
+    per_token = t_rows / len(rows) + t_index / wl.T
+    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"Eq. 1 output for {len(rows)} of {wl.T} tokens (seeded sample) in "
+                       f"{t_rows:.1f} s plus route/BRIM/co-activation on all {wl.T} tokens in "
+                       f"{t_index:.2f} s, fp64, {threads} threads")}
+
+
+if __name__ == "__main__":
+    main()

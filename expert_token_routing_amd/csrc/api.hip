@@ -1,0 +1,430 @@
+// C ABI of the Occult MoE-layer library: argument checks, workspace layout,
+// and the stage sequence of the layer (declarations and contracts in occ.h).
+#include <algorithm>
+#include <vector>
+
+#include "launch.h"
+
+#pragma GCC visibility push(default)
+#include "occ.h"
+#pragma GCC visibility pop
+
+using namespace occ;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+size_t elem_bytes(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? 2 : 4; }
+int tile_rows(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? kGemmBmBf16 : kGemmBmF32; }
+
+// Byte offsets of every buffer inside the workspace.  Sized for the worst
+// case N_sfd = T * min(k, Nd), so no data-dependent size is read back.
+struct Layout {
+    size_t ids, w, brim0, sfd_off, epd_off, tile_off, chunk_cnt, chunk_base, epd_src, epd_w,
+        tok_epd, brim1, brim_end, x_sfd, epd, sfd_out, h_sh, y_sh, total;
+};
+
+Layout layout(const occ_layer_desc &D) {
+    const size_t T = D.T, k = D.k, Nd = D.Nd, Ne = D.Ne, d = D.d, F = D.F, es = elem_bytes(D);
+    const size_t n = Ne / Nd, nsfd_max = T * std::min(k, Nd), nepd = T * k;
+    const size_t nchunks = (T + kBrimChunk - 1) / kBrimChunk, nb = Nd + Ne;
+    Layout L{};
+    size_t o = 0;
+    auto take = [&o](size_t bytes) {
+        const size_t r = o;
+        o = align_up(o + std::max<size_t>(bytes, 1));
+        return r;
+    };
+    L.ids = take(nepd * 4);
+    L.w = take(nepd * 4);
+    L.brim0 = take(Nd * T * 4);
+    L.sfd_off = take((Nd + 1) * 4);
+    L.epd_off = take((Ne + 1) * 4);
+    L.tile_off = take((Ne + 1) * 4);
+    L.chunk_cnt = take(nchunks * nb * 4);
+    L.chunk_base = take(nchunks * nb * 4);
+    L.epd_src = take(nepd * 4);
+    L.epd_w = take(nepd * 4);
+    L.tok_epd = take(nepd * 4);
+    L.brim1 = take(n * nsfd_max * 4);
+    L.brim_end = o;
+    L.x_sfd = take(nsfd_max * d * es);
+    L.epd = take(nepd * F * es);
+    L.sfd_out = take(nsfd_max * d * 4);
+    if (D.n_shared > 0) {
+        L.h_sh = take(T * static_cast<size_t>(D.n_shared) * D.F_shared * es);
+        L.y_sh = take(T * d * 4);
+    }
+    L.total = o;
+    return L;
+}
+
+occ_status check_desc(const occ_layer_desc *D) {
+    if (!D) return OCC_ERR_INVALID_ARG;
+    if (D->T < 1 || D->d < 1 || D->Ne < 1 || D->k < 1 || D->Nd < 1 || D->F < 1)
+        return OCC_ERR_INVALID_ARG;
+    if (D->k > D->Ne || D->Ne % D->Nd != 0) return OCC_ERR_INVALID_ARG;
+    if (D->n_shared < 0 || (D->n_shared > 0 && D->F_shared < 1)) return OCC_ERR_INVALID_ARG;
+    if (D->dtype != OCC_F32 && D->dtype != OCC_BF16) return OCC_ERR_INVALID_ARG;
+    if (D->prune_rule < OCC_PRUNE_OFF || D->prune_rule > OCC_PRUNE_GROUPSUM)
+        return OCC_ERR_INVALID_ARG;
+    if (D->prune_rule != OCC_PRUNE_OFF &&
+        (D->prune_groups < 1 ||
+         static_cast<int64_t>(D->prune_groups) * (D->Ne / D->Nd) < D->k))
+        return OCC_ERR_INVALID_ARG;
+    if (D->flags != 0) return OCC_ERR_INVALID_ARG;
+    if (D->Ne > kMaxNe || D->Nd > kMaxNd || D->k > kMaxK) return OCC_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(D->T) * D->k >= (1ll << 31) ||
+        static_cast<int64_t>(D->T) * D->Nd >= (1ll << 31))
+        return OCC_ERR_UNSUPPORTED;
+    const int mult = D->dtype == OCC_BF16 ? 64 : 16;
+    if (D->d % mult || D->F % mult || (D->n_shared > 0 && D->F_shared % mult))
+        return OCC_ERR_UNSUPPORTED;
+    if (D->d > (D->dtype == OCC_BF16 ? 8192 : 4096)) return OCC_ERR_UNSUPPORTED;
+    return OCC_OK;
+}
+
+occ_status make_tab(const occ_layer_desc &D, const int32_t *L, PlaceTab *tab) {
+    if (!L) return OCC_ERR_INVALID_ARG;
+    const int n = D.Ne / D.Nd;
+    bool seen[kMaxNe] = {};
+    *tab = PlaceTab{};
+    for (int g = 0; g < D.Nd; g++)
+        for (int j = 0; j < n; j++) {
+            const int e = L[g * n + j];
+            if (e < 0 || e >= D.Ne || seen[e]) return OCC_ERR_INVALID_ARG;
+            seen[e] = true;
+            tab->grp[e] = static_cast<uint8_t>(g);
+            tab->slot[e] = static_cast<uint8_t>(j);
+            tab->expert[g * n + j] = static_cast<uint8_t>(e);
+        }
+    tab->Ne = D.Ne;
+    tab->Nd = D.Nd;
+    tab->n = n;
+    return OCC_OK;
+}
+
+occ_status check_ws(const occ_layer_desc &D, const void *ws, size_t ws_bytes, size_t need) {
+    (void)D;
+    if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign != 0 || ws_bytes < need)
+        return OCC_ERR_WORKSPACE;
+    return OCC_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+occ_brim brim_view(void *ws, const Layout &L) {
+    occ_brim b;
+    b.brim0 = at<int32_t>(ws, L.brim0);
+    b.sfd_off = at<int32_t>(ws, L.sfd_off);
+    b.epd_off = at<int32_t>(ws, L.epd_off);
+    b.epd_src = at<int32_t>(ws, L.epd_src);
+    b.epd_w = at<float>(ws, L.epd_w);
+    b.tok_epd = at<int32_t>(ws, L.tok_epd);
+    b.brim1 = at<int32_t>(ws, L.brim1);
+    b.tile_off = at<int32_t>(ws, L.tile_off);
+    return b;
+}
+
+BrimBufs brim_bufs(void *ws, const Layout &L) {
+    BrimBufs b;
+    b.brim0 = at<int32_t>(ws, L.brim0);
+    b.sfd_off = at<int32_t>(ws, L.sfd_off);
+    b.epd_off = at<int32_t>(ws, L.epd_off);
+    b.tile_off = at<int32_t>(ws, L.tile_off);
+    b.epd_src = at<int32_t>(ws, L.epd_src);
+    b.tok_epd = at<int32_t>(ws, L.tok_epd);
+    b.brim1 = at<int32_t>(ws, L.brim1);
+    b.epd_w = at<float>(ws, L.epd_w);
+    b.chunk_cnt = at<int32_t>(ws, L.chunk_cnt);
+    b.chunk_base = at<int32_t>(ws, L.chunk_base);
+    return b;
+}
+
+occ_status hip_status(hipError_t e) { return e == hipSuccess ? OCC_OK : OCC_ERR_HIP; }
+
+#define OCC_TRY(expr)                              \
+    do {                                           \
+        const occ_status st_ = (expr);             \
+        if (st_ != OCC_OK) return st_;             \
+    } while (0)
+
+#define OCC_HIP(expr) OCC_TRY(hip_status(expr))
+
+}  // namespace
+
+extern "C" {
+
+const char *occ_status_string(occ_status s) {
+    switch (s) {
+        case OCC_OK: return "OCC_OK";
+        case OCC_ERR_INVALID_ARG: return "OCC_ERR_INVALID_ARG";
+        case OCC_ERR_UNSUPPORTED: return "OCC_ERR_UNSUPPORTED";
+        case OCC_ERR_WORKSPACE: return "OCC_ERR_WORKSPACE";
+        case OCC_ERR_HIP: return "OCC_ERR_HIP";
+    }
+    return "OCC_ERR_UNKNOWN";
+}
+
+occ_status occ_workspace_size(const occ_layer_desc *desc, size_t *bytes_host) {
+    OCC_TRY(check_desc(desc));
+    if (!bytes_host) return OCC_ERR_INVALID_ARG;
+    *bytes_host = layout(*desc).total;
+    return OCC_OK;
+}
+
+occ_status occ_route(const occ_layer_desc *desc, const float *logits,
+                     const int32_t *placement_host, int32_t *ids, float *w, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!logits || !ids || !w) return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(*desc, placement_host, &tab));
+    OCC_HIP(launch_route(logits, desc->T, desc->Ne, desc->k, desc->prune_rule,
+                         desc->prune_groups, tab, ids, w, static_cast<hipStream_t>(stream)));
+    return OCC_OK;
+}
+
+occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const float *w,
+                          const int32_t *placement_host, int dense_brim1, void *workspace,
+                          size_t ws_bytes, occ_brim *out_host, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!ids || !w || !out_host) return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(*desc, placement_host, &tab));
+    const Layout L = layout(*desc);
+    OCC_TRY(check_ws(*desc, workspace, ws_bytes, L.brim_end));
+    OCC_HIP(launch_brim(ids, w, desc->T, desc->k, tab, tile_rows(*desc), dense_brim1 != 0,
+                        brim_bufs(workspace, L), static_cast<hipStream_t>(stream)));
+    *out_host = brim_view(workspace, L);
+    return OCC_OK;
+}
+
+occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
+                             occ_forward_view *out_host) {
+    OCC_TRY(check_desc(desc));
+    if (!workspace || !out_host) return OCC_ERR_INVALID_ARG;
+    const Layout L = layout(*desc);
+    occ_forward_view v;
+    v.ids = at<int32_t>(workspace, L.ids);
+    v.w = at<float>(workspace, L.w);
+    v.brim = brim_view(workspace, L);
+    v.x_sfd = at<void>(workspace, L.x_sfd);
+    v.epd = at<void>(workspace, L.epd);
+    v.sfd_out = at<float>(workspace, L.sfd_out);
+    v.h_shared = desc->n_shared > 0 ? at<void>(workspace, L.h_sh) : nullptr;
+    v.y_shared = desc->n_shared > 0 ? at<float>(workspace, L.y_sh) : nullptr;
+    *out_host = v;
+    return OCC_OK;
+}
+
+occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const float *logits,
+                           const int32_t *placement_host, const void *w_gate, const void *w_up,
+                           const void *w_down, const void *ws_gate, const void *ws_up,
+                           const void *ws_down, void *y, void *workspace, size_t ws_bytes,
+                           void *const *stage_events, void *stream) {
+    OCC_TRY(check_desc(desc));
+    const occ_layer_desc &D = *desc;
+    if (!x || !logits || !w_gate || !w_up || !w_down || !y) return OCC_ERR_INVALID_ARG;
+    if (D.n_shared > 0 && (!ws_gate || !ws_up || !ws_down)) return OCC_ERR_INVALID_ARG;
+    if (stage_events)
+        for (int i = 0; i <= OCC_STAGE_COUNT; i++)
+            if (!stage_events[i]) return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(D, placement_host, &tab));
+    const Layout L = layout(D);
+    OCC_TRY(check_ws(D, workspace, ws_bytes, L.total));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> occ_status {
+        if (!stage_events) return OCC_OK;
+        return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s));
+    };
+    const bool bf16 = D.dtype == OCC_BF16;
+    const size_t es = elem_bytes(D);
+    const BrimBufs bb = brim_bufs(workspace, L);
+    int32_t *ids = at<int32_t>(workspace, L.ids);
+    float *w = at<float>(workspace, L.w);
+    void *x_sfd = at<void>(workspace, L.x_sfd);
+    void *epd = at<void>(workspace, L.epd);
+    float *sfd_out = at<float>(workspace, L.sfd_out);
+    float *y_sh = D.n_shared > 0 ? at<float>(workspace, L.y_sh) : nullptr;
+    const size_t T = D.T, nsfd_max = T * std::min(D.k, D.Nd);
+    const size_t bm = tile_rows(D);
+    const size_t routed_tiles = (T * D.k + bm - 1) / bm + D.Ne;
+    const size_t shared_tiles = (T + bm - 1) / bm;
+
+    OCC_TRY(mark(0));
+    // Eq. 2: router
+    OCC_HIP(launch_route(logits, D.T, D.Ne, D.k, D.prune_rule, D.prune_groups, tab, ids, w, s));
+    OCC_TRY(mark(1));
+    // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
+    OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
+    OCC_TRY(mark(2));
+    // Algorithm 4: ORI -> SFD
+    OCC_HIP(launch_dispatch(x, D.T, D.Nd, static_cast<size_t>(D.d) * es, bb.brim0, x_sfd, s));
+    OCC_TRY(mark(3));
+    // shared experts: dense SwiGLU over all T tokens, fp32 result
+    if (D.n_shared > 0) {
+        UpArgs su{};
+        su.A = x;
+        su.Wg = ws_gate;
+        su.Wu = ws_up;
+        su.out = at<void>(workspace, L.h_sh);
+        su.M = D.T;
+        su.K = D.d;
+        su.N = D.n_shared * D.F_shared;
+        su.Ne = 1;
+        su.tab = tab;
+        DownArgs sd{};
+        sd.A = su.out;
+        sd.W = ws_down;
+        sd.out = y_sh;
+        sd.M = D.T;
+        sd.K = su.N;
+        sd.N = D.d;
+        sd.Ne = 1;
+        sd.k_split = D.F_shared;
+        sd.tab = tab;
+        OCC_HIP(bf16 ? launch_gemm_up_bf16(su, shared_tiles, s) : launch_gemm_up_f32(su, shared_tiles, s));
+        OCC_HIP(bf16 ? launch_gemm_down_bf16(sd, shared_tiles, s)
+                     : launch_gemm_down_f32(sd, shared_tiles, s));
+    }
+    OCC_TRY(mark(4));
+    // Algorithms 6-7: SFD -> EPD, SwiGLU, weight modulation
+    UpArgs up{};
+    up.A = x_sfd;
+    up.a_rows = bb.epd_src;
+    up.Wg = w_gate;
+    up.Wu = w_up;
+    up.seg_off = bb.epd_off;
+    up.tile_off = bb.tile_off;
+    up.row_w = bb.epd_w;
+    up.out = epd;
+    up.M = D.T * D.k;
+    up.K = D.d;
+    up.N = D.F;
+    up.Ne = D.Ne;
+    up.tab = tab;
+    OCC_HIP(bf16 ? launch_gemm_up_bf16(up, routed_tiles, s) : launch_gemm_up_f32(up, routed_tiles, s));
+    OCC_TRY(mark(5));
+    // Algorithm 8 starts from a zero fp32 SFD tensor (only the N_sfd used rows)
+    OCC_HIP(launch_zero_rows(sfd_out, bb.sfd_off + D.Nd, nsfd_max, D.d, s));
+    OCC_TRY(mark(6));
+    // Algorithm 8: EPD -> SFD, summed inside each group in fp32
+    DownArgs dn{};
+    dn.A = epd;
+    dn.W = w_down;
+    dn.seg_off = bb.epd_off;
+    dn.tile_off = bb.tile_off;
+    dn.dst_rows = bb.epd_src;
+    dn.out = sfd_out;
+    dn.M = D.T * D.k;
+    dn.K = D.F;
+    dn.N = D.d;
+    dn.Ne = D.Ne;
+    dn.k_split = D.F;
+    dn.tab = tab;
+    OCC_HIP(bf16 ? launch_gemm_down_bf16(dn, routed_tiles, s) : launch_gemm_down_f32(dn, routed_tiles, s));
+    OCC_TRY(mark(7));
+    // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once
+    OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
+    OCC_TRY(mark(8));
+    return OCC_OK;
+}
+
+occ_status occ_coactivation_stats(const occ_layer_desc *desc, const int32_t *ids,
+                                  const int32_t *placement_host, int32_t *C, float *P,
+                                  int64_t *n_sfd, double *ct, double *intra, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!ids || !C || !P || !n_sfd || !ct || !intra) return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(*desc, placement_host, &tab));
+    OCC_HIP(launch_coact(ids, desc->T, desc->k, tab, C, P, n_sfd, ct, intra,
+                         static_cast<hipStream_t>(stream)));
+    return OCC_OK;
+}
+
+// Algorithm 1 (paper section 3.2).  The 1/|L| and 1/max C scalings of the
+// paper's scores do not change any argmax / argmin, so the integer counts are
+// used directly; each unused expert's summed collaboration with all placed
+// experts and with the current group is kept up to date as experts are
+// placed.
+occ_status occ_place_experts(const int32_t *C_host, int32_t Ne, int32_t Nd,
+                             int32_t *placement_host) {
+    if (!C_host || !placement_host || Ne < 1 || Nd < 1 || Ne % Nd != 0 || Ne > 65536)
+        return OCC_ERR_INVALID_ARG;
+    const int n = Ne / Nd;
+    std::vector<char> used(Ne, 0);
+    std::vector<int64_t> with_placed(Ne, 0), with_group(Ne, 0);
+    for (int g = 0; g < Nd; g++) {
+        std::fill(with_group.begin(), with_group.end(), 0);
+        int32_t *Lg = placement_host + static_cast<size_t>(g) * n;
+        int len = 0;
+        auto push = [&](int e) {
+            Lg[len++] = e;
+            used[e] = 1;
+            const int32_t *row = C_host + static_cast<size_t>(e) * Ne;
+            for (int q = 0; q < Ne; q++) {
+                with_placed[q] += row[q];
+                with_group[q] += row[q];
+            }
+        };
+        if (g == 0 && n >= 2) {
+            int bi = 0, bj = 1;
+            for (int i = 0; i < Ne; i++)
+                for (int j = i + 1; j < Ne; j++)
+                    if (C_host[static_cast<size_t>(i) * Ne + j] >
+                        C_host[static_cast<size_t>(bi) * Ne + bj]) {
+                        bi = i;
+                        bj = j;
+                    }
+            push(bi);
+            push(bj);
+        } else if (g > 0) {
+            int best = -1;
+            for (int e = 0; e < Ne; e++)
+                if (!used[e] && (best < 0 || with_placed[e] < with_placed[best])) best = e;
+            push(best);
+        }
+        while (len < n) {
+            int best = -1;
+            for (int e = 0; e < Ne; e++)
+                if (!used[e] && (best < 0 || with_group[e] > with_group[best])) best = e;
+            push(best);
+        }
+    }
+    return OCC_OK;
+}
+
+occ_status occ_events_create(int32_t n, void **events_host) {
+    if (n < 0 || (n > 0 && !events_host)) return OCC_ERR_INVALID_ARG;
+    for (int i = 0; i < n; i++) {
+        hipEvent_t e;
+        OCC_HIP(hipEventCreate(&e));
+        events_host[i] = e;
+    }
+    return OCC_OK;
+}
+
+occ_status occ_events_destroy(int32_t n, void **events_host) {
+    if (n < 0 || (n > 0 && !events_host)) return OCC_ERR_INVALID_ARG;
+    for (int i = 0; i < n; i++)
+        if (events_host[i]) OCC_HIP(hipEventDestroy(static_cast<hipEvent_t>(events_host[i])));
+    return OCC_OK;
+}
+
+occ_status occ_event_elapsed_ms(void *start, void *stop, float *ms_host) {
+    if (!start || !stop || !ms_host) return OCC_ERR_INVALID_ARG;
+    OCC_HIP(hipEventSynchronize(static_cast<hipEvent_t>(stop)));
+    OCC_HIP(hipEventElapsedTime(ms_host, static_cast<hipEvent_t>(start),
+                                static_cast<hipEvent_t>(stop)));
+    return OCC_OK;
+}
+
+}  // extern "C"

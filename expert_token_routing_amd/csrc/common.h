@@ -1,0 +1,87 @@
+// Internal helpers shared by the HIP sources of the Occult MoE-layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace occ {
+
+constexpr int kWave = 64;
+constexpr int kMaxNe = 256;
+constexpr int kMaxNd = 64;
+constexpr int kMaxK = 32;
+constexpr int kMaxBins = kMaxNd + kMaxNe;  // BRIM scan bins: groups, then experts
+
+// Row tile of the grouped GEMMs (tokens per workgroup tile); the BRIM scan
+// lays out the per-expert tile schedule with it.
+constexpr int kGemmBmBf16 = 128;
+constexpr int kGemmBmF32 = 64;
+
+// The expert placement, passed by value as a kernel argument (no device copy,
+// validated on the host).  Position p = g*n + j holds expert `expert[p]`.
+struct PlaceTab {
+    uint8_t grp[kMaxNe];     // group of expert e
+    uint8_t slot[kMaxNe];    // index of expert e inside its group
+    uint8_t expert[kMaxNe];  // expert at placement position p
+    int32_t Ne, Nd, n;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Wave-wide arg-max of (value, index): larger value wins, ties to the lower
+// index.  Every lane returns the winner.
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        float ov = __shfl_xor(v, o);
+        int oi = __shfl_xor(i, o);
+        if (ov > v || (ov == v && oi < i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+inline unsigned ceil_div(size_t a, size_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+}  // namespace occ

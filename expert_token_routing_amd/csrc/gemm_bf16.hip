@@ -1,0 +1,309 @@
+// Grouped expert GEMMs on the bf16 matrix cores of gfx950 (MFMA
+// v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// These are the paper's sparse matrix multiplications (appendix A.2):
+//   up    SMM scattering SFD -> EPD (Algorithm 6) fused with the SwiGLU
+//         activation and the weight modulation (Algorithm 7): for each
+//         expert, its EPD rows gather their SFD rows (the condensed BRIM_1,
+//         section 3.1 footnote 2) and produce
+//           epd[r, f] = bf16( w_r * silu(a_r . Wg[f]) * (a_r . Wu[f]) );
+//         the weight scales the hidden state after the activation, which is
+//         exact because the down-projection is linear;
+//   down  SMM merging EPD -> SFD (Algorithm 8): each EPD row's product with
+//         W_down is added in fp32 to its SFD row (several experts of one group
+//         share that row -- the intra-group pre-aggregation of section 3.1).
+//
+// Tiling: a 256-thread workgroup computes a 128 x 256 tile of MFMA outputs
+// from 64-deep K slices staged through LDS.  Each of the 4 waves owns a
+// 64 x 128 sub-tile = 4 x 8 MFMA blocks of 16 x 16.  In the up GEMM the 256
+// columns are 128 gate and 128 up rows of the same output features, so the
+// SwiGLU epilogue has both operands in registers.  LDS rows are 128 bytes;
+// 16-byte chunks are XOR-swizzled by row so that fragment reads of 16
+// consecutive rows hit distinct banks.  The next K slice is fetched from
+// global memory into registers while the current one is multiplied.
+//
+// Scheduling: the BRIM scan gives each expert ceil(rows / 128) row tiles
+// (tile_off), so every tile reads one expert's weights.  Workgroup b runs on
+// XCD b % 8; tiles are renumbered so each XCD takes a contiguous range of
+// (row tile, column tile) pairs, column tile fastest: the workgroups sharing
+// an expert's weights and a row tile's activations share one L2.
+#include "launch.h"
+
+namespace occ {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int BM = kGemmBmBf16;  // 128 rows (tokens)
+constexpr int BN = 256;          // MFMA columns
+constexpr int BK = 64;           // K slice
+constexpr int NT = 256;          // threads
+constexpr int WM = 64, WN = 128; // wave sub-tile
+constexpr int MI = WM / 16, NI = WN / 16;
+constexpr int A_LD = BM / (NT / 8);  // A rows loaded per thread (4)
+constexpr int B_LD = BN / (NT / 8);  // B rows loaded per thread (8)
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+
+// Workgroup -> (row tile, column tile).  Returns false when there is no tile.
+__device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int &tn) {
+    const int total = m_tiles * n_tiles;
+    const int per = (total + 7) >> 3;
+    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
+    if (idx >= per) return false;
+    const int logical = xcd * per + idx;
+    if (logical >= total) return false;
+    tm = logical / n_tiles;
+    tn = logical - tm * n_tiles;
+    return true;
+}
+
+// Placement position owning row tile tm: the last p with tile_off[p] <= tm.
+__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
+    int lo = 0, hi = Ne;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_off[mid] <= tm) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct Tile {
+    int e;     // expert
+    int seg;   // first row of the expert's segment
+    int m0;    // first row of the tile inside the segment
+    int rows;  // valid rows in the tile
+    int n0;    // first column (output feature) of the tile
+};
+
+__device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
+                                        int Ne, const PlaceTab &tab, int n_tiles, int n_step,
+                                        Tile &t) {
+    int tm, tn;
+    if (seg_off) {
+        const int m_tiles = tile_off[Ne];
+        if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
+        const int p = find_pos(tile_off, Ne, tm);
+        t.e = tab.expert[p];
+        t.seg = seg_off[p];
+        t.m0 = (tm - tile_off[p]) * BM;
+        t.rows = min(BM, seg_off[p + 1] - t.seg - t.m0);
+    } else {
+        const int m_tiles = (M + BM - 1) / BM;
+        if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
+        t.e = 0;
+        t.seg = 0;
+        t.m0 = tm * BM;
+        t.rows = min(BM, M - t.m0);
+    }
+    t.n0 = tn * n_step;
+    return true;
+}
+
+__device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB, int wm,
+                                          const int (&brow)[NI], f32x4_t (&acc)[MI][NI]) {
+    const int l = lane_id();
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ks++) {
+        const int chunk = ks * 4 + (l >> 4);
+        bf16x8_t a[MI], b[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++) {
+            const int r = wm * WM + mi * 16 + (l & 15);
+            a[mi] = *reinterpret_cast<const bf16x8_t *>(sA + swz(r, chunk));
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++)
+            b[ni] = *reinterpret_cast<const bf16x8_t *>(sB + swz(brow[ni], chunk));
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+}
+
+// K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
+// rows at k = 0 (chunk offset included); b_kstep(k0) gives the extra offset
+// of the K slice starting at k0 for B (handles the shared experts' K blocks).
+template <typename BOff>
+__device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
+                                       const uint16_t *const (&b_src)[B_LD], int K, BOff b_koff,
+                                       uint16_t *sA, uint16_t *sB, int wm,
+                                       const int (&brow)[NI], f32x4_t (&acc)[MI][NI]) {
+    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
+    uint4 ra[A_LD], rb[B_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i]);
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + b_koff(0));
+    const int nk = K / BK;
+    for (int kt = 0; kt < nk; kt++) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < A_LD; i++)
+            *reinterpret_cast<uint4 *>(sA + swz(r0 + i * (NT / 8), chunk)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_LD; i++)
+            *reinterpret_cast<uint4 *>(sB + swz(r0 + i * (NT / 8), chunk)) = rb[i];
+        __syncthreads();
+        if (kt + 1 < nk) {
+            const int k0 = (kt + 1) * BK;
+#pragma unroll
+            for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + k0);
+            const size_t bo = b_koff(k0);
+#pragma unroll
+            for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + bo);
+        }
+        mma_slice(sA, sB, wm, brow, acc);
+    }
+}
+
+__global__ __launch_bounds__(NT) void k_gemm_up(UpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[BN * BK];
+    Tile t;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
+
+    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
+    const int K = a.K, N = a.N;
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    const uint16_t *a_src[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) {
+        const int r = min(r0 + i * (NT / 8), t.rows - 1);
+        const int row = t.seg + t.m0 + r;
+        const int src = a.a_rows ? a.a_rows[row] : row;
+        a_src[i] = A + static_cast<size_t>(src) * K + chunk * 8;
+    }
+    const uint16_t *Wg = static_cast<const uint16_t *>(a.Wg) + static_cast<size_t>(t.e) * N * K;
+    const uint16_t *Wu = static_cast<const uint16_t *>(a.Wu) + static_cast<size_t>(t.e) * N * K;
+    const uint16_t *b_src[B_LD];
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) {
+        const int rb = r0 + i * (NT / 8);
+        const int f = min(t.n0 + (rb & 127), N - 1);
+        b_src[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + chunk * 8;
+    }
+
+    const int l = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
+    int brow[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ni++)
+        brow[ni] = (ni < NI / 2 ? 0 : 128) + wn * 64 + (ni % (NI / 2)) * 16 + (l & 15);
+    f32x4_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    k_loop(a_src, b_src, K, [](int k0) { return static_cast<size_t>(k0); }, sA, sB, wm, brow, acc);
+
+    uint16_t *out = static_cast<uint16_t *>(a.out);
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+            if (r >= t.rows) continue;
+            const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
+            const float wr = a.row_w ? a.row_w[row] : 1.f;
+#pragma unroll
+            for (int ni = 0; ni < NI / 2; ni++) {
+                const int f = t.n0 + wn * 64 + ni * 16 + (l & 15);
+                if (f >= N) continue;
+                const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];
+                const float h = g / (1.f + __expf(-g)) * u * wr;
+                out[row * N + f] = f32_to_bf16_bits(h);
+            }
+        }
+}
+
+__global__ __launch_bounds__(NT) void k_gemm_down(DownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[BN * BK];
+    Tile t;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t)) return;
+
+    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
+    const int K = a.K, N = a.N, ksp = a.k_split;
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    const uint16_t *a_src[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) {
+        const int r = min(r0 + i * (NT / 8), t.rows - 1);
+        a_src[i] = A + (static_cast<size_t>(t.seg) + t.m0 + r) * K + chunk * 8;
+    }
+    // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
+    const uint16_t *W = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(t.e) * N * K;
+    const uint16_t *b_src[B_LD];
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) {
+        const int n = min(t.n0 + r0 + i * (NT / 8), N - 1);
+        b_src[i] = W + static_cast<size_t>(n) * ksp + chunk * 8;
+    }
+    const size_t blk = static_cast<size_t>(N) * ksp;
+
+    const int l = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
+    int brow[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ni++) brow[ni] = wn * WN + ni * 16 + (l & 15);
+    f32x4_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    k_loop(a_src, b_src, K,
+           [=](int k0) { return static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp); },
+           sA, sB, wm, brow, acc);
+
+    float *out = a.out;
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+            if (r >= t.rows) continue;
+            const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
+            if (a.dst_rows) {
+                const size_t dst = static_cast<size_t>(a.dst_rows[row]) * N;
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) {
+                    const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
+                    if (c < N) unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) {
+                    const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
+                    if (c < N) out[row * N + c] = acc[mi][ni][v];
+                }
+            }
+        }
+}
+
+unsigned grid_for(size_t m_tiles, size_t n_tiles) {
+    const size_t total = m_tiles * n_tiles;
+    return static_cast<unsigned>(8 * ((total + 7) / 8));
+}
+
+}  // namespace
+
+hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
+    const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, 128));
+    if (grid == 0) return hipSuccess;
+    k_gemm_up<<<grid, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
+    const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, BN));
+    if (grid == 0) return hipSuccess;
+    k_gemm_down<<<grid, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace occ

@@ -1,0 +1,190 @@
+// The two grouped expert GEMMs of the Occult pipeline in fp32 (same
+// semantics as gemm_bf16.hip: SMM scattering with SwiGLU and weight
+// modulation, Algorithms 6-7; SMM merging with fp32 accumulation, Algorithm
+// 8), on the vector ALUs.  On MI355X fp32 vector FMA and fp32 MFMA have the
+// same peak, so a plain LDS-tiled kernel suffices for the fp32 workloads.
+//
+// A 256-thread workgroup computes 64 rows x 64 output columns; thread
+// (ty, tx) owns rows ty + 16*i and columns tx + 16*j (i, j < 4), so the LDS
+// reads of a 16-thread row are consecutive.  K slices of 16 are staged
+// K-major in LDS.  Tile scheduling follows the same per-expert row-tile
+// schedule (64-row tiles) as the bf16 kernels.
+#include "launch.h"
+
+namespace occ {
+namespace {
+
+constexpr int BM = kGemmBmF32;  // 64
+constexpr int BN = 64;
+constexpr int BK = 16;
+constexpr int PAD = 4;
+
+__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
+    int lo = 0, hi = Ne;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_off[mid] <= tm) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct Tile {
+    int e, seg, m0, rows, n0;
+};
+
+__device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
+                                        int Ne, const PlaceTab &tab, int n_tiles, Tile &t) {
+    const int tm = blockIdx.x / n_tiles, tn = blockIdx.x % n_tiles;
+    if (seg_off) {
+        if (tm >= tile_off[Ne]) return false;
+        const int p = find_pos(tile_off, Ne, tm);
+        t.e = tab.expert[p];
+        t.seg = seg_off[p];
+        t.m0 = (tm - tile_off[p]) * BM;
+        t.rows = min(BM, seg_off[p + 1] - t.seg - t.m0);
+    } else {
+        if (tm * BM >= M) return false;
+        t.e = 0;
+        t.seg = 0;
+        t.m0 = tm * BM;
+        t.rows = min(BM, M - t.m0);
+    }
+    t.n0 = tn * BN;
+    return true;
+}
+
+// Stage a 64 x 16 slice (rows of `src`, K-contiguous, starting at k0) into
+// LDS as [k][row].  Thread tid loads 4 consecutive k of row tid / 4.
+__device__ __forceinline__ void stage(float (*dst)[BM + PAD], const float *const src_row, int k0) {
+    const int q = (threadIdx.x & 3) * 4, r = threadIdx.x >> 2;
+    const float4 v = *reinterpret_cast<const float4 *>(src_row + k0 + q);
+    dst[q + 0][r] = v.x;
+    dst[q + 1][r] = v.y;
+    dst[q + 2][r] = v.z;
+    dst[q + 3][r] = v.w;
+}
+
+__global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
+    __shared__ float sA[BK][BM + PAD], sG[BK][BN + PAD], sU[BK][BN + PAD];
+    Tile t;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t)) return;
+    const int K = a.K, N = a.N;
+    const int r_ld = threadIdx.x >> 2;
+    const int row_ld = t.seg + t.m0 + min(r_ld, t.rows - 1);
+    const int src = a.a_rows ? a.a_rows[row_ld] : row_ld;
+    const float *a_row = static_cast<const float *>(a.A) + static_cast<size_t>(src) * K;
+    const int f_ld = min(t.n0 + r_ld, N - 1);
+    const size_t wbase = static_cast<size_t>(t.e) * N * K + static_cast<size_t>(f_ld) * K;
+    const float *g_row = static_cast<const float *>(a.Wg) + wbase;
+    const float *u_row = static_cast<const float *>(a.Wu) + wbase;
+
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float ag[4][4] = {}, au[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        __syncthreads();
+        stage(sA, a_row, k0);
+        stage(sG, g_row, k0);
+        stage(sU, u_row, k0);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; kk++) {
+            float av[4], gv[4], uv[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                gv[j] = sG[kk][tx + 16 * j];
+                uv[j] = sU[kk][tx + 16 * j];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    ag[i][j] = fmaf(av[i], gv[j], ag[i][j]);
+                    au[i][j] = fmaf(av[i], uv[j], au[i][j]);
+                }
+        }
+    }
+    float *out = static_cast<float *>(a.out);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = ty + 16 * i;
+        if (r >= t.rows) continue;
+        const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
+        const float wr = a.row_w ? a.row_w[row] : 1.f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int f = t.n0 + tx + 16 * j;
+            if (f >= N) continue;
+            const float g = ag[i][j];
+            out[row * N + f] = g / (1.f + expf(-g)) * au[i][j] * wr;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
+    __shared__ float sA[BK][BM + PAD], sB[BK][BN + PAD];
+    Tile t;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t)) return;
+    const int K = a.K, N = a.N, ksp = a.k_split;
+    const int r_ld = threadIdx.x >> 2;
+    const float *a_row = static_cast<const float *>(a.A) +
+                         (static_cast<size_t>(t.seg) + t.m0 + min(r_ld, t.rows - 1)) * K;
+    const int n_ld = min(t.n0 + r_ld, N - 1);
+    const float *W = static_cast<const float *>(a.W) + static_cast<size_t>(t.e) * N * K;
+    const size_t blk = static_cast<size_t>(N) * ksp;
+
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        __syncthreads();
+        stage(sA, a_row, k0);
+        // K slice k0 lies in block k0 / ksp (ksp is a multiple of 16)
+        stage(sB, W + (k0 / ksp) * blk + static_cast<size_t>(n_ld) * ksp, k0 % ksp);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; kk++) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) bv[j] = sB[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = ty + 16 * i;
+        if (r >= t.rows) continue;
+        const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c = t.n0 + tx + 16 * j;
+            if (c >= N) continue;
+            if (a.dst_rows) unsafeAtomicAdd(a.out + static_cast<size_t>(a.dst_rows[row]) * N + c, acc[i][j]);
+            else a.out[row * N + c] = acc[i][j];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
+    const size_t grid = max_m_tiles * ceil_div(a.N, BN);
+    if (grid == 0) return hipSuccess;
+    k_gemm_up_f32<<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
+    const size_t grid = max_m_tiles * ceil_div(a.N, BN);
+    if (grid == 0) return hipSuccess;
+    k_gemm_down_f32<<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace occ

@@ -1,0 +1,79 @@
+// Host-side launchers of the library's kernels (internal; the C ABI is in
+// include/occ.h).  Each queues its kernels on `stream` and returns the launch
+// status.  Shapes have been validated by the caller.
+#pragma once
+
+#include "common.h"
+
+namespace occ {
+
+// --- routing (route.hip) ---
+hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rule, int G,
+                        const PlaceTab &tab, int32_t *ids, float *w, hipStream_t s);
+
+// --- BRIM (brim.hip) ---
+constexpr int kBrimChunk = 1024;  // tokens per BRIM workgroup
+struct BrimBufs {
+    int32_t *brim0, *sfd_off, *epd_off, *tile_off, *epd_src, *tok_epd, *brim1;
+    float *epd_w;
+    int32_t *chunk_cnt, *chunk_base;
+};
+hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
+                       int tile_rows, int dense_brim1, const BrimBufs &b, hipStream_t s);
+
+// --- row movers (rows.hip) ---
+// x_sfd[brim0[g, t]] = x[t] for every group the token uses.
+hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
+                           void *x_sfd, hipStream_t s);
+// Zero the first (*n_rows) rows of an fp32 matrix with `row_floats` columns;
+// the launch covers max_rows rows.
+hipError_t launch_zero_rows(float *p, const int32_t *n_rows, size_t max_rows, size_t row_floats,
+                            hipStream_t s);
+// y[t] = dtype( sum over g of sfd_out[brim0[g, t]] (+ y_sh[t]) ), fp32 sums in
+// ascending group order.
+hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const float *y_sh, int T,
+                          int Nd, int d, int out_bf16, void *y, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s);
+
+// --- grouped GEMMs, bf16 MFMA (gemm_bf16.hip) ---
+// Up-projection with SwiGLU and routing-weight modulation:
+//   out[r, f] = bf16( row_w[r] * silu(a_r . Wg[e][f]) * (a_r . Wu[e][f]) )
+// a_r = A[a_rows[r]] (or A[r] when a_rows is NULL).  Routed mode walks the
+// segments [seg_off[p], seg_off[p+1]) of each placement position p with the
+// tile schedule tile_off; shared mode (seg_off NULL) is one segment of M rows.
+struct UpArgs {
+    const void *A;
+    const int32_t *a_rows;
+    const void *Wg, *Wu;
+    const int32_t *seg_off, *tile_off;
+    const float *row_w;
+    void *out;
+    int M, K, N, Ne;
+    PlaceTab tab;
+};
+hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
+
+// Down-projection.  Routed: out[dst_rows[r], :] += A[r] . W[e]^T (fp32
+// atomics; several experts of one group share an SFD row).  Shared
+// (seg_off NULL): out[r, :] = A[r] . W^T with W = n_sh blocks of (N x k_split)
+// laid end to end along K.
+struct DownArgs {
+    const void *A;
+    const void *W;
+    const int32_t *seg_off, *tile_off;
+    const int32_t *dst_rows;
+    float *out;
+    int M, K, N, Ne, k_split;
+    PlaceTab tab;
+};
+hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+
+// --- the same two GEMMs in fp32 on the vector ALUs (gemm_f32.hip) ---
+hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
+hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+
+// --- co-activation statistics (coact.hip) ---
+hipError_t launch_coact(const int32_t *ids, int T, int k, const PlaceTab &tab, int32_t *C,
+                        float *P, int64_t *n_sfd, double *ct, double *intra, hipStream_t s);
+
+}  // namespace occ

@@ -1,0 +1,177 @@
+// Memory-bound row movers of the Occult pipeline (paper, appendix A.2):
+//   dispatch  ORI -> SFD (Algorithm 4): each token row is read once and
+//             written once per group it uses, at BRIM_0[g, t];
+//   zero      the fp32 SFD output that the down-projection accumulates into
+//             (Algorithm 8 starts from a zero tensor);
+//   combine   SFD -> ORI (Algorithm 9): y[t] = sum over g of
+//             sfd_out[BRIM_0[g, t]], entries -1 skipped, summed in fp32 in
+//             ascending group order, plus the shared experts' fp32 output,
+//             cast once to the output dtype.
+// One 64-lane wave per token row; lanes move 16-byte vectors, so a wave
+// touches whole contiguous rows (fully coalesced).  BRIM_0's column for the
+// token is read by lanes 0..Nd-1 and broadcast with shuffles.
+#include <algorithm>
+
+#include "launch.h"
+
+namespace occ {
+namespace {
+
+constexpr int kRowWaves = 4;  // token rows per workgroup
+
+template <int VPL>
+__global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const uint4 *__restrict__ x, int T,
+                                                               int Nd, int row_vec,
+                                                               const int32_t *__restrict__ brim0,
+                                                               uint4 *__restrict__ x_sfd) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int br = lane < Nd ? brim0[static_cast<size_t>(lane) * T + t] : -1;
+    uint4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        const int c = lane + kWave * i;
+        if (c < row_vec) v[i] = x[static_cast<size_t>(t) * row_vec + c];
+    }
+    for (int g = 0; g < Nd; g++) {
+        const int r = __shfl(br, g);
+        if (r < 0) continue;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane + kWave * i;
+            if (c < row_vec) x_sfd[static_cast<size_t>(r) * row_vec + c] = v[i];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_zero_rows(float4 *__restrict__ p,
+                                                   const int32_t *__restrict__ n_rows,
+                                                   size_t row_vec4) {
+    const size_t n = static_cast<size_t>(*n_rows) * row_vec4;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = z;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, size_t n, int32_t v) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+template <int VPL, bool BF16>
+__global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const float4 *__restrict__ sfd_out,
+                                                              const int32_t *__restrict__ brim0,
+                                                              const float4 *__restrict__ y_sh,
+                                                              int T, int Nd, int row_vec4,
+                                                              void *__restrict__ y) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    const int br = lane < Nd ? brim0[static_cast<size_t>(lane) * T + t] : -1;
+    float4 acc[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < Nd; g++) {
+        const int r = __shfl(br, g);
+        if (r < 0) continue;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane + kWave * i;
+            if (c < row_vec4) {
+                const float4 v = sfd_out[static_cast<size_t>(r) * row_vec4 + c];
+                acc[i].x += v.x;
+                acc[i].y += v.y;
+                acc[i].z += v.z;
+                acc[i].w += v.w;
+            }
+        }
+    }
+    if (y_sh) {
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane + kWave * i;
+            if (c < row_vec4) {
+                const float4 v = y_sh[static_cast<size_t>(t) * row_vec4 + c];
+                acc[i].x += v.x;
+                acc[i].y += v.y;
+                acc[i].z += v.z;
+                acc[i].w += v.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        const int c = lane + kWave * i;
+        if (c >= row_vec4) continue;
+        const size_t o = static_cast<size_t>(t) * row_vec4 + c;
+        if constexpr (BF16) {
+            uint2 packed;
+            packed.x = static_cast<uint32_t>(f32_to_bf16_bits(acc[i].x)) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(acc[i].y)) << 16);
+            packed.y = static_cast<uint32_t>(f32_to_bf16_bits(acc[i].z)) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(acc[i].w)) << 16);
+            reinterpret_cast<uint2 *>(y)[o] = packed;
+        } else {
+            reinterpret_cast<float4 *>(y)[o] = acc[i];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
+                           void *x_sfd, hipStream_t s) {
+    const int row_vec = static_cast<int>(row_bytes / 16);
+    const int vpl = (row_vec + kWave - 1) / kWave;
+    const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
+    const uint4 *xs = static_cast<const uint4 *>(x);
+    uint4 *xd = static_cast<uint4 *>(x_sfd);
+    if (vpl <= 1) k_dispatch<1><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    else if (vpl <= 2) k_dispatch<2><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    else if (vpl <= 4) k_dispatch<4><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    else if (vpl <= 8) k_dispatch<8><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    else k_dispatch<16><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(float *p, const int32_t *n_rows, size_t max_rows, size_t row_floats,
+                            hipStream_t s) {
+    const size_t vec = max_rows * (row_floats / 4);
+    const unsigned grid = static_cast<unsigned>(std::min<size_t>(ceil_div(vec, 256 * 4), 8192));
+    k_zero_rows<<<grid > 0 ? grid : 1, 256, 0, s>>>(reinterpret_cast<float4 *>(p), n_rows,
+                                                    row_floats / 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(std::min<size_t>(ceil_div(n, 256), 4096));
+    k_fill_i32<<<grid > 0 ? grid : 1, 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const float *y_sh, int T,
+                          int Nd, int d, int out_bf16, void *y, hipStream_t s) {
+    const int row_vec4 = d / 4;
+    const int vpl = (row_vec4 + kWave - 1) / kWave;
+    const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
+    const float4 *so = reinterpret_cast<const float4 *>(sfd_out);
+    const float4 *ys = reinterpret_cast<const float4 *>(y_sh);
+#define OCC_COMBINE(V)                                                                        \
+    do {                                                                                      \
+        if (out_bf16) k_combine<V, true><<<grid, block, 0, s>>>(so, brim0, ys, T, Nd, row_vec4, y); \
+        else k_combine<V, false><<<grid, block, 0, s>>>(so, brim0, ys, T, Nd, row_vec4, y);       \
+    } while (0)
+    if (vpl <= 1) OCC_COMBINE(1);
+    else if (vpl <= 2) OCC_COMBINE(2);
+    else if (vpl <= 4) OCC_COMBINE(4);
+    else if (vpl <= 8) OCC_COMBINE(8);
+    else if (vpl <= 16) OCC_COMBINE(16);
+    else OCC_COMBINE(32);
+#undef OCC_COMBINE
+    return hipGetLastError();
+}
+
+}  // namespace occ

@@ -1,0 +1,246 @@
+/*
+ * occ.h -- C ABI of the Occult MoE-layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs, on one GPU, the data-parallel hot path of the MoE layer of
+ * "Occult: Optimizing Collaborative Communication across Experts for
+ * Accelerated Parallel MoE Training and Inference" (Luo et al., ICML 2025,
+ * arXiv 2505.13345).  The placement's Nd expert groups stand for the Nd
+ * devices of expert parallelism; the two all-to-all exchanges of the paper's
+ * pipeline (appendix A.1, Algorithm 2) are identities on one GPU, so group g's
+ * segment of every SFD buffer is "device g's receive buffer".
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; all GPU work is queued on `stream` (a hipStream_t, NULL
+ *     meaning the null stream) and the call returns at once.
+ *   - Arguments are checked on the host before anything is queued.  On any
+ *     error nothing is queued and the output buffers are untouched.
+ *   - Row-major layouts.  Weights follow nn.Linear (out, in): the reduction
+ *     dimension is contiguous.
+ *   - Float tensors x, weights and y are all of the descriptor's dtype; router
+ *     logits are always fp32.
+ *   - Calls are stateless; distinct calls may run concurrently on distinct
+ *     streams with distinct workspaces.
+ */
+#ifndef OCC_H
+#define OCC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum occ_status {
+    OCC_OK = 0,
+    OCC_ERR_INVALID_ARG = 1, /* a null pointer, an impossible shape, a bad placement */
+    OCC_ERR_UNSUPPORTED = 2, /* valid, but outside the kernels' limits (see occ_layer_desc) */
+    OCC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than occ_workspace_size */
+    OCC_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} occ_status;
+
+typedef enum occ_dtype { OCC_F32 = 0, OCC_BF16 = 1 } occ_dtype;
+
+/* Collaboration pruning (paper, section 3.3, routing-score-based): each token
+ * may use experts on at most prune_groups groups, and takes the top k experts,
+ * by routing score, among those groups' experts.  The groups are chosen
+ *   TRAVERSE: by walking the token's plain top-k experts in descending score
+ *             and collecting their groups until prune_groups are reached
+ *             (the paper's rule);
+ *   GROUPSUM: by ranking the groups that hold at least one plain top-k expert
+ *             by the fp32 sum, taken in top-k order, of those experts' logits
+ *             (ties to the lower group) and keeping prune_groups of them.
+ * Weights stay the full-softmax probabilities (not renormalised).  A token
+ * whose plain top k already spans <= prune_groups groups is unchanged. */
+typedef enum occ_prune_rule {
+    OCC_PRUNE_OFF = 0,
+    OCC_PRUNE_TRAVERSE = 1,
+    OCC_PRUNE_GROUPSUM = 2
+} occ_prune_rule;
+
+/* Shape of one MoE layer.  Limits of this build:
+ *   1 <= T, T*k < 2^31;  1 <= Ne <= 256;  1 <= k <= min(Ne, 32);
+ *   1 <= Nd <= 64 and Nd divides Ne (n = Ne/Nd experts per group);
+ *   bf16: d, F and F_shared multiples of 64;  fp32: multiples of 16;
+ *   d <= 8192 (bf16) or 4096 (fp32).
+ *   prune_rule != OFF needs prune_groups >= 1 and prune_groups*n >= k. */
+typedef struct occ_layer_desc {
+    int32_t T;            /* tokens in the batch (ORI rows) */
+    int32_t d;            /* hidden size */
+    int32_t Ne;           /* routed experts */
+    int32_t k;            /* experts per token (top-k) */
+    int32_t Nd;           /* expert groups (devices of expert parallelism) */
+    int32_t F;            /* routed expert FFN width */
+    int32_t n_shared;     /* shared experts, 0 for none */
+    int32_t F_shared;     /* shared expert FFN width */
+    int32_t prune_rule;   /* occ_prune_rule */
+    int32_t prune_groups; /* groups a token may use when pruning */
+    int32_t dtype;        /* occ_dtype of x, weights and y */
+    int32_t flags;        /* reserved, must be 0 */
+} occ_layer_desc;
+
+/* Index structures of the paper's appendix A.2, as left in the workspace by
+ * occ_build_brim / occ_moe_forward.  All device pointers, int32 unless noted.
+ *   brim0    Nd x T.  BRIM_0 (Algorithm 3): entry [g, t] is the SFD row holding
+ *            token t's single replica for group g, or -1.  One counter runs
+ *            over groups outer and tokens inner.
+ *   sfd_off  Nd+1.  Group g's SFD rows are [sfd_off[g], sfd_off[g+1]);
+ *            sfd_off[Nd] = N_sfd, the number of replicas (CT = N_sfd / T).
+ *   epd_off  Ne+1, indexed by placement position p = g*n + j (expert
+ *            placement[g][j]): that expert's EPD rows are
+ *            [epd_off[p], epd_off[p+1]).  EPD rows are the token replicas
+ *            seen by one expert each; there are exactly T*k of them.
+ *   epd_src  T*k.  SFD row of each EPD row (the condensed, CSR form of
+ *            BRIM_1: row p of BRIM_1 lists exactly these SFD rows).
+ *   epd_w    T*k, fp32.  Routing weight of each EPD row.
+ *   tok_epd  T*k.  EPD row of token t's j-th routed expert, at t*k + j.
+ *   brim1    BRIM_1 (Algorithm 5) as dense matrices, one per group: group g's
+ *            block is n x N_g (N_g = sfd_off[g+1]-sfd_off[g]) at offset
+ *            n*sfd_off[g]; entry [j, t'] is the group-local EPD row of SFD
+ *            row sfd_off[g]+t' for the group's j-th expert, or -1.  A counter
+ *            restarts per group and runs over local experts outer, SFD rows
+ *            inner.  Written only when dense BRIM_1 is requested.
+ *   tile_off Ne+1.  Row-tile schedule of the grouped GEMMs (internal). */
+typedef struct occ_brim {
+    int32_t *brim0;
+    int32_t *sfd_off;
+    int32_t *epd_off;
+    int32_t *epd_src;
+    float *epd_w;
+    int32_t *tok_epd;
+    int32_t *brim1;
+    int32_t *tile_off;
+} occ_brim;
+
+/* Where occ_moe_forward leaves its intermediate tensors in the workspace.
+ *   ids, w    T x k routing result (int32 / fp32).
+ *   x_sfd     N_sfd x d, dtype: the dispatched replicas (ORI -> SFD).
+ *   epd       T*k x F, dtype: modulated SwiGLU hidden states (SFD -> EPD).
+ *   sfd_out   N_sfd x d, fp32: stage-one sums inside each group (EPD -> SFD).
+ *   h_shared  T x n_shared*F_shared, dtype; y_shared T x d, fp32 (or NULL). */
+typedef struct occ_forward_view {
+    int32_t *ids;
+    float *w;
+    occ_brim brim;
+    void *x_sfd;
+    void *epd;
+    float *sfd_out;
+    void *h_shared;
+    float *y_shared;
+} occ_forward_view;
+
+/* Stages timed by occ_moe_forward when given events (see there). */
+enum {
+    OCC_STAGE_ROUTE = 0,
+    OCC_STAGE_BRIM = 1,
+    OCC_STAGE_DISPATCH = 2,
+    OCC_STAGE_SHARED = 3,
+    OCC_STAGE_GEMM_UP = 4,
+    OCC_STAGE_MERGE_INIT = 5,
+    OCC_STAGE_GEMM_DOWN = 6,
+    OCC_STAGE_COMBINE = 7,
+    OCC_STAGE_COUNT = 8
+};
+
+/* A fixed string naming the status.  Never NULL. */
+const char *occ_status_string(occ_status status);
+
+/* Bytes of device workspace occ_moe_forward needs for this shape (enough for
+ * every other call too).  It is sized for the worst case N_sfd = T*min(k, Nd),
+ * so no call ever has to read a data-dependent size back to the host.
+ * Errors: INVALID_ARG / UNSUPPORTED as for the other calls. */
+occ_status occ_workspace_size(const occ_layer_desc *desc, size_t *bytes_host);
+
+/* Router, paper Eq. 2 (section 2.1): R(x) = Top-K(Softmax(g(x)), k), with the
+ * logits g(x) given, plus optional collaboration pruning (section 3.3; see
+ * occ_prune_rule).
+ *   logits           T x Ne fp32.
+ *   placement_host   Nd x n int32 in host memory: group g holds experts
+ *                    placement_host[g*n + 0 .. g*n + n-1]; must be a
+ *                    permutation of 0..Ne-1 (used only when pruning).
+ *   ids  (out)       T x k int32: the token's experts, in descending logit
+ *                    order, ties to the lower expert index.
+ *   w    (out)       T x k fp32: their softmax probabilities over all Ne
+ *                    logits, not renormalised.
+ * NaN or infinite logits give unspecified (but in-bounds) ids. */
+occ_status occ_route(const occ_layer_desc *desc, const float *logits,
+                     const int32_t *placement_host, int32_t *ids, float *w, void *stream);
+
+/* BRIM_0 and BRIM_1, paper appendix A.2 (Algorithms 3 and 5), from routing
+ * ids/w (T x k, as written by occ_route) and the placement (host, as above).
+ * Writes the structures of occ_brim into `workspace` (ws_bytes >=
+ * occ_workspace_size) and returns their device addresses in *out_host.
+ * dense_brim1 != 0 also writes the dense BRIM_1 matrices.  ids must lie in
+ * 0..Ne-1 and be distinct within a token. */
+occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const float *w,
+                          const int32_t *placement_host, int dense_brim1, void *workspace,
+                          size_t ws_bytes, occ_brim *out_host, void *stream);
+
+/* The whole layer, paper Eq. 1 through the pipeline of Algorithm 2:
+ *   route (Eq. 2) -> BRIM_0/BRIM_1 -> dispatch ORI->SFD (Alg. 4) ->
+ *   SwiGLU up-projection SFD->EPD with the routing weight applied to the
+ *   hidden state (Alg. 6-7) -> down-projection EPD->SFD summed inside each
+ *   group in fp32 (Alg. 8) -> combine SFD->ORI summed across groups (Alg. 9).
+ * Without pruning the result equals the plain top-k MoE output (section 3.2).
+ *   x          T x d (dtype);  logits T x Ne fp32;  placement_host as above.
+ *   w_gate     Ne x F x d;  w_up Ne x F x d;  w_down Ne x d x F (dtype).
+ *   ws_gate    n_shared x F_shared x d, ws_up likewise, ws_down
+ *              n_shared x d x F_shared: shared experts, dense and ungated,
+ *              added with weight 1; NULL when n_shared = 0.
+ *   y (out)    T x d (dtype).
+ *   workspace  device, 256-byte aligned, ws_bytes >= occ_workspace_size;
+ *              holds the intermediates afterwards (occ_forward_views).
+ *   stage_events  NULL, or OCC_STAGE_COUNT+1 hipEvent_t handles: event 0 is
+ *              recorded on `stream` before the first stage and event s+1
+ *              right after stage s, so the pair (s, s+1) times stage s. */
+occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const float *logits,
+                           const int32_t *placement_host, const void *w_gate, const void *w_up,
+                           const void *w_down, const void *ws_gate, const void *ws_up,
+                           const void *ws_down, void *y, void *workspace, size_t ws_bytes,
+                           void *const *stage_events, void *stream);
+
+/* Device addresses of the intermediates occ_moe_forward leaves in a
+ * workspace (pure host arithmetic, nothing queued). */
+occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
+                             occ_forward_view *out_host);
+
+/* Co-activation statistics of a routed batch (ids T x k, placement host).
+ *   C (out)      Ne x Ne int32, paper Eq. 3: tokens activating both i and j,
+ *                over ordered pairs of a token's experts (C[i][i] = load of i).
+ *   P (out)      Ne x Ne fp32, Eq. 4: C / max C with the max over i != j,
+ *                one correctly rounded fp32 division per entry, P[i][i] = 0
+ *                (all zero when no pair exists).
+ *   n_sfd (out)  1 int64: replicas, i.e. distinct groups summed over tokens.
+ *   ct (out)     1 fp64: CT = n_sfd / T, the mean replicas per token (section
+ *                2.2), bounded by Eq. 5: ceil(k*Nd/Ne) <= CT <= min(k, Nd).
+ *   intra (out)  1 fp64: share of the off-diagonal co-activations whose two
+ *                experts share a group (the Intra / Inter split of Table 1). */
+occ_status occ_coactivation_stats(const occ_layer_desc *desc, const int32_t *ids,
+                                  const int32_t *placement_host, int32_t *C, float *P,
+                                  int64_t *n_sfd, double *ct, double *intra, void *stream);
+
+/* Expert placement rescheduling, paper section 3.2, Algorithm 1, on the host
+ * (an offline step run once per layer on profiled counts).  C_host: Ne x Ne
+ * co-activation counts (as from occ_coactivation_stats, copied to the host).
+ * Group 0 is seeded with the most collaborative pair, each later group with
+ * the unused expert least collaborative with all placed experts, and each
+ * group grows to n = Ne/Nd experts by the unused expert most collaborative
+ * with its members; ties go to the lowest index.  Writes Nd x n experts to
+ * placement_host in push order. */
+occ_status occ_place_experts(const int32_t *C_host, int32_t Ne, int32_t Nd,
+                             int32_t *placement_host);
+
+/* Small helpers so callers can time stages without linking HIP themselves:
+ * create / destroy n hipEvent_t handles, and read the milliseconds between
+ * two recorded events (waits for the second one). */
+occ_status occ_events_create(int32_t n, void **events_host);
+occ_status occ_events_destroy(int32_t n, void **events_host);
+occ_status occ_event_elapsed_ms(void *start, void *stop, float *ms_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OCC_H */

@@ -1,0 +1,72 @@
+"""Helpers for the GPU parity tests (device inputs, oracle views, error metric)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from expert_token_routing_amd import occ, synth, workloads as W
+
+# Layer-output tolerance: max over rows of ||y_t - y*_t||_inf / ||y*_t||_inf,
+# y* the fp64 oracle.  bf16: inputs and weights are exact bf16; the EPD hidden
+# state and the output are rounded to bf16 (2^-9 relative each), fp32
+# accumulation elsewhere -> observed ~5e-3; 2e-2 leaves margin for the
+# accumulation-order spread.  fp32: rounding of K <= 2048-term fp32 dot
+# products, ~1e-6 -> 1e-5.
+TOL = {W.DTYPE_BF16: 2e-2, W.DTYPE_F32: 1e-5}
+# Routing weights: fp32 expf of a rounded difference plus a sum of Ne terms
+# in fp32 against the fp64 softmax: a few ulp of fp32 -> 1e-5 relative.
+W_RTOL = 1e-5
+
+_cache: dict = {}
+
+
+def inputs(wl: W.Workload) -> dict:
+    """Host inputs of a workload (cached for the session)."""
+    if wl.name not in _cache:
+        _cache[wl.name] = synth.make_all(wl)
+    return _cache[wl.name]
+
+
+def to_dev(inp: dict) -> dict:
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def bits(t: torch.Tensor | None):
+    """Oracle view of a host tensor: bf16 as bit patterns, fp32 as is."""
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def row_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    den = np.abs(ref).max(1)
+    den[den == 0] = 1.0
+    return np.abs(got.astype(np.float64) - ref).max(1) / den
+
+
+def forward(wl: W.Workload, inp: dict, placement=None, dev: dict | None = None):
+    """Run occ_moe_forward; returns (y on host as float64, workspace, views, desc)."""
+    desc = occ.desc_of(wl)
+    dev = dev or to_dev(inp)
+    L = inp["placement"] if placement is None else placement
+    ws = occ.alloc_workspace(desc)
+    y = torch.empty(wl.T, wl.d, dtype=synth.torch_dtype(wl), device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), ws, occ.occ_forward_views(desc, ws), desc
+
+
+def oracle_rows(wl: W.Workload, inp: dict, rows, ids, w, nthreads: int = 0):
+    return oracle.moe_rows(rows, bits(inp["x"]), ids, w, bits(inp["w_gate"]), bits(inp["w_up"]),
+                           bits(inp["w_down"]), bits(inp["ws_gate"]), bits(inp["ws_up"]),
+                           bits(inp["ws_down"]), nthreads=nthreads)
+
+
+def oracle_route(wl: W.Workload, inp: dict, placement=None):
+    L = inp["placement"] if placement is None else placement
+    return oracle.route(inp["logits"].numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)

@@ -1,0 +1,171 @@
+"""The C ABI on the host (no GPU): the library loads, exports exactly what
+include/occ.h declares, rejects bad arguments before queueing any work, and
+its host-side Algorithm 1 agrees with the oracle's bit for bit."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_amd import occ, synth, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "occ.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(occ.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return occ.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(occ_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported(L):
+    names = declared_symbols()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", occ.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    # nothing else leaks out of the library under an occ_ name
+    assert {n for n in exported if n.startswith("occ_")} == set(names)
+    assert sorted(occ.EXPORTED) == names
+    for n in names:
+        getattr(L, n)
+
+
+def test_status_strings(L):
+    for s, name in enumerate(["OCC_OK", "OCC_ERR_INVALID_ARG", "OCC_ERR_UNSUPPORTED",
+                              "OCC_ERR_WORKSPACE", "OCC_ERR_HIP"]):
+        assert occ.status_string(s) == name
+    assert occ.status_string(99) == "OCC_ERR_UNKNOWN"
+
+
+def _ws(desc):
+    n = ctypes.c_size_t(0)
+    rc = occ.lib().occ_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=0), occ.OCC_ERR_INVALID_ARG),
+    (dict(k=0), occ.OCC_ERR_INVALID_ARG),
+    (dict(k=65), occ.OCC_ERR_INVALID_ARG),           # k > Ne
+    (dict(Nd=7), occ.OCC_ERR_INVALID_ARG),           # Ne % Nd != 0
+    (dict(dtype=5), occ.OCC_ERR_INVALID_ARG),
+    (dict(prune_rule=3), occ.OCC_ERR_INVALID_ARG),
+    (dict(prune_rule=1, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
+    (dict(prune_rule=2, prune_groups=1, k=9), occ.OCC_ERR_INVALID_ARG),  # 1 group of 8 < k
+    (dict(flags=1), occ.OCC_ERR_INVALID_ARG),
+    (dict(n_shared=1, F_shared=0), occ.OCC_ERR_INVALID_ARG),
+    (dict(d=2000), occ.OCC_ERR_UNSUPPORTED),          # bf16 needs multiples of 64
+    (dict(F=1000), occ.OCC_ERR_UNSUPPORTED),
+    (dict(k=33), occ.OCC_ERR_UNSUPPORTED),
+    (dict(Ne=512, Nd=8), occ.OCC_ERR_UNSUPPORTED),
+    (dict(Ne=128, Nd=128), occ.OCC_ERR_UNSUPPORTED),
+    (dict(d=16384), occ.OCC_ERR_UNSUPPORTED),
+])
+def test_descriptor_validation(L, over, code):
+    rc, _ = _ws(occ.desc_of(W.OLMOE, **over))
+    assert rc == code
+
+
+def test_workspace_size_covers_the_worst_case(L):
+    for wl in W.ALL:
+        rc, n = _ws(occ.desc_of(wl))
+        assert rc == occ.OCC_OK
+        es = 2 if wl.dtype == W.DTYPE_BF16 else 4
+        nsfd_max = wl.T * min(wl.k, wl.Nd)
+        floor = nsfd_max * wl.d * (es + 4) + wl.T * wl.k * wl.F * es
+        assert n >= floor
+        assert n < 300 * 2**30
+
+
+def _null():
+    return ctypes.c_void_p(0)
+
+
+def test_calls_reject_bad_pointers_and_placements_without_a_gpu(L):
+    wl = W.OLMOE
+    desc = occ.desc_of(wl)
+    good = np.ascontiguousarray(synth.contiguous_placement(wl))
+    dup = good.copy()
+    dup[0, 0] = dup[0, 1]
+    fake = ctypes.c_void_p(0x1000)
+    hp = lambda a: ctypes.c_void_p(a.ctypes.data)
+    # null device pointers
+    assert L.occ_route(ctypes.byref(desc), _null(), hp(good), fake, fake, _null()) == occ.OCC_ERR_INVALID_ARG
+    # placement missing / not a permutation
+    assert L.occ_route(ctypes.byref(desc), fake, _null(), fake, fake, _null()) == occ.OCC_ERR_INVALID_ARG
+    assert L.occ_route(ctypes.byref(desc), fake, hp(dup), fake, fake, _null()) == occ.OCC_ERR_INVALID_ARG
+    out_of_range = good.copy()
+    out_of_range[1, 1] = 64
+    assert L.occ_route(ctypes.byref(desc), fake, hp(out_of_range), fake, fake, _null()) == occ.OCC_ERR_INVALID_ARG
+    # workspace: missing, misaligned, too small
+    b = occ.Brim()
+    args = (ctypes.byref(desc), fake, fake, hp(good), 1)
+    assert L.occ_build_brim(*args, _null(), 1 << 40, ctypes.byref(b), _null()) == occ.OCC_ERR_WORKSPACE
+    assert L.occ_build_brim(*args, ctypes.c_void_p(0x1008), 1 << 40, ctypes.byref(b), _null()) == occ.OCC_ERR_WORKSPACE
+    assert L.occ_build_brim(*args, fake, 1024, ctypes.byref(b), _null()) == occ.OCC_ERR_WORKSPACE
+    # forward: missing weights / shared weights / events
+    _, ws = _ws(desc)
+    fwd = lambda *p: L.occ_moe_forward(ctypes.byref(desc), *p)
+    assert fwd(fake, fake, hp(good), fake, fake, _null(), None, None, None, fake, fake, ws, None, None) == occ.OCC_ERR_INVALID_ARG
+    d3 = occ.desc_of(W.DEEPSEEK)
+    _, ws3 = _ws(d3)
+    good3 = np.ascontiguousarray(synth.contiguous_placement(W.DEEPSEEK))
+    assert L.occ_moe_forward(ctypes.byref(d3), fake, fake, hp(good3), fake, fake, fake, None, None, None,
+                             fake, fake, ws3, None, None) == occ.OCC_ERR_INVALID_ARG
+    ev = (ctypes.c_void_p * (occ.OCC_STAGE_COUNT + 1))()
+    assert fwd(fake, fake, hp(good), fake, fake, fake, None, None, None, fake, fake, ws,
+               ctypes.cast(ev, ctypes.c_void_p), None) == occ.OCC_ERR_INVALID_ARG
+    assert fwd(fake, fake, hp(good), fake, fake, fake, None, None, None, fake, fake, ws - 256,
+               None, None) == occ.OCC_ERR_WORKSPACE
+    st = L.occ_coactivation_stats(ctypes.byref(desc), fake, hp(good), fake, fake, _null(), fake, fake, _null())
+    assert st == occ.OCC_ERR_INVALID_ARG
+    assert L.occ_place_experts(_null(), 64, 8, fake) == occ.OCC_ERR_INVALID_ARG
+    C = np.zeros((64, 64), np.int32)
+    assert L.occ_place_experts(hp(C), 64, 7, hp(np.zeros(64, np.int32))) == occ.OCC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("Ne,Nd,seed", [(64, 8, 0), (60, 4, 1), (8, 2, 2), (16, 16, 3), (12, 1, 4),
+                                        (64, 32, 5)])
+def test_host_algorithm1_matches_oracle(L, Ne, Nd, seed):
+    rng = np.random.default_rng(seed)
+    C = rng.integers(0, 40, (Ne, Ne))
+    C = (C + C.T).astype(np.int32)
+    C[rng.random((Ne, Ne)) < 0.2] = 7  # plenty of ties
+    C = np.triu(C) + np.triu(C, 1).T
+    got = occ.occ_place_experts(C, Nd)
+    assert np.array_equal(got, oracle.placement(C.astype(np.int64), Nd))
+
+
+def test_host_algorithm1_on_routed_counts(L):
+    wl = W.OLMOE
+    ids, _ = oracle.route(synth.make_logits(wl, 4096).numpy(), wl.k,
+                          synth.contiguous_placement(wl))
+    C = oracle.coact(ids, wl.Ne, synth.contiguous_placement(wl))["C"]
+    got = occ.occ_place_experts(C.astype(np.int32), wl.Nd)
+    assert np.array_equal(got, oracle.placement(C, wl.Nd))
+    # the worked example of Algorithm 1
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "algorithm1_example.json")))
+    assert occ.occ_place_experts(np.array(g["C"]), g["Nd"]).tolist() == g["placement"]
+
+
+def test_binding_refuses_host_tensors(L):
+    desc = occ.desc_of(W.TINY_F32)
+    with pytest.raises(ValueError):
+        occ.occ_route(desc, torch.zeros(256, 8), synth.contiguous_placement(W.TINY_F32),
+                      torch.zeros(256, 2, dtype=torch.int32), torch.zeros(256, 2))

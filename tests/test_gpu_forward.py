@@ -1,0 +1,163 @@
+"""GPU parity of the whole layer (occ_moe_forward) against the oracle's
+Eq. 1 output, and of its intermediates: the dispatched SFD replicas (a pure
+copy, bit-exact), the modulated EPD hidden states and the stage-one SFD sums
+(within tolerance).  Small ragged sizes are checked on every row; the full
+workload sizes, in the launch configuration the benchmark times, on a seeded
+sample of rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_amd import occ, synth, workloads as W
+
+from gpu_common import TOL, bits, forward, inputs, oracle_route, oracle_rows, row_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    occ.lib()
+
+
+def check_forward(wl, rows=None, placement=None, inp=None):
+    inp = inp or inputs(wl)
+    L = inp["placement"] if placement is None else placement
+    y, ws, v, desc = forward(wl, inp, L)
+    ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
+    assert np.array_equal(ids, ids_o)
+    rows = np.arange(wl.T) if rows is None else rows
+    ref = oracle_rows(wl, inp, rows, ids_o, w_o)
+    err = row_err(y[rows], ref)
+    assert err.max() <= TOL[wl.dtype], f"{wl.name}: max per-row rel err {err.max():.3e}"
+    return y, ws, v, err
+
+
+SMALL = [
+    W.TINY_F32,
+    W.scaled(W.OLMOE, 300),
+    W.scaled(W.DEEPSEEK, 261),
+    W.scaled(W.OLMOE_PRUNED, 333),
+    W.scaled(W.QWEN, 197),
+    W.scaled(W.TINY_F32, 1000, n_shared=2, F_shared=128),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_forward_small_all_rows(wl):
+    check_forward(wl)
+
+
+FULL = [W.TINY_F32, W.OLMOE, W.DEEPSEEK, W.OLMOE_PRUNED, W.QWEN]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_forward_full_size_sampled_rows(wl):
+    rows = synth.sample_rows(wl.T, 96, seed=wl.index)
+    y, *_ = check_forward(wl, rows)
+    assert np.isfinite(y).all()
+
+
+def test_forward_intermediates():
+    """x_sfd is a bit-exact copy of x at BRIM_0; the EPD hidden states and the
+    stage-one group sums match an fp64 replay of the same rows."""
+    wl = W.scaled(W.OLMOE, 517)
+    inp = inputs(wl)
+    y, ws, v, desc = forward(wl, inp)
+    T, d, k, Nd, F = wl.T, wl.d, wl.k, wl.Nd, wl.F
+    b0 = occ.ws_view(ws, v.brim.brim0, (Nd, T), torch.int32).cpu().numpy()
+    sfd_off = occ.ws_view(ws, v.brim.sfd_off, (Nd + 1,), torch.int32).cpu().numpy()
+    N_sfd = int(sfd_off[-1])
+    x_sfd = occ.ws_view(ws, v.x_sfd, (N_sfd, d), torch.bfloat16).cpu()
+    x = inp["x"]
+    for g in range(Nd):
+        tok = np.flatnonzero(b0[g] >= 0)
+        assert torch.equal(x_sfd[b0[g, tok]], x[tok])
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), k, inp["placement"])
+    r = oracle.brim1(ids_o, w_o, wl.Ne, inp["placement"])
+    epd = occ.ws_view(ws, v.epd, (T * k, F), torch.bfloat16).float().cpu().numpy()
+    sfd_out = occ.ws_view(ws, v.sfd_out, (N_sfd, d), torch.float32).cpu().numpy()
+    # EPD row r = w * SwiGLU hidden state of its SFD row's token for expert L[p]
+    tok_of_sfd = np.empty(N_sfd, np.int64)
+    for g in range(Nd):
+        tok = np.flatnonzero(b0[g] >= 0)
+        tok_of_sfd[b0[g, tok]] = tok
+    pos_expert = inp["placement"].reshape(-1)
+    xd = x.double()
+    rng = np.random.default_rng(0)
+    for p in rng.choice(wl.Ne, 6, replace=False):
+        e = pos_expert[p]
+        lo, hi = r["epd_off"][p], r["epd_off"][p + 1]
+        rows = np.arange(lo, hi)
+        t = tok_of_sfd[r["epd_src"][rows]]
+        h = torch.nn.functional.silu(xd[t] @ inp["w_gate"][e].double().T) * \
+            (xd[t] @ inp["w_up"][e].double().T)
+        h = (h * torch.from_numpy(r["epd_w"][rows])[:, None]).numpy()
+        assert row_err(epd[rows], h).max() <= 1e-2
+    # stage one: sfd_out[s] = sum over the group's experts of W_down h
+    for s in rng.choice(N_sfd, 12, replace=False):
+        contrib = np.flatnonzero(r["epd_src"] == s)
+        p_of = np.searchsorted(r["epd_off"], contrib, side="right") - 1
+        ref = sum(epd[c].astype(np.float64) @ inp["w_down"][pos_expert[p]].double().numpy().T
+                  for c, p in zip(contrib, p_of))
+        assert row_err(sfd_out[s][None], np.asarray(ref)[None]).max() <= 1e-4
+
+
+def test_placement_invariance_and_rescheduling():
+    """Sections 3.2-3.3: the rescheduled placement changes CT but not y."""
+    wl = W.scaled(W.OLMOE, 700)
+    inp = inputs(wl)
+    L0 = inp["placement"]
+    ids_o, _ = oracle.route(inp["logits"].numpy(), wl.k, L0)
+    L1 = occ.occ_place_experts(oracle.coact(ids_o, wl.Ne, L0)["C"].astype(np.int32), wl.Nd)
+    dev = to_dev(inp)
+    y0, ws0, v0, _ = forward(wl, inp, L0, dev)
+    y1, ws1, v1, _ = forward(wl, inp, L1, dev)
+    n0 = occ.ws_view(ws0, v0.brim.sfd_off, (wl.Nd + 1,), torch.int32)[-1].item()
+    n1 = occ.ws_view(ws1, v1.brim.sfd_off, (wl.Nd + 1,), torch.int32)[-1].item()
+    assert n1 < n0
+    ref = oracle_rows(wl, inp, np.arange(wl.T), *oracle.route(inp["logits"].numpy(), wl.k, L0))
+    assert row_err(y0, ref).max() <= TOL[wl.dtype]
+    assert row_err(y1, ref).max() <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=1), dict(T=7, k=1), dict(T=129, Nd=1), dict(T=200, Ne=8, Nd=8, k=3),
+    dict(T=150, Ne=16, Nd=4, k=16), dict(T=300, F=192, d=192),
+    dict(T=260, n_shared=3, F_shared=64),
+    dict(T=400, prune_rule=W.PRUNE_TRAVERSE, prune_groups=1, Ne=16, Nd=4, k=4),
+])
+def test_forward_edge_shapes(shape):
+    base = dict(d=128, Ne=16, k=2, Nd=4, F=128, n_c=4, bonus=1.5)
+    base.update(shape)
+    wl = W.Workload("edge_" + "_".join(f"{k}{v}" for k, v in shape.items()), 14, **base)
+    check_forward(wl, inp=synth.make_all(wl))
+    wl32 = W.Workload(wl.name + "_f32", 15, dtype=W.DTYPE_F32,
+                      **{k: v for k, v in base.items() if k not in ("dtype",)})
+    check_forward(wl32, inp=synth.make_all(wl32))
+
+
+def test_forward_with_starved_expert_and_group():
+    wl = W.Workload("starved_fwd", 16, T=600, d=128, Ne=16, k=2, Nd=4, F=128, n_c=2)
+    inp = synth.make_all(wl)
+    inp["logits"][:, 4:8] = -50.0
+    inp["logits"][:, 13] = -50.0
+    check_forward(wl, inp=inp)
+
+
+def test_repeat_runs_are_stable():
+    """Integer outputs repeat exactly; y only by the fp32 atomic order."""
+    wl = W.scaled(W.OLMOE, 1200)
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    y0, ws0, v0, _ = forward(wl, inp, dev=dev)
+    y1, ws1, v1, _ = forward(wl, inp, dev=dev)
+    for name, shape in [("brim0", (wl.Nd, wl.T)), ("epd_src", (wl.T * wl.k,))]:
+        a = occ.ws_view(ws0, getattr(v0.brim, name), shape, torch.int32)
+        b = occ.ws_view(ws1, getattr(v1.brim, name), shape, torch.int32)
+        assert torch.equal(a, b)
+    assert row_err(y1, y0).max() <= 1e-2
