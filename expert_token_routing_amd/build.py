@@ -26,6 +26,9 @@ SOURCES = ["api.hip", "route.hip", "brim.hip", "rows.hip", "gemm_bf16.hip", "gem
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep small per-thread arrays (GEMM staging registers) out of LDS: the
+    # promotion runs before unrolling and would add a conflicting LDS copy
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

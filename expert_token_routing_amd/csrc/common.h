@@ -8,6 +8,11 @@
 namespace occ {
 
 constexpr int kWave = 64;
+
+// Native 16-byte vectors for register-resident staging (HIP's uint4/float4
+// wrap a union, which keeps per-thread arrays of them out of registers).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kMaxNe = 256;
 constexpr int kMaxNd = 64;
 constexpr int kMaxK = 32;
@@ -15,7 +20,10 @@ constexpr int kMaxBins = kMaxNd + kMaxNe;  // BRIM scan bins: groups, then exper
 
 // Row tile of the grouped GEMMs (tokens per workgroup tile); the BRIM scan
 // lays out the per-expert tile schedule with it.
-constexpr int kGemmBmBf16 = 128;
+#ifndef OCC_GEMM_BM
+#define OCC_GEMM_BM 128
+#endif
+constexpr int kGemmBmBf16 = OCC_GEMM_BM;
 constexpr int kGemmBmF32 = 64;
 
 // The expert placement, passed by value as a kernel argument (no device copy,

@@ -13,46 +13,89 @@
 //         W_down is added in fp32 to its SFD row (several experts of one group
 //         share that row -- the intra-group pre-aggregation of section 3.1).
 //
-// Tiling: a 256-thread workgroup computes a 128 x 256 tile of MFMA outputs
-// from 64-deep K slices staged through LDS.  Each of the 4 waves owns a
-// 64 x 128 sub-tile = 4 x 8 MFMA blocks of 16 x 16.  In the up GEMM the 256
-// columns are 128 gate and 128 up rows of the same output features, so the
-// SwiGLU epilogue has both operands in registers.  LDS rows are 128 bytes;
-// 16-byte chunks are XOR-swizzled by row so that fragment reads of 16
-// consecutive rows hit distinct banks.  The next K slice is fetched from
-// global memory into registers while the current one is multiplied.
+// Tiling: a 256-thread workgroup computes a BM x 256 tile of MFMA outputs
+// (BM = 256 by default) from 64-deep K slices.  Each of the 4 waves owns a
+// (BM/2) x 128 sub-tile of 16 x 16 MFMA blocks, so a wave reads
+// (BM/2 + 128) rows of fragments per BM/2 x 128 x 64 products -- the LDS
+// bytes per flop that bound this kernel.  In the up GEMM the 256 columns are
+// 128 gate and 128 up rows of the same output features, so the SwiGLU
+// epilogue has both operands in registers.  K slices are double-buffered in
+// LDS: the next slice is fetched from global memory into registers while the
+// current one is multiplied, then written to the other buffer, with one
+// barrier per slice.  LDS rows are 128 bytes and their 16-byte chunks are
+// XOR-swizzled by row, so fragment reads of 16 consecutive rows hit distinct
+// banks.  The up GEMM's bf16 output tile is staged through LDS and written as
+// whole 16-byte row chunks.
 //
-// Scheduling: the BRIM scan gives each expert ceil(rows / 128) row tiles
+// Scheduling: the BRIM scan gives each expert ceil(rows / BM) row tiles
 // (tile_off), so every tile reads one expert's weights.  Workgroup b runs on
-// XCD b % 8; tiles are renumbered so each XCD takes a contiguous range of
-// (row tile, column tile) pairs, column tile fastest: the workgroups sharing
-// an expert's weights and a row tile's activations share one L2.
+// XCD b % 8; tiles are renumbered so that each XCD takes a contiguous range
+// of (row tile, column tile) pairs, column tile fastest: the workgroups
+// sharing an expert's weights and a row tile's activations share one L2.
 #include "launch.h"
 
 namespace occ {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef f32x4 f32x4_t;
 
-constexpr int BM = kGemmBmBf16;  // 128 rows (tokens)
-constexpr int BN = 256;          // MFMA columns
-constexpr int BK = 64;           // K slice
-constexpr int NT = 256;          // threads
-constexpr int WM = 64, WN = 128; // wave sub-tile
+#ifndef OCC_GEMM_BK
+#define OCC_GEMM_BK 32
+#endif
+#ifndef OCC_GEMM_WG_PER_CU
+#define OCC_GEMM_WG_PER_CU 2
+#endif
+#ifndef OCC_XCD_MAP
+#define OCC_XCD_MAP 1
+#endif
+constexpr int BM = kGemmBmBf16;   // rows (tokens) per tile
+constexpr int BN = 256;           // MFMA columns per tile
+constexpr int BK = OCC_GEMM_BK;   // K slice
+constexpr int NT = 256;           // threads
+constexpr int WM = BM / 2, WN = BN / 2;  // wave sub-tile (2 x 2 waves)
 constexpr int MI = WM / 16, NI = WN / 16;
-constexpr int A_LD = BM / (NT / 8);  // A rows loaded per thread (4)
-constexpr int B_LD = BN / (NT / 8);  // B rows loaded per thread (8)
+constexpr int CHUNKS = BK / 8;           // 16-byte chunks per LDS row
+constexpr int ROWS_PER_PASS = NT / CHUNKS;  // rows one pass of the workgroup moves
+constexpr int A_LD = BM / ROWS_PER_PASS;
+constexpr int B_LD = BN / ROWS_PER_PASS;
+constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per LDS buffer
+constexpr int OUT_PITCH = 128 + 8;       // up epilogue staging row (elements)
+static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS");
+static_assert(BM * OUT_PITCH <= 2 * STAGE, "epilogue staging fits in the K buffers");
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+#ifndef OCC_SWZ
+#define OCC_SWZ 3
+#endif
+// Chunk c of row r sits at chunk slot c ^ f(r).  A 16-byte fragment read
+// covers 16 consecutive rows at one logical chunk; f must send them to 16
+// distinct bank groups of the 64-bank LDS (rows of 128 bytes put odd rows in
+// the upper half) and to 8 distinct groups within each 8-row half.
+__device__ __forceinline__ int swz_key(int row) {
+#if OCC_SWZ == 0
+    return row & 7;
+#elif OCC_SWZ == 1
+    return (row >> 1) & 7;
+#elif OCC_SWZ == 2
+    return (row & 7) ^ ((row >> 3) & 1);
+#else
+    // rows sharing one 256-byte bank sweep get distinct keys
+    return row / (128 / BK);
+#endif
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (swz_key(row) & (BK / 8 - 1))) << 3); }
 
 // Workgroup -> (row tile, column tile).  Returns false when there is no tile.
 __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int &tn) {
     const int total = m_tiles * n_tiles;
     const int per = (total + 7) >> 3;
-    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
+    const int b = blockIdx.x, idx = b >> 3;
     if (idx >= per) return false;
-    const int logical = xcd * per + idx;
+#if OCC_XCD_MAP
+    const int logical = (b & 7) * per + idx;
+#else
+    const int logical = b;
+#endif
     if (logical >= total) return false;
     tm = logical / n_tiles;
     tn = logical - tm * n_tiles;
@@ -126,54 +169,68 @@ __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB
 }
 
 // K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
-// rows at k = 0 (chunk offset included); b_kstep(k0) gives the extra offset
-// of the K slice starting at k0 for B (handles the shared experts' K blocks).
-template <typename BOff>
+// rows at k = 0 (chunk offset included).  B is laid out as blocks of
+// ksp-wide K ranges, blk elements apart (the shared experts' down weights);
+// a single block (ksp = K) is the plain case.  The staging registers are
+// plain arrays indexed with constants only, so they stay in VGPRs.
 __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
-                                       const uint16_t *const (&b_src)[B_LD], int K, BOff b_koff,
-                                       uint16_t *sA, uint16_t *sB, int wm,
-                                       const int (&brow)[NI], f32x4_t (&acc)[MI][NI]) {
-    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
-    uint4 ra[A_LD], rb[B_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i]);
-#pragma unroll
-    for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + b_koff(0));
+                                       const uint16_t *const (&b_src)[B_LD], int K, int ksp,
+                                       size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
+                                       f32x4_t (&acc)[MI][NI]) {
+    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
+    u32x4 ra[A_LD], rb[B_LD];
     const int nk = K / BK;
-    for (int kt = 0; kt < nk; kt++) {
-        __syncthreads();
+#pragma unroll
+    for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i]);
+#pragma unroll
+    for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i]);
+    {
+        uint16_t *sA = smem, *sB = smem + BM * BK;
 #pragma unroll
         for (int i = 0; i < A_LD; i++)
-            *reinterpret_cast<uint4 *>(sA + swz(r0 + i * (NT / 8), chunk)) = ra[i];
+            *reinterpret_cast<u32x4 *>(sA + swz(r0 + i * ROWS_PER_PASS, chunk)) = ra[i];
 #pragma unroll
         for (int i = 0; i < B_LD; i++)
-            *reinterpret_cast<uint4 *>(sB + swz(r0 + i * (NT / 8), chunk)) = rb[i];
-        __syncthreads();
-        if (kt + 1 < nk) {
+            *reinterpret_cast<u32x4 *>(sB + swz(r0 + i * ROWS_PER_PASS, chunk)) = rb[i];
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
             const int k0 = (kt + 1) * BK;
+            const size_t bo = static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp);
 #pragma unroll
-            for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + k0);
-            const size_t bo = b_koff(k0);
+            for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
 #pragma unroll
-            for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + bo);
+            for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + bo);
         }
-        mma_slice(sA, sB, wm, brow, acc);
+        mma_slice(smem + cur * STAGE, smem + cur * STAGE + BM * BK, wm, brow, acc);
+        if (more) {
+            uint16_t *sA = smem + (cur ^ 1) * STAGE, *sB = sA + BM * BK;
+#pragma unroll
+            for (int i = 0; i < A_LD; i++)
+                *reinterpret_cast<u32x4 *>(sA + swz(r0 + i * ROWS_PER_PASS, chunk)) = ra[i];
+#pragma unroll
+            for (int i = 0; i < B_LD; i++)
+                *reinterpret_cast<u32x4 *>(sB + swz(r0 + i * ROWS_PER_PASS, chunk)) = rb[i];
+        }
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(NT) void k_gemm_up(UpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[BN * BK];
+__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
 
-    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
+    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
-        const int r = min(r0 + i * (NT / 8), t.rows - 1);
+        const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
         const int row = t.seg + t.m0 + r;
         const int src = a.a_rows ? a.a_rows[row] : row;
         a_src[i] = A + static_cast<size_t>(src) * K + chunk * 8;
@@ -183,7 +240,7 @@ __global__ __launch_bounds__(NT) void k_gemm_up(UpArgs a) {
     const uint16_t *b_src[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
-        const int rb = r0 + i * (NT / 8);
+        const int rb = r0 + i * ROWS_PER_PASS;
         const int f = min(t.n0 + (rb & 127), N - 1);
         b_src[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + chunk * 8;
     }
@@ -199,41 +256,48 @@ __global__ __launch_bounds__(NT) void k_gemm_up(UpArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    k_loop(a_src, b_src, K, [](int k0) { return static_cast<size_t>(k0); }, sA, sB, wm, brow, acc);
+    k_loop(a_src, b_src, K, K, 0, smem, wm, brow, acc);
 
-    uint16_t *out = static_cast<uint16_t *>(a.out);
+    // SwiGLU + modulation in registers, bf16 tile staged in LDS (the K
+    // buffers are free after the loop's last barrier).
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
-            if (r >= t.rows) continue;
-            const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
-            const float wr = a.row_w ? a.row_w[row] : 1.f;
+            const int rr = min(r, t.rows - 1);
+            const float wr = a.row_w ? a.row_w[t.seg + t.m0 + rr] : 1.f;
 #pragma unroll
             for (int ni = 0; ni < NI / 2; ni++) {
-                const int f = t.n0 + wn * 64 + ni * 16 + (l & 15);
-                if (f >= N) continue;
                 const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];
                 const float h = g / (1.f + __expf(-g)) * u * wr;
-                out[row * N + f] = f32_to_bf16_bits(h);
+                smem[r * OUT_PITCH + wn * 64 + ni * 16 + (l & 15)] = f32_to_bf16_bits(h);
             }
         }
+    __syncthreads();
+    uint16_t *out = static_cast<uint16_t *>(a.out);
+    constexpr int CH = 128 / 8;  // 16-byte chunks per staged row
+#pragma unroll 4
+    for (int i = tid; i < BM * CH; i += NT) {
+        const int r = i / CH, c = (i % CH) * 8;
+        if (r >= t.rows || t.n0 + c >= N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * OUT_PITCH + c);
+        *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(t.seg) + t.m0 + r) * N + t.n0 + c) = v;
+    }
 }
 
-__global__ __launch_bounds__(NT) void k_gemm_down(DownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[BN * BK];
+__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t)) return;
 
-    const int tid = threadIdx.x, chunk = tid & 7, r0 = tid >> 3;
+    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N, ksp = a.k_split;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
-        const int r = min(r0 + i * (NT / 8), t.rows - 1);
+        const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
         a_src[i] = A + (static_cast<size_t>(t.seg) + t.m0 + r) * K + chunk * 8;
     }
     // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
@@ -241,7 +305,7 @@ __global__ __launch_bounds__(NT) void k_gemm_down(DownArgs a) {
     const uint16_t *b_src[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
-        const int n = min(t.n0 + r0 + i * (NT / 8), N - 1);
+        const int n = min(t.n0 + r0 + i * ROWS_PER_PASS, N - 1);
         b_src[i] = W + static_cast<size_t>(n) * ksp + chunk * 8;
     }
     const size_t blk = static_cast<size_t>(N) * ksp;
@@ -256,9 +320,7 @@ __global__ __launch_bounds__(NT) void k_gemm_down(DownArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    k_loop(a_src, b_src, K,
-           [=](int k0) { return static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp); },
-           sA, sB, wm, brow, acc);
+    k_loop(a_src, b_src, K, ksp, blk, smem, wm, brow, acc);
 
     float *out = a.out;
 #pragma unroll

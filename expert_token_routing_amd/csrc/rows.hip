@@ -20,19 +20,19 @@ namespace {
 constexpr int kRowWaves = 4;  // token rows per workgroup
 
 template <int VPL>
-__global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const uint4 *__restrict__ x, int T,
+__global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const u32x4 *__restrict__ x, int T,
                                                                int Nd, int row_vec,
                                                                const int32_t *__restrict__ brim0,
-                                                               uint4 *__restrict__ x_sfd) {
+                                                               u32x4 *__restrict__ x_sfd) {
     const int lane = lane_id();
     const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
     if (t >= T) return;
     const int br = lane < Nd ? brim0[static_cast<size_t>(lane) * T + t] : -1;
-    uint4 v[VPL];
+    u32x4 v[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
-        const int c = lane + kWave * i;
-        if (c < row_vec) v[i] = x[static_cast<size_t>(t) * row_vec + c];
+        const int c = min(lane + kWave * i, row_vec - 1);
+        v[i] = x[static_cast<size_t>(t) * row_vec + c];
     }
     for (int g = 0; g < Nd; g++) {
         const int r = __shfl(br, g);
@@ -127,8 +127,8 @@ hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const
     const int row_vec = static_cast<int>(row_bytes / 16);
     const int vpl = (row_vec + kWave - 1) / kWave;
     const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
-    const uint4 *xs = static_cast<const uint4 *>(x);
-    uint4 *xd = static_cast<uint4 *>(x_sfd);
+    const u32x4 *xs = static_cast<const u32x4 *>(x);
+    u32x4 *xd = static_cast<u32x4 *>(x_sfd);
     if (vpl <= 1) k_dispatch<1><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
     else if (vpl <= 2) k_dispatch<2><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
     else if (vpl <= 4) k_dispatch<4><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
