@@ -60,30 +60,37 @@ constexpr int ROWS_PER_PASS = NT / CHUNKS;  // rows one pass of the workgroup mo
 constexpr int A_LD = BM / ROWS_PER_PASS;
 constexpr int B_LD = BN / ROWS_PER_PASS;
 constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per LDS buffer
-constexpr int OUT_PITCH = 128 + 8;       // up epilogue staging row (elements)
-static_assert(2 * STAGE * 2 <= 160 * 1024, "LDS");
-static_assert(BM * OUT_PITCH <= 2 * STAGE, "epilogue staging fits in the K buffers");
-
-#ifndef OCC_SWZ
-#define OCC_SWZ 3
+#ifndef OCC_GEMM_DMA
+#define OCC_GEMM_DMA 1
 #endif
-// Chunk c of row r sits at chunk slot c ^ f(r).  A 16-byte fragment read
-// covers 16 consecutive rows at one logical chunk; f must send them to 16
-// distinct bank groups of the 64-bank LDS (rows of 128 bytes put odd rows in
-// the upper half) and to 8 distinct groups within each 8-row half.
-__device__ __forceinline__ int swz_key(int row) {
-#if OCC_SWZ == 0
-    return row & 7;
-#elif OCC_SWZ == 1
-    return (row >> 1) & 7;
-#elif OCC_SWZ == 2
-    return (row & 7) ^ ((row >> 3) & 1);
+#if OCC_GEMM_DMA
+constexpr int NSTAGE = 3;                // LDS ring filled by direct global->LDS loads
+static_assert(BK == 32 && NT == 256, "the DMA loader moves 16 rows of 64 bytes per wave load");
 #else
-    // rows sharing one 256-byte bank sweep get distinct keys
-    return row / (128 / BK);
+constexpr int NSTAGE = 2;
 #endif
-}
+constexpr int OUT_PITCH = 128 + 8;       // up epilogue staging row (elements)
+static_assert(NSTAGE * STAGE * 2 * OCC_GEMM_WG_PER_CU <= 160 * 1024, "LDS");
+static_assert(BM * OUT_PITCH <= NSTAGE * STAGE, "epilogue staging fits in the K buffers");
+
+// Chunk c of row r sits at chunk slot c ^ ((r >> 1) mod chunks-per-row).  A
+// 16-byte fragment read covers 16 consecutive rows at one logical chunk;
+// measured on gfx950 (one workgroup timing ds_read_b128 patterns), this key
+// reads such a fragment without bank conflicts for both 64- and 128-byte
+// rows, while r mod 4 or (r >> 2) mod 4 on 64-byte rows cost 35-45% more
+// LDS time.
+__device__ __forceinline__ int swz_key(int row) { return row >> 1; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (swz_key(row) & (BK / 8 - 1))) << 3); }
+
+// The K chunk of tile row `row` that this thread fetches.  Thread t moves
+// rows (t / CHUNKS) + i * ROWS_PER_PASS, i.e. wave w owns 16-row groups; with
+// register staging it fetches logical chunk t % CHUNKS and stores it at its
+// swizzled slot; the direct loads write LDS slot t % CHUNKS, so they fetch
+// the logical chunk that belongs there.
+__device__ __forceinline__ int fetch_chunk(int row) {
+    const int c = threadIdx.x % CHUNKS;
+    return OCC_GEMM_DMA ? (c ^ (swz_key(row) & (CHUNKS - 1))) : c;
+}
 
 // Workgroup -> (row tile, column tile).  Returns false when there is no tile.
 __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int &tn) {
@@ -168,6 +175,66 @@ __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB
     }
 }
 
+#if OCC_GEMM_DMA
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).  m0 must be
+// wave-uniform.  Issued as inline assembly because the compiler's builtin
+// does not model the LDS write; completion is tracked with vmcnt below.  M0
+// is reserved by the compiler, which these kernels never use it for (checked
+// in their assembly), so it is set here without a clobber.
+__device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
+// fetch chunk of its rows at k = 0.  A ring of NSTAGE LDS buffers is filled
+// by direct loads: slice kt+2 is issued right after the barrier that opens
+// slice kt, so each load has two slices of MFMA work to land, and the
+// barrier also certifies that every wave has finished reading the buffer it
+// overwrites (slice kt-1's).  B is laid out as blocks of ksp-wide K ranges,
+// blk elements apart (the shared experts' down weights); one block (ksp = K)
+// is the plain case.
+__device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
+                                       const uint16_t *const (&b_src)[B_LD], int K, int ksp,
+                                       size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
+                                       f32x4_t (&acc)[MI][NI]) {
+    constexpr int LOADS = A_LD + B_LD;
+    const int nk = K / BK;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
+    auto issue = [&](int kt) {
+        const int k0 = kt * BK;
+        const size_t bo = ksp == K ? static_cast<size_t>(k0)
+                                   : static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp);
+        const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
+#pragma unroll
+        for (int i = 0; i < A_LD; i++)
+            dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + ((i * (NT / kWave) + w) * 16) * BK * 2));
+#pragma unroll
+        for (int i = 0; i < B_LD; i++)
+            dma16(b_src[i] + bo, __builtin_amdgcn_readfirstlane(st + BM * BK * 2 + ((i * (NT / kWave) + w) * 16) * BK * 2));
+    };
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; kt++) {
+        if (kt + 1 < nk) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + 2 < nk) issue(kt + 2);
+        uint16_t *buf = smem + (kt % NSTAGE) * STAGE;
+        mma_slice(buf, buf + BM * BK, wm, brow, acc);
+    }
+    __syncthreads();
+}
+#else
 // K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
 // rows at k = 0 (chunk offset included).  B is laid out as blocks of
 // ksp-wide K ranges, blk elements apart (the shared experts' down weights);
@@ -218,9 +285,10 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
         __syncthreads();
     }
 }
+#endif
 
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
 
@@ -233,7 +301,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
         const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
         const int row = t.seg + t.m0 + r;
         const int src = a.a_rows ? a.a_rows[row] : row;
-        a_src[i] = A + static_cast<size_t>(src) * K + chunk * 8;
+        a_src[i] = A + static_cast<size_t>(src) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
     const uint16_t *Wg = static_cast<const uint16_t *>(a.Wg) + static_cast<size_t>(t.e) * N * K;
     const uint16_t *Wu = static_cast<const uint16_t *>(a.Wu) + static_cast<size_t>(t.e) * N * K;
@@ -242,7 +310,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
     for (int i = 0; i < B_LD; i++) {
         const int rb = r0 + i * ROWS_PER_PASS;
         const int f = min(t.n0 + (rb & 127), N - 1);
-        b_src[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + chunk * 8;
+        b_src[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + fetch_chunk(rb) * 8;
     }
 
     const int l = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
@@ -287,7 +355,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
 }
 
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t)) return;
 
@@ -298,7 +366,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
         const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
-        a_src[i] = A + (static_cast<size_t>(t.seg) + t.m0 + r) * K + chunk * 8;
+        a_src[i] = A + (static_cast<size_t>(t.seg) + t.m0 + r) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
     // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
     const uint16_t *W = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(t.e) * N * K;
@@ -306,7 +374,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
         const int n = min(t.n0 + r0 + i * ROWS_PER_PASS, N - 1);
-        b_src[i] = W + static_cast<size_t>(n) * ksp + chunk * 8;
+        b_src[i] = W + static_cast<size_t>(n) * ksp + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
     const size_t blk = static_cast<size_t>(N) * ksp;
 
