@@ -23,14 +23,15 @@ int tile_rows(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? kGemmBmBf1
 // Byte offsets of every buffer inside the workspace.  Sized for the worst
 // case N_sfd = T * min(k, Nd), so no data-dependent size is read back.
 struct Layout {
-    size_t ids, w, brim0, sfd_off, epd_off, tile_off, chunk_cnt, chunk_base, epd_src, epd_w,
-        tok_epd, brim1, brim_end, x_sfd, epd, sfd_out, h_sh, y_sh, total;
+    size_t ids, w, brim0, sfd_off, epd_off, tile_off, tile_off_first, tile_off_rest, first_cnt,
+        chunk_cnt, chunk_base, epd_src, epd_w, tok_epd, down_rows, brim1, brim_end, x_sfd, epd,
+        sfd_out, h_sh, y_sh, total;
 };
 
 Layout layout(const occ_layer_desc &D) {
     const size_t T = D.T, k = D.k, Nd = D.Nd, Ne = D.Ne, d = D.d, F = D.F, es = elem_bytes(D);
     const size_t n = Ne / Nd, nsfd_max = T * std::min(k, Nd), nepd = T * k;
-    const size_t nchunks = (T + kBrimChunk - 1) / kBrimChunk, nb = Nd + Ne;
+    const size_t nchunks = (T + kBrimChunk - 1) / kBrimChunk, nb = Nd + 2 * Ne;
     Layout L{};
     size_t o = 0;
     auto take = [&o](size_t bytes) {
@@ -44,11 +45,15 @@ Layout layout(const occ_layer_desc &D) {
     L.sfd_off = take((Nd + 1) * 4);
     L.epd_off = take((Ne + 1) * 4);
     L.tile_off = take((Ne + 1) * 4);
+    L.tile_off_first = take((Ne + 1) * 4);
+    L.tile_off_rest = take((Ne + 1) * 4);
+    L.first_cnt = take(Ne * 4);
     L.chunk_cnt = take(nchunks * nb * 4);
     L.chunk_base = take(nchunks * nb * 4);
     L.epd_src = take(nepd * 4);
     L.epd_w = take(nepd * 4);
     L.tok_epd = take(nepd * 4);
+    L.down_rows = take(nepd * 4);
     L.brim1 = take(n * nsfd_max * 4);
     L.brim_end = o;
     L.x_sfd = take(nsfd_max * d * es);
@@ -128,6 +133,8 @@ occ_brim brim_view(void *ws, const Layout &L) {
     b.epd_w = at<float>(ws, L.epd_w);
     b.tok_epd = at<int32_t>(ws, L.tok_epd);
     b.brim1 = at<int32_t>(ws, L.brim1);
+    b.down_rows = at<int32_t>(ws, L.down_rows);
+    b.first_cnt = at<int32_t>(ws, L.first_cnt);
     b.tile_off = at<int32_t>(ws, L.tile_off);
     return b;
 }
@@ -142,6 +149,10 @@ BrimBufs brim_bufs(void *ws, const Layout &L) {
     b.tok_epd = at<int32_t>(ws, L.tok_epd);
     b.brim1 = at<int32_t>(ws, L.brim1);
     b.epd_w = at<float>(ws, L.epd_w);
+    b.down_rows = at<int32_t>(ws, L.down_rows);
+    b.first_cnt = at<int32_t>(ws, L.first_cnt);
+    b.tile_off_first = at<int32_t>(ws, L.tile_off_first);
+    b.tile_off_rest = at<int32_t>(ws, L.tile_off_rest);
     b.chunk_cnt = at<int32_t>(ws, L.chunk_cnt);
     b.chunk_base = at<int32_t>(ws, L.chunk_base);
     return b;
@@ -254,7 +265,7 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     void *epd = at<void>(workspace, L.epd);
     float *sfd_out = at<float>(workspace, L.sfd_out);
     float *y_sh = D.n_shared > 0 ? at<float>(workspace, L.y_sh) : nullptr;
-    const size_t T = D.T, nsfd_max = T * std::min(D.k, D.Nd);
+    const size_t T = D.T;
     const size_t bm = tile_rows(D);
     const size_t routed_tiles = (T * D.k + bm - 1) / bm + D.Ne;
     const size_t shared_tiles = (T + bm - 1) / bm;
@@ -313,15 +324,15 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     up.tab = tab;
     OCC_HIP(bf16 ? launch_gemm_up_bf16(up, routed_tiles, s) : launch_gemm_up_f32(up, routed_tiles, s));
     OCC_TRY(mark(5));
-    // Algorithm 8 starts from a zero fp32 SFD tensor (only the N_sfd used rows)
-    OCC_HIP(launch_zero_rows(sfd_out, bb.sfd_off + D.Nd, nsfd_max, D.d, s));
-    OCC_TRY(mark(6));
-    // Algorithm 8: EPD -> SFD, summed inside each group in fp32
+    // Algorithm 8: EPD -> SFD, summed inside each group in fp32.  The first
+    // contributor to every SFD row stores (so no zero-fill is needed), then
+    // the other rows of the group add with atomics.
     DownArgs dn{};
     dn.A = epd;
     dn.W = w_down;
     dn.seg_off = bb.epd_off;
-    dn.tile_off = bb.tile_off;
+    dn.rows = bb.down_rows;
+    dn.first_cnt = bb.first_cnt;
     dn.dst_rows = bb.epd_src;
     dn.out = sfd_out;
     dn.M = D.T * D.k;
@@ -330,6 +341,12 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     dn.Ne = D.Ne;
     dn.k_split = D.F;
     dn.tab = tab;
+    dn.phase = 1;
+    dn.tile_off = bb.tile_off_first;
+    OCC_HIP(bf16 ? launch_gemm_down_bf16(dn, routed_tiles, s) : launch_gemm_down_f32(dn, routed_tiles, s));
+    OCC_TRY(mark(6));
+    dn.phase = 2;
+    dn.tile_off = bb.tile_off_rest;
     OCC_HIP(bf16 ? launch_gemm_down_bf16(dn, routed_tiles, s) : launch_gemm_down_f32(dn, routed_tiles, s));
     OCC_TRY(mark(7));
     // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once

@@ -7,11 +7,15 @@
 // experts lives on group g) and Ne expert bins, in placement order, for
 // BRIM_1 (the group-local counter of Algorithm 5 is the global EPD row minus
 // the group's first EPD row, because groups' EPD blocks are laid end to end).
+// A third family of Ne bins counts, per expert, the EPD rows that are the
+// first contributor to their SFD row (the token's lowest-slot expert in that
+// group); it orders each expert's rows for the down-projection merge: first
+// contributors, then the rest, each in token order.
 //
 //   k_brim_count  per chunk of 1024 tokens, the token count of every bin;
 //   k_brim_scan   one workgroup: exclusive scans over chunks and over bins,
 //                 giving each (chunk, bin) its first row, plus sfd_off,
-//                 epd_off and the GEMM row-tile schedule;
+//                 epd_off, first-contributor counts and GEMM tile schedules;
 //   k_brim_fill   per chunk: a token's rank inside a bin is the popcount of
 //                 the lower lanes' bits in a per-wave 64-bit mask (built with
 //                 LDS atomic OR, so the result does not depend on timing)
@@ -28,26 +32,40 @@ __device__ __forceinline__ bool has_pos(const uint64_t (&em)[4], int p) {
     return (em[p >> 6] >> (p & 63)) & 1ull;
 }
 
+// Is placement position p (one of the token's experts, mask em) the token's
+// lowest position inside p's group?  Positions g*n .. g*n+n-1 form group g.
+__device__ __forceinline__ bool first_in_group(const uint64_t (&em)[4], int p, int n) {
+    for (int q = (p / n) * n; q < p; q++)
+        if (has_pos(em, q)) return false;
+    return true;
+}
+
 __global__ __launch_bounds__(kBrimChunk) void k_brim_count(const int32_t *__restrict__ ids, int T,
                                                            int k, PlaceTab tab,
                                                            int32_t *__restrict__ chunk_cnt) {
     __shared__ int cnt[kMaxBins];
     __shared__ uint8_t s_grp[kMaxNe];
     __shared__ int16_t s_pos[kMaxNe];
-    const int Nd = tab.Nd, Ne = tab.Ne, NB = Nd + Ne;
+    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
     for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
     for (int e = threadIdx.x; e < Ne; e += blockDim.x) {
         s_grp[e] = tab.grp[e];
-        s_pos[e] = static_cast<int16_t>(tab.grp[e] * tab.n + tab.slot[e]);
+        s_pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
     }
     __syncthreads();
     const int t = blockIdx.x * kBrimChunk + threadIdx.x;
     if (t < T) {
-        uint64_t gmask = 0;
+        uint64_t gmask = 0, em[4] = {0, 0, 0, 0};
         for (int j = 0; j < k; j++) {
             const int e = ids[static_cast<size_t>(t) * k + j];
-            atomicAdd(&cnt[Nd + s_pos[e]], 1);
+            const int p = s_pos[e];
+            em[p >> 6] |= 1ull << (p & 63);
+            atomicAdd(&cnt[Nd + p], 1);
             gmask |= 1ull << s_grp[e];
+        }
+        for (int j = 0; j < k; j++) {
+            const int p = s_pos[ids[static_cast<size_t>(t) * k + j]];
+            if (first_in_group(em, p, n)) atomicAdd(&cnt[Nd + Ne + p], 1);
         }
         while (gmask) {
             const int g = __ffsll(static_cast<unsigned long long>(gmask)) - 1;
@@ -65,10 +83,13 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ chunk_base,
                                                     int32_t *__restrict__ sfd_off,
                                                     int32_t *__restrict__ epd_off,
-                                                    int32_t *__restrict__ tile_off) {
+                                                    int32_t *__restrict__ tile_off,
+                                                    int32_t *__restrict__ first_cnt,
+                                                    int32_t *__restrict__ tile_off_first,
+                                                    int32_t *__restrict__ tile_off_rest) {
     __shared__ int total[kMaxBins];
     __shared__ int binoff[kMaxBins];
-    const int NB = Nd + Ne;
+    const int NB = Nd + 2 * Ne;
     const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
 
     // 1. per bin, exclusive scan over chunks (64 chunks per wave step)
@@ -85,8 +106,10 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     }
     __syncthreads();
 
-    // 2. across bins: groups give sfd_off, experts (placement order) epd_off,
-    //    and ceil(load / tile_rows) gives the GEMM row-tile schedule.
+    // 2. across bins: groups give sfd_off; experts (placement order) give
+    //    epd_off; first-contributor bins start at their expert's first EPD
+    //    row.  ceil(rows / tile_rows) gives the GEMM row-tile schedules: all
+    //    rows (up-projection), first contributors and the rest (merge).
     if (wv == 0) {
         const int vg = lane < Nd ? total[lane] : 0;
         const int ig = wave_incl_scan(vg);
@@ -95,23 +118,35 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
             sfd_off[lane] = ig - vg;
         }
         if (lane == kWave - 1) sfd_off[Nd] = ig;
-        int run = 0, run_t = 0;
+        int run = 0, run_t = 0, run_f = 0, run_r = 0;
         for (int p0 = 0; p0 < Ne; p0 += kWave) {
             const int p = p0 + lane;
             const int v = p < Ne ? total[Nd + p] : 0;
+            const int f = p < Ne ? total[Nd + Ne + p] : 0;
             const int vt = (v + tile_rows - 1) / tile_rows;
+            const int vf = (f + tile_rows - 1) / tile_rows;
+            const int vr = (v - f + tile_rows - 1) / tile_rows;
             const int inc = wave_incl_scan(v), inc_t = wave_incl_scan(vt);
+            const int inc_f = wave_incl_scan(vf), inc_r = wave_incl_scan(vr);
             if (p < Ne) {
                 binoff[Nd + p] = run + inc - v;
+                binoff[Nd + Ne + p] = run + inc - v;
                 epd_off[p] = run + inc - v;
                 tile_off[p] = run_t + inc_t - vt;
+                tile_off_first[p] = run_f + inc_f - vf;
+                tile_off_rest[p] = run_r + inc_r - vr;
+                first_cnt[p] = f;
             }
             run += __shfl(inc, kWave - 1);
             run_t += __shfl(inc_t, kWave - 1);
+            run_f += __shfl(inc_f, kWave - 1);
+            run_r += __shfl(inc_r, kWave - 1);
         }
         if (lane == 0) {
             epd_off[Ne] = run;
             tile_off[Ne] = run_t;
+            tile_off_first[Ne] = run_f;
+            tile_off_rest[Ne] = run_r;
         }
     }
     __syncthreads();
@@ -124,15 +159,16 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
 __global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
     const int32_t *__restrict__ ids, const float *__restrict__ w, int T, int k, PlaceTab tab,
     const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ sfd_off,
-    const int32_t *__restrict__ epd_off, int dense, int32_t *__restrict__ brim0,
-    int32_t *__restrict__ epd_src, float *__restrict__ epd_w, int32_t *__restrict__ tok_epd,
+    const int32_t *__restrict__ epd_off, const int32_t *__restrict__ first_cnt, int dense,
+    int32_t *__restrict__ brim0, int32_t *__restrict__ epd_src, float *__restrict__ epd_w,
+    int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows,
     int32_t *__restrict__ brim1) {
     __shared__ unsigned long long wmask[kWavesPerChunk][kMaxBins];
     __shared__ int wpre[kWavesPerChunk][kMaxBins];
     __shared__ int s_base[kMaxBins];
     __shared__ uint8_t s_grp[kMaxNe];
     __shared__ int16_t s_pos[kMaxNe];
-    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + Ne;
+    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
     for (int i = threadIdx.x; i < kWavesPerChunk * NB; i += blockDim.x)
         wmask[i / NB][i % NB] = 0ull;
     for (int b = threadIdx.x; b < NB; b += blockDim.x)
@@ -156,6 +192,10 @@ __global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
             gmask |= 1ull << s_grp[e];
             atomicOr(&wmask[wv][Nd + p], bit);
         }
+        for (int j = 0; j < k; j++) {
+            const int p = s_pos[ids[static_cast<size_t>(t) * k + j]];
+            if (first_in_group(em, p, n)) atomicOr(&wmask[wv][Nd + Ne + p], bit);
+        }
         for (uint64_t m = gmask; m; m &= m - 1)
             atomicOr(&wmask[wv][__ffsll(static_cast<unsigned long long>(m)) - 1], bit);
     }
@@ -170,20 +210,24 @@ __global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
     __syncthreads();
     if (!valid) return;
 
-    for (int g = 0; g < Nd; g++) {
-        const int row = ((gmask >> g) & 1ull)
-                            ? s_base[g] + wpre[wv][g] + __popcll(wmask[wv][g] & lower)
-                            : -1;
-        brim0[static_cast<size_t>(g) * T + t] = row;
-    }
+    // rank of this token among the chunk-ordered tokens of bin b
+    auto slot_of = [&](int b) { return s_base[b] + wpre[wv][b] + __popcll(wmask[wv][b] & lower); };
+
+    for (int g = 0; g < Nd; g++)
+        brim0[static_cast<size_t>(g) * T + t] = ((gmask >> g) & 1ull) ? slot_of(g) : -1;
     for (int j = 0; j < k; j++) {
         const size_t o = static_cast<size_t>(t) * k + j;
         const int p = s_pos[ids[o]], g = p / n;
-        const int srow = s_base[g] + wpre[wv][g] + __popcll(wmask[wv][g] & lower);
-        const int erow = s_base[Nd + p] + wpre[wv][Nd + p] + __popcll(wmask[wv][Nd + p] & lower);
+        const int srow = slot_of(g);
+        const int erow = slot_of(Nd + p);
         epd_src[erow] = srow;
         epd_w[erow] = w[o];
         tok_epd[o] = erow;
+        // merge order: first contributors of expert p, then its other rows
+        const int e0 = epd_off[p];
+        const int f_before = slot_of(Nd + Ne + p);  // e0 + first rows of p before t
+        if (first_in_group(em, p, n)) down_rows[f_before] = erow;
+        else down_rows[e0 + first_cnt[p] + (erow - e0) - (f_before - e0)] = erow;
         if (dense) {
             const int g0 = sfd_off[g], Ng = sfd_off[g + 1] - g0;
             brim1[static_cast<size_t>(n) * g0 + static_cast<size_t>(p - g * n) * Ng + (srow - g0)] =
@@ -194,7 +238,7 @@ __global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
         for (uint64_t m = gmask; m; m &= m - 1) {
             const int g = __ffsll(static_cast<unsigned long long>(m)) - 1;
             const int g0 = sfd_off[g], Ng = sfd_off[g + 1] - g0;
-            const int srow = s_base[g] + wpre[wv][g] + __popcll(wmask[wv][g] & lower);
+            const int srow = slot_of(g);
             for (int j = 0; j < n; j++)
                 if (!has_pos(em, g * n + j))
                     brim1[static_cast<size_t>(n) * g0 + static_cast<size_t>(j) * Ng + (srow - g0)] = -1;
@@ -209,10 +253,12 @@ hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const P
     const int nchunks = static_cast<int>(ceil_div(T, kBrimChunk));
     k_brim_count<<<nchunks, kBrimChunk, 0, s>>>(ids, T, k, tab, b.chunk_cnt);
     k_brim_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, tab.Nd, tab.Ne, tile_rows, b.chunk_base,
-                                   b.sfd_off, b.epd_off, b.tile_off);
+                                   b.sfd_off, b.epd_off, b.tile_off, b.first_cnt,
+                                   b.tile_off_first, b.tile_off_rest);
     k_brim_fill<<<nchunks, kBrimChunk, 0, s>>>(ids, w, T, k, tab, b.chunk_base, b.sfd_off,
-                                               b.epd_off, dense_brim1, b.brim0, b.epd_src,
-                                               b.epd_w, b.tok_epd, b.brim1);
+                                               b.epd_off, b.first_cnt, dense_brim1, b.brim0,
+                                               b.epd_src, b.epd_w, b.tok_epd, b.down_rows,
+                                               b.brim1);
     return hipGetLastError();
 }
 

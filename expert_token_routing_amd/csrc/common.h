@@ -16,7 +16,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kMaxNe = 256;
 constexpr int kMaxNd = 64;
 constexpr int kMaxK = 32;
-constexpr int kMaxBins = kMaxNd + kMaxNe;  // BRIM scan bins: groups, then experts
+constexpr int kMaxBins = kMaxNd + 2 * kMaxNe;  // BRIM bins: groups, experts, first contributors
 
 // Row tile of the grouped GEMMs (tokens per workgroup tile); the BRIM scan
 // lays out the per-expert tile schedule with it.

@@ -128,18 +128,25 @@ struct Tile {
     int n0;    // first column (output feature) of the tile
 };
 
+// Routed tiles walk expert segments [seg_off[p], seg_off[p+1]) -- all rows
+// (phase 0), the first first_cnt[p] rows (phase 1) or the rest (phase 2) --
+// with the phase's row-tile schedule tile_off; shared tiles (seg_off NULL)
+// walk M rows.
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
                                         int Ne, const PlaceTab &tab, int n_tiles, int n_step,
-                                        Tile &t) {
+                                        Tile &t, const int32_t *first_cnt = nullptr,
+                                        int phase = 0) {
     int tm, tn;
     if (seg_off) {
         const int m_tiles = tile_off[Ne];
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
         const int p = find_pos(tile_off, Ne, tm);
+        const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
+        const int nf = phase ? first_cnt[p] : 0;
         t.e = tab.expert[p];
-        t.seg = seg_off[p];
+        t.seg = phase == 2 ? seg0 + nf : seg0;
         t.m0 = (tm - tile_off[p]) * BM;
-        t.rows = min(BM, seg_off[p + 1] - t.seg - t.m0);
+        t.rows = min(BM, (phase == 1 ? nf : len - nf) - t.m0);
     } else {
         const int m_tiles = (M + BM - 1) / BM;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
 
-    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
+    const int tid = threadIdx.x, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
@@ -357,16 +364,20 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_up(UpArgs a) {
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     Tile t;
-    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t)) return;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t, a.first_cnt,
+                 a.phase))
+        return;
 
-    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
+    const int tid = threadIdx.x, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N, ksp = a.k_split;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
         const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
-        a_src[i] = A + (static_cast<size_t>(t.seg) + t.m0 + r) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
+        const int row = t.seg + t.m0 + r;
+        const int src = a.rows ? a.rows[row] : row;
+        a_src[i] = A + static_cast<size_t>(src) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
     // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
     const uint16_t *W = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(t.e) * N * K;
@@ -399,11 +410,20 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU) void k_gemm_down(DownArgs a
             if (r >= t.rows) continue;
             const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
             if (a.dst_rows) {
-                const size_t dst = static_cast<size_t>(a.dst_rows[row]) * N;
+                const int erow = a.rows ? a.rows[row] : static_cast<int>(row);
+                const size_t dst = static_cast<size_t>(a.dst_rows[erow]) * N;
+                if (a.phase == 1) {
 #pragma unroll
-                for (int ni = 0; ni < NI; ni++) {
-                    const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
-                    if (c < N) unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                    for (int ni = 0; ni < NI; ni++) {
+                        const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
+                        if (c < N) out[dst + c] = acc[mi][ni][v];
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < NI; ni++) {
+                        const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
+                        if (c < N) unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                    }
                 }
             } else {
 #pragma unroll

@@ -33,16 +33,21 @@ struct Tile {
     int e, seg, m0, rows, n0;
 };
 
+// Routed tiles walk expert segments [seg_off[p], seg_off[p+1]) -- all rows
+// (phase 0), the first first_cnt[p] rows (phase 1) or the rest (phase 2).
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
-                                        int Ne, const PlaceTab &tab, int n_tiles, Tile &t) {
+                                        int Ne, const PlaceTab &tab, int n_tiles, Tile &t,
+                                        const int32_t *first_cnt = nullptr, int phase = 0) {
     const int tm = blockIdx.x / n_tiles, tn = blockIdx.x % n_tiles;
     if (seg_off) {
         if (tm >= tile_off[Ne]) return false;
         const int p = find_pos(tile_off, Ne, tm);
+        const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
+        const int nf = phase ? first_cnt[p] : 0;
         t.e = tab.expert[p];
-        t.seg = seg_off[p];
+        t.seg = phase == 2 ? seg0 + nf : seg0;
         t.m0 = (tm - tile_off[p]) * BM;
-        t.rows = min(BM, seg_off[p + 1] - t.seg - t.m0);
+        t.rows = min(BM, (phase == 1 ? nf : len - nf) - t.m0);
     } else {
         if (tm * BM >= M) return false;
         t.e = 0;
@@ -126,11 +131,14 @@ __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
 __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
     __shared__ float sA[BK][BM + PAD], sB[BK][BN + PAD];
     Tile t;
-    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t)) return;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t, a.first_cnt,
+                 a.phase))
+        return;
     const int K = a.K, N = a.N, ksp = a.k_split;
     const int r_ld = threadIdx.x >> 2;
+    const int row_ld = t.seg + t.m0 + min(r_ld, t.rows - 1);
     const float *a_row = static_cast<const float *>(a.A) +
-                         (static_cast<size_t>(t.seg) + t.m0 + min(r_ld, t.rows - 1)) * K;
+                         static_cast<size_t>(a.rows ? a.rows[row_ld] : row_ld) * K;
     const int n_ld = min(t.n0 + r_ld, N - 1);
     const float *W = static_cast<const float *>(a.W) + static_cast<size_t>(t.e) * N * K;
     const size_t blk = static_cast<size_t>(N) * ksp;
@@ -161,12 +169,14 @@ __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
         const int r = ty + 16 * i;
         if (r >= t.rows) continue;
         const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
+        const int erow = a.rows ? a.rows[row] : static_cast<int>(row);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int c = t.n0 + tx + 16 * j;
             if (c >= N) continue;
-            if (a.dst_rows) unsafeAtomicAdd(a.out + static_cast<size_t>(a.dst_rows[row]) * N + c, acc[i][j]);
-            else a.out[row * N + c] = acc[i][j];
+            if (!a.dst_rows) a.out[row * N + c] = acc[i][j];
+            else if (a.phase == 1) a.out[static_cast<size_t>(a.dst_rows[erow]) * N + c] = acc[i][j];
+            else unsafeAtomicAdd(a.out + static_cast<size_t>(a.dst_rows[erow]) * N + c, acc[i][j]);
         }
     }
 }

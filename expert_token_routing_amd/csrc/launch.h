@@ -16,6 +16,7 @@ constexpr int kBrimChunk = 1024;  // tokens per BRIM workgroup
 struct BrimBufs {
     int32_t *brim0, *sfd_off, *epd_off, *tile_off, *epd_src, *tok_epd, *brim1;
     float *epd_w;
+    int32_t *down_rows, *first_cnt, *tile_off_first, *tile_off_rest;
     int32_t *chunk_cnt, *chunk_base;
 };
 hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
@@ -25,10 +26,6 @@ hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const P
 // x_sfd[brim0[g, t]] = x[t] for every group the token uses.
 hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
                            void *x_sfd, hipStream_t s);
-// Zero the first (*n_rows) rows of an fp32 matrix with `row_floats` columns;
-// the launch covers max_rows rows.
-hipError_t launch_zero_rows(float *p, const int32_t *n_rows, size_t max_rows, size_t row_floats,
-                            hipStream_t s);
 // y[t] = dtype( sum over g of sfd_out[brim0[g, t]] (+ y_sh[t]) ), fp32 sums in
 // ascending group order.
 hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const float *y_sh, int T,
@@ -53,17 +50,22 @@ struct UpArgs {
 };
 hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 
-// Down-projection.  Routed: out[dst_rows[r], :] += A[r] . W[e]^T (fp32
-// atomics; several experts of one group share an SFD row).  Shared
-// (seg_off NULL): out[r, :] = A[r] . W^T with W = n_sh blocks of (N x k_split)
-// laid end to end along K.
+// Down-projection.  Routed: the EPD rows of expert position p are
+// rows[seg_off[p] ..  seg_off[p+1]), first_cnt[p] of them first contributors
+// to their SFD row; phase 1 multiplies those and stores
+// out[dst_rows[r], :] = A[r] . W[e]^T, which writes every SFD row once;
+// phase 2 multiplies the others and adds with fp32 atomics (several experts
+// of one group share an SFD row).  tile_off is the phase's row-tile schedule.
+// Shared (seg_off NULL): out[r, :] = A[r] . W^T with W = n_sh blocks of
+// (N x k_split) laid end to end along K.
 struct DownArgs {
     const void *A;
     const void *W;
     const int32_t *seg_off, *tile_off;
+    const int32_t *rows, *first_cnt;
     const int32_t *dst_rows;
     float *out;
-    int M, K, N, Ne, k_split;
+    int M, K, N, Ne, k_split, phase;
     PlaceTab tab;
 };
 hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);

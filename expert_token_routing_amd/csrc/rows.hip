@@ -1,8 +1,6 @@
 // Memory-bound row movers of the Occult pipeline (paper, appendix A.2):
 //   dispatch  ORI -> SFD (Algorithm 4): each token row is read once and
 //             written once per group it uses, at BRIM_0[g, t];
-//   zero      the fp32 SFD output that the down-projection accumulates into
-//             (Algorithm 8 starts from a zero tensor);
 //   combine   SFD -> ORI (Algorithm 9): y[t] = sum over g of
 //             sfd_out[BRIM_0[g, t]], entries -1 skipped, summed in fp32 in
 //             ascending group order, plus the shared experts' fp32 output,
@@ -43,16 +41,6 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const u32x4 *__re
             if (c < row_vec) x_sfd[static_cast<size_t>(r) * row_vec + c] = v[i];
         }
     }
-}
-
-__global__ __launch_bounds__(256) void k_zero_rows(float4 *__restrict__ p,
-                                                   const int32_t *__restrict__ n_rows,
-                                                   size_t row_vec4) {
-    const size_t n = static_cast<size_t>(*n_rows) * row_vec4;
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * blockDim.x)
-        p[i] = z;
 }
 
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, size_t n, int32_t v) {
@@ -134,15 +122,6 @@ hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const
     else if (vpl <= 4) k_dispatch<4><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
     else if (vpl <= 8) k_dispatch<8><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
     else k_dispatch<16><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero_rows(float *p, const int32_t *n_rows, size_t max_rows, size_t row_floats,
-                            hipStream_t s) {
-    const size_t vec = max_rows * (row_floats / 4);
-    const unsigned grid = static_cast<unsigned>(std::min<size_t>(ceil_div(vec, 256 * 4), 8192));
-    k_zero_rows<<<grid > 0 ? grid : 1, 256, 0, s>>>(reinterpret_cast<float4 *>(p), n_rows,
-                                                    row_floats / 4);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(HERE, "libocc.so")
 OCC_OK, OCC_ERR_INVALID_ARG, OCC_ERR_UNSUPPORTED, OCC_ERR_WORKSPACE, OCC_ERR_HIP = range(5)
 OCC_F32, OCC_BF16 = 0, 1
 OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM = 0, 1, 2
-STAGES = ["route", "brim", "dispatch", "shared", "gemm_up", "merge_init", "gemm_down", "combine"]
+STAGES = ["route", "brim", "dispatch", "shared", "gemm_up", "gemm_down_first", "gemm_down_rest",
+          "combine"]
 OCC_STAGE_COUNT = len(STAGES)
 
 EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route", "occ_build_brim",
@@ -48,7 +49,8 @@ class Brim(ctypes.Structure):
     _fields_ = [("brim0", ctypes.c_void_p), ("sfd_off", ctypes.c_void_p),
                 ("epd_off", ctypes.c_void_p), ("epd_src", ctypes.c_void_p),
                 ("epd_w", ctypes.c_void_p), ("tok_epd", ctypes.c_void_p),
-                ("brim1", ctypes.c_void_p), ("tile_off", ctypes.c_void_p)]
+                ("brim1", ctypes.c_void_p), ("down_rows", ctypes.c_void_p),
+                ("first_cnt", ctypes.c_void_p), ("tile_off", ctypes.c_void_p)]
 
 
 class ForwardView(ctypes.Structure):

@@ -91,3 +91,107 @@ def traffic_bytes(kernel: str, workload: str, source: str) -> float | None:
     if rec.get("src_sha") != source_sha(source):
         return None
     return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
+
+
+def _fmt_ns(ns: float) -> str:
+    return f"{ns / 1e3:.1f}"
+
+
+def summarize_stats(out_dir: str, command: str, title: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    rows = kernel_stats(out_dir)
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average us | min us | max us | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {_fmt_ns(float(r['AverageNs']))} | "
+                     f"{_fmt_ns(float(r['MinNs']))} | {_fmt_ns(float(r['MaxNs']))} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str,
+                      workload: str, copy_bytes: int, sources: dict[str, str],
+                      title: str) -> str:
+    """HBM traffic per dispatch from FETCH_SIZE / WRITE_SIZE passes, scaled by
+    the reading for a plain device copy of `copy_bytes` (the largest
+    copyBuffer dispatches of the run)."""
+    fr, wr = counter_rows(fetch_dir), counter_rows(write_dir)
+
+    def per_kernel(rows, counter):
+        by: dict[str, list[tuple[float, str]]] = {}
+        for r in rows:
+            if (r.get("Counter_Name") or "") != counter:
+                continue
+            name = r.get("Kernel_Name") or ""
+            key = "copy" if "copyBuffer" in name else short_name(name)
+            by.setdefault(key, []).append(float(r.get("Counter_Value") or 0) * 1024.0)
+        return by
+
+    f, w = per_kernel(fr, "FETCH_SIZE"), per_kernel(wr, "WRITE_SIZE")
+    big = lambda xs: [x for x in xs if x >= 0.5 * copy_bytes]
+    fc, wc = big(f.get("copy", [])), big(w.get("copy", []))
+    if not fc or not wc:
+        raise RuntimeError("no calibration copy found in the counter runs")
+    f_scale = copy_bytes / (sum(fc) / len(fc))
+    w_scale = copy_bytes / (sum(wc) / len(wc))
+    lines = [f"# {title}", "", "Commands (run from the repository root on one MI355X):", "",
+             "```", fetch_cmd, write_cmd, "```", "",
+             f"Calibration: a plain device copy of {copy_bytes} bytes reads "
+             f"{sum(fc) / len(fc):.4g} B (FETCH_SIZE) and writes {sum(wc) / len(wc):.4g} B "
+             f"(WRITE_SIZE); scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+             "| kernel | dispatches | fetch MB / dispatch | write MB / dispatch |",
+             "|---|---|---|---|"]
+    recs = []
+    for k in sorted(set(f) | set(w)):
+        if k == "copy":
+            continue
+        fv, wv = f.get(k, [0.0]), w.get(k, [0.0])
+        fb, wb = f_scale * sum(fv) / len(fv), w_scale * sum(wv) / len(wv)
+        lines.append(f"| {k} | {len(fv)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        if k in sources:
+            recs.append({"kernel": k, "workload": workload, "fetch_bytes": round(fb),
+                         "write_bytes": round(wb), "src_sha": source_sha(sources[k]),
+                         "source": sources[k]})
+    lines.append("")
+    for rec in recs:
+        lines.append(f"<!-- occ-profile {json.dumps(rec)} -->")
+    return "\n".join(lines) + "\n"
+
+
+def _main(argv=None):
+    import argparse
+
+    ap = argparse.ArgumentParser(description="Summarize rocprofv3 output for profiles/")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--fetch-command", required=True)
+    t.add_argument("--write-command", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-bytes", type=int, default=1 << 30)
+    t.add_argument("--title", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        text = summarize_stats(a.dir, a.command, a.title)
+    else:
+        sources = {"k_gemm_up": "gemm_bf16.hip", "k_gemm_down": "gemm_bf16.hip",
+                   "k_dispatch": "rows.hip", "k_combine": "rows.hip",
+                   "k_route": "route.hip", "k_brim_fill": "brim.hip"}
+        text = summarize_traffic(a.fetch_dir, a.write_dir, a.fetch_command, a.write_command,
+                                 a.workload, a.copy_bytes, sources, a.title)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    _main()

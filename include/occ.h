@@ -102,6 +102,13 @@ typedef struct occ_layer_desc {
  *            row sfd_off[g]+t' for the group's j-th expert, or -1.  A counter
  *            restarts per group and runs over local experts outer, SFD rows
  *            inner.  Written only when dense BRIM_1 is requested.
+ *   down_rows T*k.  Each expert's EPD rows reordered for the merge of
+ *            Algorithm 8: first the rows that are the first contributor to
+ *            their SFD row (the token's lowest-slot expert in that group),
+ *            then the others, each in token order; expert p's rows occupy
+ *            [epd_off[p], epd_off[p+1]) and the first first_cnt[p] of them
+ *            are first contributors.
+ *   first_cnt Ne, indexed by placement position.
  *   tile_off Ne+1.  Row-tile schedule of the grouped GEMMs (internal). */
 typedef struct occ_brim {
     int32_t *brim0;
@@ -111,6 +118,8 @@ typedef struct occ_brim {
     float *epd_w;
     int32_t *tok_epd;
     int32_t *brim1;
+    int32_t *down_rows;
+    int32_t *first_cnt;
     int32_t *tile_off;
 } occ_brim;
 
@@ -138,8 +147,8 @@ enum {
     OCC_STAGE_DISPATCH = 2,
     OCC_STAGE_SHARED = 3,
     OCC_STAGE_GEMM_UP = 4,
-    OCC_STAGE_MERGE_INIT = 5,
-    OCC_STAGE_GEMM_DOWN = 6,
+    OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores */
+    OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds */
     OCC_STAGE_COMBINE = 7,
     OCC_STAGE_COUNT = 8
 };
@@ -182,7 +191,8 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const 
  *   route (Eq. 2) -> BRIM_0/BRIM_1 -> dispatch ORI->SFD (Alg. 4) ->
  *   SwiGLU up-projection SFD->EPD with the routing weight applied to the
  *   hidden state (Alg. 6-7) -> down-projection EPD->SFD summed inside each
- *   group in fp32 (Alg. 8) -> combine SFD->ORI summed across groups (Alg. 9).
+ *   group in fp32 (Alg. 8: the first contributor to each SFD row stores, the
+ *   others add) -> combine SFD->ORI summed across groups (Alg. 9).
  * Without pruning the result equals the plain top-k MoE output (section 3.2).
  *   x          T x d (dtype);  logits T x Ne fp32;  placement_host as above.
  *   w_gate     Ne x F x d;  w_up Ne x F x d;  w_down Ne x d x F (dtype).

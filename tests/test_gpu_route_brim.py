@@ -90,6 +90,7 @@ def gpu_brim(wl, ids_t, w_t, placement, dense=True):
     return dict(brim0=v(b.brim0, (Nd, T)), sfd_off=sfd_off, epd_off=v(b.epd_off, (Ne + 1,)),
                 epd_src=v(b.epd_src, (T * k,)), epd_w=v(b.epd_w, (T * k,), torch.float32),
                 tok_epd=v(b.tok_epd, (T, k)), tile_off=v(b.tile_off, (Ne + 1,)),
+                down_rows=v(b.down_rows, (T * k,)), first_cnt=v(b.first_cnt, (Ne,)),
                 brim1=v(b.brim1, (wl.n * N_sfd,)) if dense else None)
 
 
@@ -117,6 +118,24 @@ def check_brim(wl, placement, ids_g=None, w_g=None):
     bm = 128 if wl.dtype == W.DTYPE_BF16 else 64
     loads = np.diff(b["epd_off"])
     assert np.array_equal(np.diff(b["tile_off"]), (loads + bm - 1) // bm)
+    # merge order: per expert, the EPD rows that are the first (lowest-slot)
+    # contributor to their SFD row, then the others, each in token order
+    pos = np.empty(wl.Ne, np.int64)
+    pos[placement.reshape(-1)] = np.arange(wl.Ne)
+    p_of = pos[ids_g]                                   # T x k placement positions
+    g_of = p_of // wl.n
+    lower_same = (g_of[:, :, None] == g_of[:, None, :]) & (p_of[:, None, :] < p_of[:, :, None])
+    is_first = ~lower_same.any(2)
+    erow = b["tok_epd"]
+    for p in range(wl.Ne):
+        lo, hi = b["epd_off"][p], b["epd_off"][p + 1]
+        mine = p_of == p
+        firsts = np.sort(erow[mine & is_first])
+        rest = np.sort(erow[mine & ~is_first])
+        assert b["first_cnt"][p] == len(firsts)
+        assert np.array_equal(b["down_rows"][lo:hi], np.concatenate([firsts, rest]))
+    # every SFD row has exactly one first contributor
+    assert int(is_first.sum()) == int(b["sfd_off"][-1])
     return b
 
 
