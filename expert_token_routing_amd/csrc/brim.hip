@@ -12,7 +12,7 @@
 // group); it orders each expert's rows for the down-projection merge: first
 // contributors, then the rest, each in token order.
 //
-//   k_brim_count  per chunk of 1024 tokens, the token count of every bin;
+//   k_brim_count  per chunk of kBrimChunk tokens, the token count of every bin;
 //   k_brim_scan   one workgroup: exclusive scans over chunks and over bins,
 //                 giving each (chunk, bin) its first row, plus sfd_off,
 //                 epd_off, first-contributor counts and GEMM tile schedules;
@@ -26,7 +26,7 @@
 namespace occ {
 namespace {
 
-constexpr int kWavesPerChunk = kBrimChunk / kWave;  // 16
+constexpr int kWavesPerChunk = kBrimChunk / kWave;
 
 __device__ __forceinline__ bool has_pos(const uint64_t (&em)[4], int p) {
     return (em[p >> 6] >> (p & 63)) & 1ull;

@@ -21,7 +21,7 @@ constexpr int kMaxBins = kMaxNd + 2 * kMaxNe;  // BRIM bins: groups, experts, fi
 // Row tile of the grouped GEMMs (tokens per workgroup tile); the BRIM scan
 // lays out the per-expert tile schedule with it.
 #ifndef OCC_GEMM_BM
-#define OCC_GEMM_BM 128
+#define OCC_GEMM_BM 256
 #endif
 constexpr int kGemmBmBf16 = OCC_GEMM_BM;
 constexpr int kGemmBmF32 = 64;

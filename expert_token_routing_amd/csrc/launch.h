@@ -12,7 +12,7 @@ hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rul
                         const PlaceTab &tab, int32_t *ids, float *w, hipStream_t s);
 
 // --- BRIM (brim.hip) ---
-constexpr int kBrimChunk = 1024;  // tokens per BRIM workgroup
+constexpr int kBrimChunk = 256;  // tokens per BRIM workgroup
 struct BrimBufs {
     int32_t *brim0, *sfd_off, *epd_off, *tile_off, *epd_src, *tok_epd, *brim1;
     float *epd_w;

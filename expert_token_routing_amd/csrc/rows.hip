@@ -49,46 +49,66 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, size_
         p[i] = v;
 }
 
+template <int VPL>
+__device__ __forceinline__ void load_row(const f32x4 *__restrict__ src, int lane, int row_vec4,
+                                         f32x4 (&v)[VPL]) {
+#pragma unroll
+    for (int i = 0; i < VPL; i++) v[i] = src[min(lane + kWave * i, row_vec4 - 1)];
+}
+
+// The groups holding a replica of the token are the set bits of `mask`;
+// rows are summed in ascending group order, two rows' loads in flight at a
+// time.
 template <int VPL, bool BF16>
-__global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const float4 *__restrict__ sfd_out,
+__global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__restrict__ sfd_out,
                                                               const int32_t *__restrict__ brim0,
-                                                              const float4 *__restrict__ y_sh,
+                                                              const f32x4 *__restrict__ y_sh,
                                                               int T, int Nd, int row_vec4,
                                                               void *__restrict__ y) {
     const int lane = lane_id();
     const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
     if (t >= T) return;
     const int br = lane < Nd ? brim0[static_cast<size_t>(lane) * T + t] : -1;
-    float4 acc[VPL];
+    uint64_t mask = __ballot(br >= 0);
+    f32x4 acc[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; i++) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = 0; g < Nd; g++) {
-        const int r = __shfl(br, g);
-        if (r < 0) continue;
+    for (int i = 0; i < VPL; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (VPL > 8) {  // wide rows: one row at a time keeps registers in bounds
+        for (; mask; mask &= mask - 1) {
+            const int r = __shfl(br, __ffsll(static_cast<unsigned long long>(mask)) - 1);
+            const f32x4 *src = sfd_out + static_cast<size_t>(r) * row_vec4;
 #pragma unroll
-        for (int i = 0; i < VPL; i++) {
-            const int c = lane + kWave * i;
-            if (c < row_vec4) {
-                const float4 v = sfd_out[static_cast<size_t>(r) * row_vec4 + c];
-                acc[i].x += v.x;
-                acc[i].y += v.y;
-                acc[i].z += v.z;
-                acc[i].w += v.w;
-            }
+            for (int i = 0; i < VPL; i++) acc[i] += src[min(lane + kWave * i, row_vec4 - 1)];
+        }
+        if (y_sh) {
+            const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) acc[i] += src[min(lane + kWave * i, row_vec4 - 1)];
+        }
+    } else {
+    f32x4 a[VPL], b[VPL];
+    while (mask) {
+        const int g0 = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+        mask &= mask - 1;
+        const int r0 = __shfl(br, g0);
+        load_row<VPL>(sfd_out + static_cast<size_t>(r0) * row_vec4, lane, row_vec4, a);
+        if (mask) {
+            const int g1 = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+            mask &= mask - 1;
+            const int r1 = __shfl(br, g1);
+            load_row<VPL>(sfd_out + static_cast<size_t>(r1) * row_vec4, lane, row_vec4, b);
+#pragma unroll
+            for (int i = 0; i < VPL; i++) acc[i] = (acc[i] + a[i]) + b[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < VPL; i++) acc[i] += a[i];
         }
     }
     if (y_sh) {
+        load_row<VPL>(y_sh + static_cast<size_t>(t) * row_vec4, lane, row_vec4, a);
 #pragma unroll
-        for (int i = 0; i < VPL; i++) {
-            const int c = lane + kWave * i;
-            if (c < row_vec4) {
-                const float4 v = y_sh[static_cast<size_t>(t) * row_vec4 + c];
-                acc[i].x += v.x;
-                acc[i].y += v.y;
-                acc[i].z += v.z;
-                acc[i].w += v.w;
-            }
-        }
+        for (int i = 0; i < VPL; i++) acc[i] += a[i];
+    }
     }
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
@@ -103,7 +123,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const float4 *__re
                        (static_cast<uint32_t>(f32_to_bf16_bits(acc[i].w)) << 16);
             reinterpret_cast<uint2 *>(y)[o] = packed;
         } else {
-            reinterpret_cast<float4 *>(y)[o] = acc[i];
+            reinterpret_cast<f32x4 *>(y)[o] = acc[i];
         }
     }
 }
@@ -136,8 +156,8 @@ hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const floa
     const int row_vec4 = d / 4;
     const int vpl = (row_vec4 + kWave - 1) / kWave;
     const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
-    const float4 *so = reinterpret_cast<const float4 *>(sfd_out);
-    const float4 *ys = reinterpret_cast<const float4 *>(y_sh);
+    const f32x4 *so = reinterpret_cast<const f32x4 *>(sfd_out);
+    const f32x4 *ys = reinterpret_cast<const f32x4 *>(y_sh);
 #define OCC_COMBINE(V)                                                                        \
     do {                                                                                      \
         if (out_bf16) k_combine<V, true><<<grid, block, 0, s>>>(so, brim0, ys, T, Nd, row_vec4, y); \

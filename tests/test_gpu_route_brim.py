@@ -115,7 +115,7 @@ def check_brim(wl, placement, ids_g=None, w_g=None):
         grp[row] = g
     tt = np.repeat(np.arange(T), k)
     assert np.array_equal(b["epd_src"][rows], b["brim0"][grp[ids_g.reshape(-1)], tt])
-    bm = 128 if wl.dtype == W.DTYPE_BF16 else 64
+    bm = 256 if wl.dtype == W.DTYPE_BF16 else 64
     loads = np.diff(b["epd_off"])
     assert np.array_equal(np.diff(b["tile_off"]), (loads + bm - 1) // bm)
     # merge order: per expert, the EPD rows that are the first (lowest-slot)
