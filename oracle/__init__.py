@@ -22,7 +22,7 @@ SRC = os.path.join(HERE, "occ_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-PRUNE_OFF, PRUNE_TRAVERSE, PRUNE_GROUPSUM = 0, 1, 2
+PRUNE_OFF, PRUNE_TRAVERSE, PRUNE_GROUPSUM, PRUNE_SIMILARITY = 0, 1, 2, 3
 
 _lib = None
 
@@ -82,6 +82,44 @@ def route(logits: np.ndarray, k: int, placement: np.ndarray, prune_rule: int = P
     w = np.empty((T, k), np.float64)
     rc = _load().orc_route(T, Ne, k, _p(lg), Nd, _p(L), prune_rule, prune_groups, _p(ids), _p(w))
     _check(rc, "route")
+    return ids, w
+
+
+def sim_accumulate(logits: np.ndarray, gram: np.ndarray | None = None) -> np.ndarray:
+    """Eq. 6-8's Gram matrix of the logit columns, fp64, one more batch added
+    (tokens in ascending order) to `gram` (a fresh zero matrix if None)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, Ne = lg.shape
+    g = np.zeros((Ne, Ne), np.float64) if gram is None else np.array(gram, np.float64, order="C")
+    _check(_load().orc_sim_accumulate(T, Ne, _p(lg), _p(g)), "sim_accumulate")
+    return g
+
+
+def sim_rank(gram: np.ndarray):
+    """Squared cosine similarity table (Eq. 7/8) and each row's ranking:
+    returns (t2 (Ne, Ne) float64, rank (Ne, Ne) int32)."""
+    g = np.ascontiguousarray(gram, dtype=np.float64)
+    Ne = g.shape[0]
+    t2 = np.empty((Ne, Ne), np.float64)
+    rank = np.empty((Ne, Ne), np.int32)
+    _check(_load().orc_sim_rank(Ne, _p(g), _p(t2), _p(rank)), "sim_rank")
+    return t2, rank
+
+
+def route_similarity(logits: np.ndarray, k: int, placement: np.ndarray, prune_groups: int,
+                     rank: np.ndarray):
+    """Expert-similarity-based collaboration pruning (section 3.3): ids (T, k)
+    int32 and w (T, k) float64."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, Ne = lg.shape
+    L = _i32(placement)
+    Nd = L.shape[0]
+    r = _i32(rank)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    rc = _load().orc_route_similarity(T, Ne, k, _p(lg), Nd, _p(L), prune_groups, _p(r),
+                                      _p(ids), _p(w))
+    _check(rc, "route_similarity")
     return ids, w
 
 

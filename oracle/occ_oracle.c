@@ -178,6 +178,129 @@ int orc_route(int T, int Ne, int k, const float *logits, int Nd, const int32_t *
     return rc;
 }
 
+/*
+ * Expert similarity table, appendix A.3, Eq. 6-8.  H is the profiled
+ * router-logit matrix (tokens x Ne).  Eq. 8's numerator and denominator are
+ * built from the Gram matrix of H's columns, gram[i][j] = sum_t H[t][i] H[t][j],
+ * which is accumulated batch by batch: this call adds one batch, tokens in
+ * ascending order, in fp64 (the products of two fp32 logits are exact).
+ */
+int orc_sim_accumulate(int T, int Ne, const float *logits, double *gram)
+{
+    if (T < 0 || Ne < 1)
+        return ORC_BAD;
+    for (int i = 0; i < Ne; i++)
+        for (int j = 0; j < Ne; j++) {
+            double acc = gram[(size_t)i * Ne + j];
+            for (int t = 0; t < T; t++)
+                acc += (double)logits[(size_t)t * Ne + i] * (double)logits[(size_t)t * Ne + j];
+            gram[(size_t)i * Ne + j] = acc;
+        }
+    return ORC_OK;
+}
+
+/*
+ * The table itself.  Eq. 7 (equal to Eq. 8, whose 1/N factors cancel): the
+ * squared cosine similarity of columns i and j,
+ *   T2[i][j] = gram[i][j]^2 / (gram[i][i] * gram[j][j]),
+ * 0 when either column is all zero.  The table the pruning rule consults is
+ * declared integer (section 3.3), read as each row's ranking: rank[i][q] is
+ * the q-th most similar expert to i, by T2 descending, ties to the lower
+ * index (a plain insertion sort per row).  t2 may be NULL.
+ */
+int orc_sim_rank(int Ne, const double *gram, double *t2, int32_t *rank)
+{
+    if (Ne < 1)
+        return ORC_BAD;
+    double *row = malloc(sizeof(double) * Ne);
+    for (int i = 0; i < Ne; i++) {
+        double gii = gram[(size_t)i * Ne + i];
+        for (int j = 0; j < Ne; j++) {
+            double gij = gram[(size_t)i * Ne + j], gjj = gram[(size_t)j * Ne + j];
+            double den = gii * gjj;
+            row[j] = den > 0.0 ? (gij * gij) / den : 0.0;
+            if (t2)
+                t2[(size_t)i * Ne + j] = row[j];
+        }
+        int32_t *r = rank + (size_t)i * Ne;
+        for (int j = 0; j < Ne; j++) {
+            int q = j;
+            while (q > 0 && (row[j] > row[r[q - 1]] || (row[j] == row[r[q - 1]] && j < r[q - 1]))) {
+                r[q] = r[q - 1];
+                q--;
+            }
+            r[q] = j;
+        }
+    }
+    free(row);
+    return ORC_OK;
+}
+
+/*
+ * Collaboration pruning, expert-similarity-based (section 3.3): the allowed
+ * groups are the first G met walking the token's top-k list in descending
+ * score (as in TRAVERSE).  The list is walked again in the same order; an
+ * expert in an allowed group stays, any other is replaced by the first
+ * expert of its row of the ranked table that sits in an allowed group and is
+ * not yet selected.  "Selected" holds the experts of the list that stay plus
+ * the replacements made so far, so the k results are distinct.  A
+ * replacement takes the replaced expert's place and routing weight (its
+ * full-softmax probability).  rank must hold a permutation of 0..Ne-1 in
+ * every row.
+ */
+int orc_route_similarity(int T, int Ne, int k, const float *logits, int Nd, const int32_t *L,
+                         int G, const int32_t *rank, int32_t *ids, double *w)
+{
+    if (T < 0 || k < 1 || k > Ne)
+        return ORC_BAD;
+    int *grp = malloc(sizeof(int) * Ne), *ord = malloc(sizeof(int) * Ne);
+    int *chosen = malloc(sizeof(int) * Nd), *picked = malloc(sizeof(int) * Ne);
+    int rc = group_table(Ne, Nd, L, grp, NULL);
+    if (G < 1 || G * (Ne / Nd) < k)
+        rc = ORC_BAD;
+    for (int t = 0; t < T && rc == ORC_OK; t++) {
+        const float *l = logits + (size_t)t * Ne;
+        score_order(l, Ne, ord);
+        double m = l[ord[0]], s = 0.0;
+        for (int e = 0; e < Ne; e++)
+            s += exp((double)l[e] - m);
+
+        for (int g = 0; g < Nd; g++)
+            chosen[g] = 0;
+        int have = 0;
+        for (int j = 0; j < k && have < G; j++)
+            if (!chosen[grp[ord[j]]]) {
+                chosen[grp[ord[j]]] = 1;
+                have++;
+            }
+        for (int e = 0; e < Ne; e++)
+            picked[e] = 0;
+        for (int j = 0; j < k; j++)
+            if (chosen[grp[ord[j]]])
+                picked[ord[j]] = 1;
+        for (int j = 0; j < k; j++) {
+            int e = ord[j];
+            if (!chosen[grp[e]]) {
+                const int32_t *row = rank + (size_t)e * Ne;
+                int q = 0;
+                while (q < Ne && !(chosen[grp[row[q]]] && !picked[row[q]]))
+                    q++;
+                if (q == Ne) {
+                    rc = ORC_BAD;
+                    break;
+                }
+                picked[row[q]] = 1;
+                ids[(size_t)t * k + j] = row[q];
+            } else {
+                ids[(size_t)t * k + j] = e;
+            }
+            w[(size_t)t * k + j] = exp((double)l[ord[j]] - m) / s;
+        }
+    }
+    free(grp); free(ord); free(chosen); free(picked);
+    return rc;
+}
+
 /* Does token t route to an expert kept on group g? */
 static int token_uses_group(const int32_t *ids_t, int k, const int *grp, int g)
 {

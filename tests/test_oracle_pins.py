@@ -165,6 +165,119 @@ def test_route_rejects_infeasible_pruning():
 
 
 # --------------------------------------------------------------------------
+# Expert similarity table (appendix A.3, Eq. 6-8) and similarity-based
+# pruning (section 3.3)
+
+
+def test_similarity_table_worked_example():
+    g = golden("similarity_pruning.json")["table"]
+    H = np.array(g["H"], np.float32)
+    gram = oracle.sim_accumulate(H)
+    assert np.array_equal(gram, np.array(g["gram"], np.float64))
+    t2, rank = oracle.sim_rank(gram)
+    np.testing.assert_allclose(t2, np.array(g["t2"]), rtol=1e-15, atol=0)
+    assert rank.tolist() == g["rank"]
+
+
+def test_similarity_table_closed_forms():
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal(40).astype(np.float32)
+    other = rng.standard_normal(40).astype(np.float32)
+    H = np.zeros((40 + 3, 5), np.float32)
+    H[:40, 0] = base
+    H[:40, 1] = 4.0 * base            # proportional: squared cosine 1
+    H[:40, 2] = -2.0 * base           # opposite sign: squared cosine also 1
+    H[40:, 3] = [1.0, 2.0, 3.0]       # support disjoint from column 0: 0
+    H[:40, 4] = other
+    t2, rank = oracle.sim_rank(oracle.sim_accumulate(H))
+    assert np.allclose(np.diag(t2), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(t2[0, [1, 2]], 1.0, rtol=1e-14)
+    assert t2[0, 3] == 0.0 and t2[3, 0] == 0.0
+    np.testing.assert_allclose(t2, t2.T, rtol=1e-15, atol=0)
+    # cosine of the normalised columns, squared: a different route to Eq. 6
+    Hn = H.astype(np.float64) / np.linalg.norm(H.astype(np.float64), axis=0)
+    np.testing.assert_allclose(t2, (Hn.T @ Hn) ** 2, rtol=1e-12, atol=1e-15)
+    # an all-zero column is similar to nothing
+    Z = H.copy()
+    Z[:, 4] = 0.0
+    tz, _ = oracle.sim_rank(oracle.sim_accumulate(Z))
+    assert np.all(tz[4] == 0.0) and np.all(tz[:, 4] == 0.0)
+
+
+def test_similarity_table_batches_and_scale():
+    """Eq. 8 accumulates the sums batch by batch; scaling an expert's logits
+    leaves its similarities unchanged."""
+    wl = W.OLMOE
+    H = synth.make_logits(wl, 1000).numpy()
+    full = oracle.sim_accumulate(H)
+    part = oracle.sim_accumulate(H[600:], oracle.sim_accumulate(H[:600]))
+    assert np.array_equal(full, part)  # same order, same bits
+    t2, rank = oracle.sim_rank(full)
+    S = H.copy()
+    S[:, 7] *= 0.25  # a power of two: the products stay exact
+    t2s, rank_s = oracle.sim_rank(oracle.sim_accumulate(S))
+    np.testing.assert_allclose(t2s, t2, rtol=1e-12)
+    # ranking: each row sorted by (-t2, j), checked with Python's sort
+    for i in range(0, wl.Ne, 9):
+        assert rank[i].tolist() == sorted(range(wl.Ne), key=lambda j: (-t2[i, j], j))
+    # the synthetic clusters (expert e in cluster e mod n_c) are what the
+    # table finds: an expert's nearest other expert shares its cluster
+    near = rank[:, 1]
+    assert np.mean(near % wl.n_c == np.arange(wl.Ne) % wl.n_c) > 0.9
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_similarity_pruning_worked_examples(case):
+    g = golden("similarity_pruning.json")["route"]
+    c = g["cases"][case]
+    logits = np.array([c["logits"]], np.float32)
+    L = np.array(g["placement"], np.int32)
+    rank = np.array(g["rank"], np.int32)
+    ids, w = oracle.route_similarity(logits, g["k"], L, g["G"], rank)
+    assert ids[0].tolist() == c["ids"]
+    prob = torch.softmax(torch.tensor(c["logits"], dtype=torch.float32).double(), 0).numpy()
+    np.testing.assert_allclose(w[0], prob[c["topk"]], rtol=1e-14)
+
+
+def test_similarity_pruning_properties():
+    wl = W.OLMOE
+    T = 1024
+    logits = synth.make_logits(wl, T).numpy()
+    L = synth.contiguous_placement(wl)
+    grp = group_of(L)
+    _, rank = oracle.sim_rank(oracle.sim_accumulate(synth.make_logits(wl, 2000).numpy()))
+    ids0, w0 = oracle.route(logits, wl.k, L)
+    ids_all, w_all = oracle.route_similarity(logits, wl.k, L, wl.Nd, rank)
+    assert np.array_equal(ids_all, ids0) and np.array_equal(w_all, w0)
+    for G in (1, 2, 4):
+        ids, w = oracle.route_similarity(logits, wl.k, L, G, rank)
+        ids_tr, _ = oracle.route(logits, wl.k, L, oracle.PRUNE_TRAVERSE, G)
+        assert np.array_equal(w, w0)  # replacements keep the replaced weight
+        for t in range(T):
+            allowed = set(grp[ids_tr[t]].tolist())  # TRAVERSE's groups
+            row = ids[t].tolist()
+            assert len(set(row)) == wl.k and set(grp[row].tolist()) <= allowed
+            assert set(grp[row].tolist()) == allowed
+            taken = {e for e in ids0[t].tolist() if grp[e] in allowed}
+            for j, e in enumerate(ids0[t].tolist()):
+                if grp[e] in allowed:
+                    assert row[j] == e
+                else:  # the most similar free allowed expert, brute force
+                    best = next(q for q in rank[e].tolist()
+                                if grp[q] in allowed and q not in taken)
+                    assert row[j] == best
+                    taken.add(best)
+
+
+def test_similarity_pruning_rejects_infeasible():
+    logits = np.zeros((2, 8), np.float32)
+    L = np.arange(8, dtype=np.int32).reshape(4, 2)
+    rank = np.tile(np.arange(8, dtype=np.int32), (8, 1))
+    with pytest.raises(ValueError):
+        oracle.route_similarity(logits, 4, L, 1, rank)
+
+
+# --------------------------------------------------------------------------
 # BRIM_0 / BRIM_1 (Algorithms 3 and 5) and CT (section 2.2, Eq. 5)
 
 
