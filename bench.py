@@ -72,11 +72,30 @@ def main():
     y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
 
+    sim = wl.prune_rule == W.PRUNE_SIMILARITY
+    sim_rank, table_ms = None, None
+    if sim:
+        # --- expert similarity table (appendix A.3; offline, timed on its own)
+        prof = synth.make_profile_logits(wl).to(dev)
+        gram = torch.zeros(wl.Ne, wl.Ne, dtype=torch.float64, device=dev)
+        sim_rank = torch.empty(wl.Ne, wl.Ne, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        occ.occ_similarity_accumulate(prof, gram)
+        occ.occ_similarity_rank(gram, sim_rank)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        table_ms = e0.elapsed_time(e1)
+        log(f"[bench] similarity table from {prof.shape[0]} profiled tokens: {table_ms:.3f} ms")
+
     # --- placement (offline step, untimed): Algorithm 1 on this batch's counts
     L_contig = inp["placement"]
     ids = torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev)
     wts = torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev)
-    occ.occ_route(desc, g["logits"], L_contig, ids, wts)
+    if sim:
+        occ.occ_route_similarity(desc, g["logits"], L_contig, sim_rank, ids, wts)
+    else:
+        occ.occ_route(desc, g["logits"], L_contig, ids, wts)
     C = torch.empty(wl.Ne, wl.Ne, dtype=torch.int32, device=dev)
     P = torch.empty(wl.Ne, wl.Ne, dtype=torch.float32, device=dev)
     n_sfd = torch.empty(1, dtype=torch.int64, device=dev)
@@ -90,22 +109,41 @@ def main():
     torch.cuda.synchronize()
     ct_alg1, nsfd_alg1, intra_alg1 = float(ct.item()), int(n_sfd.item()), float(intra.item())
 
-    def run(L, steps, events=None):
+    r_ids = torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev)
+    r_w = torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev)
+
+    def run(L, steps, events=None, route_events=None):
         for i in range(steps):
             ev = events[i].handles if events is not None else None
-            occ.occ_moe_forward(desc, g["x"], g["logits"], L, g["w_gate"], g["w_up"], g["w_down"],
-                                g["ws_gate"], g["ws_up"], g["ws_down"], y, ws, stage_events=ev)
+            if not sim:
+                occ.occ_moe_forward(desc, g["x"], g["logits"], L, g["w_gate"], g["w_up"],
+                                    g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], y, ws,
+                                    stage_events=ev)
+                continue
+            # similarity-pruned routing, then the layer on that routing
+            if route_events is not None:
+                route_events[i][0].record(stream)
+            occ.occ_route_similarity(desc, g["logits"], L, sim_rank, r_ids, r_w)
+            if route_events is not None:
+                route_events[i][1].record(stream)
+            occ.occ_moe_forward_routed(desc, g["x"], r_ids, r_w, L, g["w_gate"], g["w_up"],
+                                       g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], y,
+                                       ws, stage_events=ev)
 
     def timed(L, label):
         log(f"[bench] {label}: warmup {args.warmup}")
         run(L, args.warmup)
         torch.cuda.synchronize()
         events = [occ.StageEvents() for _ in range(args.steps)]
+        rev = None
+        if sim:
+            rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record(stream)
-        run(L, args.steps, events)
+        run(L, args.steps, events, rev)
         stop.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -113,8 +151,13 @@ def main():
         stages = np.array([e.elapsed_ms() for e in events])  # steps x stages
         for e in events:
             e.close()
+        st = {s: float(v) for s, v in zip(occ.STAGES, stages.mean(0))}
+        if sim:
+            # the routed forward's route stage is the copy of the given routing
+            st["route_copy"] = st.pop("route")
+            st = {"route_similarity": float(np.mean([a.elapsed_time(b) for a, b in rev])), **st}
         log(f"[bench] {label}: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
-        return ms, stages.mean(0)
+        return ms, st
 
     ms, stages = timed(L_alg1, "alg1 placement")
     tokens_per_s = wl.T / (ms / 1e3)
@@ -122,8 +165,7 @@ def main():
     if not args.no_contiguous:
         ms_c, stages_c = timed(L_contig, "contiguous placement")
         res_contig = {"value": wl.T / (ms_c / 1e3), "ms_per_step": ms_c, "ct": ct_contig,
-                      "intra": intra_contig,
-                      "stages_ms": {s: float(v) for s, v in zip(occ.STAGES, stages_c)}}
+                      "intra": intra_contig, "stages_ms": stages_c}
 
     if args.copy_calibration:
         n = 1 << 30
@@ -134,7 +176,7 @@ def main():
         torch.cuda.synchronize()
 
     # --- roofline of the dominant kernel: the up-projection grouped GEMM
-    up_ms = float(stages[occ.STAGES.index("gemm_up")])
+    up_ms = stages["gemm_up"]
     flops_up = 2.0 * wl.T * wl.k * wl.d * 2 * wl.F
     achieved = flops_up / (up_ms / 1e3) / 1e12
     traffic = profiling.traffic_bytes("k_gemm_up", wl.name, "gemm_bf16.hip")
@@ -146,7 +188,8 @@ def main():
     # --- CPU baseline: the oracle on a bounded sample of this workload
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inp, L_alg1, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, L_alg1, args.cpu_seconds,
+                           None if sim_rank is None else sim_rank.cpu().numpy())
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -158,13 +201,16 @@ def main():
         "ct": ct_alg1, "n_sfd": nsfd_alg1, "intra": intra_alg1,
         "ct_bounds": [-(-wl.k * wl.Nd // wl.Ne), min(wl.k, wl.Nd)],
         "roofline": roofline, "cpu_baseline": cpu,
-        "stages_ms": {s: round(float(v), 5) for s, v in zip(occ.STAGES, stages)},
+        "stages_ms": {s: round(v, 5) for s, v in stages.items()},
         "contiguous": res_contig,
     }
+    if sim:
+        out["config"]["pruning"] = f"similarity, {wl.prune_groups} groups"
+        out["similarity_table_ms"] = round(table_ms, 4)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, placement, seconds):
+def cpu_baseline(wl, inp, placement, seconds, sim_rank=None):
     """Time the oracle (route, BRIM, stats on the full batch; Eq. 1 rows on a
     sample sized to about `seconds`) and scale to tokens/s."""
     import numpy as np
@@ -175,7 +221,12 @@ def cpu_baseline(wl, inp, placement, seconds):
 
     log("[bench] cpu baseline: oracle route/BRIM/stats on the full batch")
     t0 = time.perf_counter()
-    ids, w = oracle.route(inp["logits"].numpy(), wl.k, placement, wl.prune_rule, wl.prune_groups)
+    if sim_rank is not None:
+        ids, w = oracle.route_similarity(inp["logits"].numpy(), wl.k, placement,
+                                         wl.prune_groups, sim_rank)
+    else:
+        ids, w = oracle.route(inp["logits"].numpy(), wl.k, placement, wl.prune_rule,
+                              wl.prune_groups)
     oracle.brim1(ids, w, wl.Ne, placement)
     oracle.coact(ids, wl.Ne, placement)
     t_index = time.perf_counter() - t0

@@ -74,7 +74,7 @@ occ_status check_desc(const occ_layer_desc *D) {
     if (D->k > D->Ne || D->Ne % D->Nd != 0) return OCC_ERR_INVALID_ARG;
     if (D->n_shared < 0 || (D->n_shared > 0 && D->F_shared < 1)) return OCC_ERR_INVALID_ARG;
     if (D->dtype != OCC_F32 && D->dtype != OCC_BF16) return OCC_ERR_INVALID_ARG;
-    if (D->prune_rule < OCC_PRUNE_OFF || D->prune_rule > OCC_PRUNE_GROUPSUM)
+    if (D->prune_rule < OCC_PRUNE_OFF || D->prune_rule > OCC_PRUNE_SIMILARITY)
         return OCC_ERR_INVALID_ARG;
     if (D->prune_rule != OCC_PRUNE_OFF &&
         (D->prune_groups < 1 ||
@@ -193,11 +193,41 @@ occ_status occ_workspace_size(const occ_layer_desc *desc, size_t *bytes_host) {
 occ_status occ_route(const occ_layer_desc *desc, const float *logits,
                      const int32_t *placement_host, int32_t *ids, float *w, void *stream) {
     OCC_TRY(check_desc(desc));
-    if (!logits || !ids || !w) return OCC_ERR_INVALID_ARG;
+    if (!logits || !ids || !w || desc->prune_rule == OCC_PRUNE_SIMILARITY)
+        return OCC_ERR_INVALID_ARG;
     PlaceTab tab;
     OCC_TRY(make_tab(*desc, placement_host, &tab));
     OCC_HIP(launch_route(logits, desc->T, desc->Ne, desc->k, desc->prune_rule,
-                         desc->prune_groups, tab, ids, w, static_cast<hipStream_t>(stream)));
+                         desc->prune_groups, tab, nullptr, ids, w,
+                         static_cast<hipStream_t>(stream)));
+    return OCC_OK;
+}
+
+occ_status occ_similarity_accumulate(int32_t T, int32_t Ne, const float *logits, double *gram,
+                                     void *stream) {
+    if (T < 0 || Ne < 1 || Ne > kMaxNe || !gram || (T > 0 && !logits)) return OCC_ERR_INVALID_ARG;
+    OCC_HIP(launch_sim_gram(logits, T, Ne, gram, static_cast<hipStream_t>(stream)));
+    return OCC_OK;
+}
+
+occ_status occ_similarity_rank(int32_t Ne, const double *gram, double *t2, int32_t *rank,
+                               void *stream) {
+    if (Ne < 1 || Ne > kMaxNe || !gram || !rank) return OCC_ERR_INVALID_ARG;
+    OCC_HIP(launch_sim_rank(gram, Ne, t2, rank, static_cast<hipStream_t>(stream)));
+    return OCC_OK;
+}
+
+occ_status occ_route_similarity(const occ_layer_desc *desc, const float *logits,
+                                const int32_t *placement_host, const int32_t *sim_rank,
+                                int32_t *ids, float *w, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!logits || !ids || !w || !sim_rank || desc->prune_rule != OCC_PRUNE_SIMILARITY)
+        return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(*desc, placement_host, &tab));
+    OCC_HIP(launch_route(logits, desc->T, desc->Ne, desc->k, desc->prune_rule,
+                         desc->prune_groups, tab, sim_rank, ids, w,
+                         static_cast<hipStream_t>(stream)));
     return OCC_OK;
 }
 
@@ -210,8 +240,12 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const 
     OCC_TRY(make_tab(*desc, placement_host, &tab));
     const Layout L = layout(*desc);
     OCC_TRY(check_ws(*desc, workspace, ws_bytes, L.brim_end));
-    OCC_HIP(launch_brim(ids, w, desc->T, desc->k, tab, tile_rows(*desc), dense_brim1 != 0,
-                        brim_bufs(workspace, L), static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *ids_ws = at<int32_t>(workspace, L.ids);
+    float *w_ws = at<float>(workspace, L.w);
+    OCC_HIP(launch_sanitize_ids(ids, w, desc->T, desc->k, desc->Ne, ids_ws, w_ws, s));
+    OCC_HIP(launch_brim(ids_ws, w_ws, desc->T, desc->k, tab, tile_rows(*desc), dense_brim1 != 0,
+                        brim_bufs(workspace, L), s));
     *out_host = brim_view(workspace, L);
     return OCC_OK;
 }
@@ -234,14 +268,19 @@ occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
     return OCC_OK;
 }
 
-occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const float *logits,
-                           const int32_t *placement_host, const void *w_gate, const void *w_up,
-                           const void *w_down, const void *ws_gate, const void *ws_up,
-                           const void *ws_down, void *y, void *workspace, size_t ws_bytes,
-                           void *const *stage_events, void *stream) {
+// The layer's stage sequence.  Stage 0 routes `logits` (the desc's rule) or,
+// with logits NULL, copies the caller's routing ids_in / w_in.
+static occ_status forward(const occ_layer_desc *desc, const void *x, const float *logits,
+                          const int32_t *ids_in, const float *w_in,
+                          const int32_t *placement_host, const void *w_gate, const void *w_up,
+                          const void *w_down, const void *ws_gate, const void *ws_up,
+                          const void *ws_down, void *y, void *workspace, size_t ws_bytes,
+                          void *const *stage_events, void *stream) {
     OCC_TRY(check_desc(desc));
     const occ_layer_desc &D = *desc;
-    if (!x || !logits || !w_gate || !w_up || !w_down || !y) return OCC_ERR_INVALID_ARG;
+    if (!x || !w_gate || !w_up || !w_down || !y) return OCC_ERR_INVALID_ARG;
+    if (logits ? D.prune_rule == OCC_PRUNE_SIMILARITY : (!ids_in || !w_in))
+        return OCC_ERR_INVALID_ARG;
     if (D.n_shared > 0 && (!ws_gate || !ws_up || !ws_down)) return OCC_ERR_INVALID_ARG;
     if (stage_events)
         for (int i = 0; i <= OCC_STAGE_COUNT; i++)
@@ -271,8 +310,12 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     const size_t shared_tiles = (T + bm - 1) / bm;
 
     OCC_TRY(mark(0));
-    // Eq. 2: router
-    OCC_HIP(launch_route(logits, D.T, D.Ne, D.k, D.prune_rule, D.prune_groups, tab, ids, w, s));
+    // Eq. 2: router (or the caller's routing, checked)
+    if (logits)
+        OCC_HIP(launch_route(logits, D.T, D.Ne, D.k, D.prune_rule, D.prune_groups, tab, nullptr,
+                             ids, w, s));
+    else
+        OCC_HIP(launch_sanitize_ids(ids_in, w_in, D.T, D.k, D.Ne, ids, w, s));
     OCC_TRY(mark(1));
     // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
     OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
@@ -353,6 +396,27 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
     OCC_TRY(mark(8));
     return OCC_OK;
+}
+
+occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const float *logits,
+                           const int32_t *placement_host, const void *w_gate, const void *w_up,
+                           const void *w_down, const void *ws_gate, const void *ws_up,
+                           const void *ws_down, void *y, void *workspace, size_t ws_bytes,
+                           void *const *stage_events, void *stream) {
+    if (!logits) return OCC_ERR_INVALID_ARG;
+    return forward(desc, x, logits, nullptr, nullptr, placement_host, w_gate, w_up, w_down,
+                   ws_gate, ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+}
+
+occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, const int32_t *ids,
+                                  const float *w, const int32_t *placement_host,
+                                  const void *w_gate, const void *w_up, const void *w_down,
+                                  const void *ws_gate, const void *ws_up, const void *ws_down,
+                                  void *y, void *workspace, size_t ws_bytes,
+                                  void *const *stage_events, void *stream) {
+    if (!ids || !w) return OCC_ERR_INVALID_ARG;
+    return forward(desc, x, nullptr, ids, w, placement_host, w_gate, w_up, w_down, ws_gate,
+                   ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
 }
 
 occ_status occ_coactivation_stats(const occ_layer_desc *desc, const int32_t *ids,

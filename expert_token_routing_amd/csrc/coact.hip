@@ -24,6 +24,12 @@ __global__ __launch_bounds__(256) void k_coact_zero(int32_t *C, int n, int64_t *
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_sfd = 0;
 }
 
+// Caller ids outside 0..Ne-1 are counted as expert 0 (unspecified result,
+// in-bounds accesses).
+__device__ __forceinline__ int in_range(int e, int Ne) {
+    return static_cast<unsigned>(e) < static_cast<unsigned>(Ne) ? e : 0;
+}
+
 __global__ __launch_bounds__(kCoactTokens) void k_coact(const int32_t *__restrict__ ids, int T,
                                                         int k, PlaceTab tab,
                                                         int32_t *__restrict__ C,
@@ -41,10 +47,10 @@ __global__ __launch_bounds__(kCoactTokens) void k_coact(const int32_t *__restric
         const int32_t *it = ids + static_cast<size_t>(t) * k;
         uint64_t gmask = 0;
         for (int a = 0; a < k; a++) {
-            const int ea = it[a];
+            const int ea = in_range(it[a], Ne);
             gmask |= 1ull << tab.grp[ea];
             for (int b = 0; b < k; b++) {
-                const int idx = ea * Ne + it[b];
+                const int idx = ea * Ne + in_range(it[b], Ne);
                 if (in_lds) atomicAdd(&hist[idx], 1);
                 else atomicAdd(&C[idx], 1);
             }

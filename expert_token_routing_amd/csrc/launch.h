@@ -8,8 +8,21 @@
 namespace occ {
 
 // --- routing (route.hip) ---
+// prune_rule 0 none, 1 TRAVERSE, 2 GROUPSUM, 3 similarity (sim_rank: Ne x Ne
+// ranked table, used only by rule 3).
 hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rule, int G,
-                        const PlaceTab &tab, int32_t *ids, float *w, hipStream_t s);
+                        const PlaceTab &tab, const int32_t *sim_rank, int32_t *ids, float *w,
+                        hipStream_t s);
+// Copies caller routing into ids/w, replacing out-of-range or repeated ids of
+// a token by the lowest unused experts with weight 0.
+hipError_t launch_sanitize_ids(const int32_t *ids_in, const float *w_in, int T, int k, int Ne,
+                               int32_t *ids, float *w, hipStream_t s);
+
+// --- expert similarity table (similarity.hip) ---
+// gram += H^T H (fp64, tokens ascending); H is T x Ne fp32.
+hipError_t launch_sim_gram(const float *H, int T, int Ne, double *gram, hipStream_t s);
+// Squared cosine similarities (t2 may be NULL) and each row's ranking.
+hipError_t launch_sim_rank(const double *gram, int Ne, double *t2, int32_t *rank, hipStream_t s);
 
 // --- BRIM (brim.hip) ---
 constexpr int kBrimChunk = 256;  // tokens per BRIM workgroup

@@ -1,11 +1,13 @@
 // Router: top-k softmax gating (Occult paper, section 2.1, Eq. 2) with
-// routing-score-based collaboration pruning (section 3.3).
+// collaboration pruning (section 3.3), routing-score-based or
+// expert-similarity-based.
 //
 // One 64-lane wave per token; lane l holds the logits of experts l, l+64, ...
 // Softmax max and denominator are wave reductions; the top k come from k
 // rounds of a wave arg-max on (logit, -index), so the order is (logit
 // descending, index ascending).  Softmax is monotone, so selecting on the
-// logits selects the top k probabilities.
+// logits selects the top k probabilities.  A NaN logit ranks as -inf, so the
+// k results are always distinct experts.
 #include "launch.h"
 
 namespace occ {
@@ -31,14 +33,17 @@ __device__ void select_topk(const TokenLogits<NI> &l, int Ne, int k, uint64_t al
         const int e = lane + kWave * i;
         ok[i] = e < Ne && ((allowed >> s_grp[e]) & 1ull);
     }
+    float v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) v[i] = l.v[i] == l.v[i] ? l.v[i] : -INFINITY;
     for (int j = 0; j < k; j++) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             const int e = lane + kWave * i;
-            if (ok[i] && !((taken >> i) & 1u) && (l.v[i] > bv || (l.v[i] == bv && e < bi))) {
-                bv = l.v[i];
+            if (ok[i] && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+                bv = v[i];
                 bi = e;
             }
         }
@@ -52,11 +57,89 @@ __device__ void select_topk(const TokenLogits<NI> &l, int Ne, int k, uint64_t al
     __builtin_amdgcn_wave_barrier();
 }
 
+// Bit e of a 256-bit expert set held as four words.
+__device__ __forceinline__ bool in_set(const uint64_t (&m)[4], int e) {
+    const uint64_t w = e < 64 ? m[0] : e < 128 ? m[1] : e < 192 ? m[2] : m[3];
+    return (w >> (e & 63)) & 1ull;
+}
+__device__ __forceinline__ void add_to_set(uint64_t (&m)[4], int e) {
+    const uint64_t bit = 1ull << (e & 63);
+    if (e < 64) m[0] |= bit;
+    else if (e < 128) m[1] |= bit;
+    else if (e < 192) m[2] |= bit;
+    else m[3] |= bit;
+}
+
+// Expert-similarity-based pruning (section 3.3): walking the top-k list
+// sel[0..k) in score order, an expert outside the allowed groups is replaced
+// by the first expert of its ranked similarity row that is allowed and not
+// yet selected (the list's allowed experts plus earlier replacements).  The
+// replacement keeps the replaced expert's place, and its logit in sel_l, so
+// it inherits the routing weight.  The lanes test 64 row entries at a time
+// and a ballot finds the first hit.  A row that is not a permutation of the
+// experts may find none; the expert then stays (in bounds, unspecified).
+__device__ void replace_similar(const int32_t *__restrict__ sim_rank, int Ne, int k,
+                                uint64_t chosen, const uint8_t *s_grp, int *sel) {
+    const int lane = lane_id();
+    uint64_t picked[4] = {0, 0, 0, 0};
+    for (int j = 0; j < k; j++)
+        if ((chosen >> s_grp[sel[j]]) & 1ull) add_to_set(picked, sel[j]);
+    for (int j = 0; j < k; j++) {
+        const int e = sel[j];
+        if ((chosen >> s_grp[e]) & 1ull) continue;
+        const int32_t *row = sim_rank + static_cast<size_t>(e) * Ne;
+        int rep = e;
+        for (int q0 = 0; q0 < Ne; q0 += kWave) {
+            const int q = q0 + lane;
+            const int c = q < Ne ? row[q] : -1;
+            const bool ok = c >= 0 && c < Ne && ((chosen >> s_grp[c]) & 1ull) && !in_set(picked, c);
+            const uint64_t hit = __ballot(ok);
+            if (hit) {
+                rep = __shfl(c, __builtin_ctzll(hit));
+                break;
+            }
+        }
+        add_to_set(picked, rep);
+        if (lane == 0) sel[j] = rep;
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Caller-supplied routing made safe for the BRIM kernels: a token's id that
+// is out of range or repeats an earlier one is replaced by the lowest expert
+// not yet in the token's list, with weight 0.  Valid tokens are copied
+// unchanged.  One thread per token.
+__global__ __launch_bounds__(256) void k_sanitize_ids(const int32_t *__restrict__ ids_in,
+                                                      const float *__restrict__ w_in, int T,
+                                                      int k, int Ne, int32_t *__restrict__ ids,
+                                                      float *__restrict__ w) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const size_t o = static_cast<size_t>(t) * k;
+    for (int j = 0; j < k; j++) {
+        int e = ids_in[o + j];
+        float wj = w_in[o + j];
+        bool ok = e >= 0 && e < Ne;
+        for (int q = 0; q < j && ok; q++) ok = ids[o + q] != e;
+        if (!ok) {
+            wj = 0.f;
+            for (e = 0; e < Ne; e++) {
+                bool used = false;
+                for (int q = 0; q < j && !used; q++) used = ids[o + q] == e;
+                if (!used) break;
+            }
+        }
+        ids[o + j] = e;
+        w[o + j] = wj;
+    }
+}
+
 template <int NI>
 __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__restrict__ logits,
                                                               int T, int Ne, int k,
                                                               int prune_rule, int G,
                                                               PlaceTab tab,
+                                                              const int32_t *__restrict__ sim_rank,
                                                               int32_t *__restrict__ ids,
                                                               float *__restrict__ w) {
     __shared__ uint8_t s_grp[kMaxNe];
@@ -95,8 +178,9 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
         for (int j = 0; j < k; j++) span |= 1ull << s_grp[sel[j]];
         if (__popcll(span) > G) {
             uint64_t chosen = 0;
-            if (prune_rule == 1) {
-                // TRAVERSE: groups of the top-k list in score order, first G.
+            if (prune_rule == 1 || prune_rule == 3) {
+                // TRAVERSE (and similarity-based pruning): groups of the top-k
+                // list in score order, first G.
                 int have = 0;
                 for (int j = 0; j < k && have < G; j++) {
                     const uint64_t bit = 1ull << s_grp[sel[j]];
@@ -126,7 +210,10 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
                 }
             }
             __builtin_amdgcn_wave_barrier();
-            select_topk<NI>(l, Ne, k, chosen, s_grp, sel, sel_l);
+            if (prune_rule == 3)
+                replace_similar(sim_rank, Ne, k, chosen, s_grp, sel);
+            else
+                select_topk<NI>(l, Ne, k, chosen, s_grp, sel, sel_l);
         }
     }
 
@@ -140,15 +227,22 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
 }  // namespace
 
 hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rule, int G,
-                        const PlaceTab &tab, int32_t *ids, float *w, hipStream_t s) {
+                        const PlaceTab &tab, const int32_t *sim_rank, int32_t *ids, float *w,
+                        hipStream_t s) {
     const dim3 grid(ceil_div(T, kRouteWaves)), block(kRouteWaves * kWave);
     const int ni = (Ne + kWave - 1) / kWave;
     switch (ni) {
-        case 1: k_route<1><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, ids, w); break;
-        case 2: k_route<2><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, ids, w); break;
-        case 3: k_route<3><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, ids, w); break;
-        default: k_route<4><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, ids, w); break;
+        case 1: k_route<1><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, sim_rank, ids, w); break;
+        case 2: k_route<2><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, sim_rank, ids, w); break;
+        case 3: k_route<3><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, sim_rank, ids, w); break;
+        default: k_route<4><<<grid, block, 0, s>>>(logits, T, Ne, k, prune_rule, G, tab, sim_rank, ids, w); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sanitize_ids(const int32_t *ids_in, const float *w_in, int T, int k, int Ne,
+                               int32_t *ids, float *w, hipStream_t s) {
+    k_sanitize_ids<<<ceil_div(T, 256), 256, 0, s>>>(ids_in, w_in, T, k, Ne, ids, w);
     return hipGetLastError();
 }
 

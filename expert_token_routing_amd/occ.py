@@ -22,15 +22,16 @@ LIB_PATH = os.path.join(HERE, "libocc.so")
 
 OCC_OK, OCC_ERR_INVALID_ARG, OCC_ERR_UNSUPPORTED, OCC_ERR_WORKSPACE, OCC_ERR_HIP = range(5)
 OCC_F32, OCC_BF16 = 0, 1
-OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM = 0, 1, 2
+OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM, OCC_PRUNE_SIMILARITY = 0, 1, 2, 3
 STAGES = ["route", "brim", "dispatch", "shared", "gemm_up", "gemm_down_first", "gemm_down_rest",
           "combine"]
 OCC_STAGE_COUNT = len(STAGES)
 
-EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route", "occ_build_brim",
-            "occ_moe_forward", "occ_forward_views", "occ_coactivation_stats",
-            "occ_place_experts", "occ_events_create", "occ_events_destroy",
-            "occ_event_elapsed_ms"]
+EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route",
+            "occ_similarity_accumulate", "occ_similarity_rank", "occ_route_similarity",
+            "occ_build_brim", "occ_moe_forward", "occ_moe_forward_routed", "occ_forward_views",
+            "occ_coactivation_stats", "occ_place_experts", "occ_events_create",
+            "occ_events_destroy", "occ_event_elapsed_ms"]
 
 
 class OccError(RuntimeError):
@@ -76,10 +77,15 @@ def lib() -> ctypes.CDLL:
             "occ_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "occ_workspace_size": ([dp, ctypes.POINTER(sz)], ctypes.c_int),
             "occ_route": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "occ_similarity_accumulate": ([i32, i32, vp, vp, vp], ctypes.c_int),
+            "occ_similarity_rank": ([i32, vp, vp, vp, vp], ctypes.c_int),
+            "occ_route_similarity": ([dp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "occ_build_brim": ([dp, vp, vp, vp, ctypes.c_int, vp, sz, ctypes.POINTER(Brim), vp],
                                ctypes.c_int),
             "occ_moe_forward": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp],
                                 ctypes.c_int),
+            "occ_moe_forward_routed": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        vp, vp], ctypes.c_int),
             "occ_forward_views": ([dp, vp, ctypes.POINTER(ForwardView)], ctypes.c_int),
             "occ_coactivation_stats": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "occ_place_experts": ([vp, i32, i32, vp], ctypes.c_int),
@@ -163,6 +169,32 @@ def occ_route(desc: LayerDesc, logits, placement, ids, w, stream=None):
                            _dev(w, "w", torch.float32, (T, k)), _stream(stream)), "occ_route")
 
 
+def occ_similarity_accumulate(logits, gram, stream=None):
+    """gram (Ne x Ne fp64) += logits^T logits, one batch (appendix A.3)."""
+    T, Ne = logits.shape
+    _check(lib().occ_similarity_accumulate(
+        T, Ne, _dev(logits, "logits", torch.float32, (T, Ne)),
+        _dev(gram, "gram", torch.float64, (Ne, Ne)), _stream(stream)), "occ_similarity_accumulate")
+
+
+def occ_similarity_rank(gram, rank, t2=None, stream=None):
+    """Squared cosine table (optional t2) and per-row ranking from a Gram matrix."""
+    Ne = gram.shape[0]
+    _check(lib().occ_similarity_rank(
+        Ne, _dev(gram, "gram", torch.float64, (Ne, Ne)),
+        _dev(t2, "t2", torch.float64, (Ne, Ne)), _dev(rank, "rank", torch.int32, (Ne, Ne)),
+        _stream(stream)), "occ_similarity_rank")
+
+
+def occ_route_similarity(desc: LayerDesc, logits, placement, sim_rank, ids, w, stream=None):
+    T, Ne, k = desc.T, desc.Ne, desc.k
+    L = _host_i32(placement, "placement", (desc.Nd, Ne // desc.Nd))
+    _check(lib().occ_route_similarity(
+        ctypes.byref(desc), _dev(logits, "logits", torch.float32, (T, Ne)), _hp(L),
+        _dev(sim_rank, "sim_rank", torch.int32, (Ne, Ne)), _dev(ids, "ids", torch.int32, (T, k)),
+        _dev(w, "w", torch.float32, (T, k)), _stream(stream)), "occ_route_similarity")
+
+
 def occ_build_brim(desc: LayerDesc, ids, w, placement, workspace, dense_brim1=True,
                    stream=None) -> Brim:
     T, k = desc.T, desc.k
@@ -197,6 +229,29 @@ def occ_moe_forward(desc: LayerDesc, x, logits, placement, w_gate, w_up, w_down,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
         "occ_moe_forward")
+
+
+def occ_moe_forward_routed(desc: LayerDesc, x, ids, w, placement, w_gate, w_up, w_down, ws_gate,
+                           ws_up, ws_down, y, workspace, stage_events=None, stream=None):
+    T, d, Ne, F, k = desc.T, desc.d, desc.Ne, desc.F, desc.k
+    dt = torch.bfloat16 if desc.dtype == OCC_BF16 else torch.float32
+    L = _host_i32(placement, "placement", (desc.Nd, Ne // desc.Nd))
+    nsh, Fsh = desc.n_shared, desc.F_shared
+    sh = [None, None, None]
+    if nsh > 0:
+        sh = [_dev(ws_gate, "ws_gate", dt, (nsh, Fsh, d)), _dev(ws_up, "ws_up", dt, (nsh, Fsh, d)),
+              _dev(ws_down, "ws_down", dt, (nsh, d, Fsh))]
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * (OCC_STAGE_COUNT + 1))(*stage_events)
+    _check(lib().occ_moe_forward_routed(
+        ctypes.byref(desc), _dev(x, "x", dt, (T, d)), _dev(ids, "ids", torch.int32, (T, k)),
+        _dev(w, "w", torch.float32, (T, k)), _hp(L),
+        _dev(w_gate, "w_gate", dt, (Ne, F, d)), _dev(w_up, "w_up", dt, (Ne, F, d)),
+        _dev(w_down, "w_down", dt, (Ne, d, F)), *sh, _dev(y, "y", dt, (T, d)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
+        "occ_moe_forward_routed")
 
 
 def occ_forward_views(desc: LayerDesc, workspace) -> ForwardView:

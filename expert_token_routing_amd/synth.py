@@ -11,6 +11,8 @@ seed_base + j:
   j=3  routed expert weights ~ N(0, 0.02^2), drawn expert by expert in index
        order: gate (F x d), up (F x d), down (d x F)
   j=4  shared expert weights, drawn the same way
+  j=5, j=6  a profiling batch of router logits drawn like j=0 and j=1 (the
+       input of the expert similarity table)
 
 Values are drawn in fp32 and rounded to the workload's dtype (round to nearest
 even, torch's conversion).  Logits stay fp32.  Weight layouts follow
@@ -34,12 +36,20 @@ def _gen(w: Workload, j: int) -> torch.Generator:
     return torch.Generator().manual_seed(w.seed_base + j)
 
 
-def make_logits(w: Workload, T: int | None = None) -> torch.Tensor:
-    T = w.T if T is None else T
-    cluster = torch.randint(w.n_c, (T,), generator=_gen(w, 0))
-    noise = torch.randn(T, w.Ne, generator=_gen(w, 1), dtype=torch.float32)
+def _logits(w: Workload, T: int, j_cluster: int, j_noise: int) -> torch.Tensor:
+    cluster = torch.randint(w.n_c, (T,), generator=_gen(w, j_cluster))
+    noise = torch.randn(T, w.Ne, generator=_gen(w, j_noise), dtype=torch.float32)
     member = (torch.arange(w.Ne)[None, :] % w.n_c) == cluster[:, None]
     return (noise + w.bonus * member.to(torch.float32)).contiguous()
+
+
+def make_logits(w: Workload, T: int | None = None) -> torch.Tensor:
+    return _logits(w, w.T if T is None else T, 0, 1)
+
+
+def make_profile_logits(w: Workload, T: int = 16384) -> torch.Tensor:
+    """A profiling batch from the same distribution, drawn independently."""
+    return _logits(w, T, 5, 6)
 
 
 def make_x(w: Workload, T: int | None = None) -> torch.Tensor:

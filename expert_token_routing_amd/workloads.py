@@ -18,6 +18,7 @@ from dataclasses import dataclass, field
 PRUNE_OFF = 0
 PRUNE_TRAVERSE = 1  # groups gathered by walking the top-k list (paper, section 3.3)
 PRUNE_GROUPSUM = 2  # groups ranked by the sum of their top-k logits
+PRUNE_SIMILARITY = 3  # TRAVERSE's groups, other experts replaced by the most similar (A.3 table)
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -70,7 +71,12 @@ OLMOE_PRUNED = Workload("olmoe_pruned2_t32768", 4, T=32768, d=2048, Ne=64, k=8, 
 QWEN = Workload("qwen_t65536", 5, T=65536, d=2048, Ne=60, k=4, Nd=4, F=1408,
                 n_shared=1, F_shared=5632, n_c=10, bonus=1.0)
 
-ALL = [TINY_F32, OLMOE, DEEPSEEK, OLMOE_PRUNED, QWEN]
+# The pruned OLMoE shape under expert-similarity-based pruning (section 3.3);
+# its table is built from a separate profiling batch (synth.make_profile_logits).
+OLMOE_SIM = Workload("olmoe_sim2_t32768", 6, T=32768, d=2048, Ne=64, k=8, Nd=8, F=1024,
+                     n_c=8, bonus=1.5, prune_rule=PRUNE_SIMILARITY, prune_groups=2)
+
+ALL = [TINY_F32, OLMOE, DEEPSEEK, OLMOE_PRUNED, QWEN, OLMOE_SIM]
 BY_NAME = {w.name: w for w in ALL}
 
 

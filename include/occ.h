@@ -43,21 +43,30 @@ typedef enum occ_status {
 
 typedef enum occ_dtype { OCC_F32 = 0, OCC_BF16 = 1 } occ_dtype;
 
-/* Collaboration pruning (paper, section 3.3, routing-score-based): each token
- * may use experts on at most prune_groups groups, and takes the top k experts,
- * by routing score, among those groups' experts.  The groups are chosen
+/* Collaboration pruning (paper, section 3.3): each token may use experts on
+ * at most prune_groups groups.
+ * Routing-score-based: the token takes the top k experts, by routing score,
+ * among the chosen groups' experts.  The groups are chosen
  *   TRAVERSE: by walking the token's plain top-k experts in descending score
  *             and collecting their groups until prune_groups are reached
  *             (the paper's rule);
  *   GROUPSUM: by ranking the groups that hold at least one plain top-k expert
  *             by the fp32 sum, taken in top-k order, of those experts' logits
  *             (ties to the lower group) and keeping prune_groups of them.
- * Weights stay the full-softmax probabilities (not renormalised).  A token
- * whose plain top k already spans <= prune_groups groups is unchanged. */
+ * Weights stay the full-softmax probabilities (not renormalised).
+ * Expert-similarity-based (SIMILARITY, occ_route_similarity only): the groups
+ * are chosen as by TRAVERSE; the plain top-k experts in them stay where they
+ * are, and each other one, in descending score, is replaced by the first
+ * expert of its row of the ranked similarity table (appendix A.3, see
+ * occ_similarity_rank) that lies in a chosen group and is not yet selected;
+ * the replacement takes over the replaced expert's weight.
+ * A token whose plain top k already spans <= prune_groups groups is unchanged
+ * under every rule. */
 typedef enum occ_prune_rule {
     OCC_PRUNE_OFF = 0,
     OCC_PRUNE_TRAVERSE = 1,
-    OCC_PRUNE_GROUPSUM = 2
+    OCC_PRUNE_GROUPSUM = 2,
+    OCC_PRUNE_SIMILARITY = 3
 } occ_prune_rule;
 
 /* Shape of one MoE layer.  Limits of this build:
@@ -173,16 +182,57 @@ occ_status occ_workspace_size(const occ_layer_desc *desc, size_t *bytes_host);
  *                    order, ties to the lower expert index.
  *   w    (out)       T x k fp32: their softmax probabilities over all Ne
  *                    logits, not renormalised.
- * NaN or infinite logits give unspecified (but in-bounds) ids. */
+ * A NaN logit ranks as -inf (the ids stay distinct and in range; the weights
+ * are then unspecified).  prune_rule SIMILARITY needs the table: use
+ * occ_route_similarity (INVALID_ARG here). */
 occ_status occ_route(const occ_layer_desc *desc, const float *logits,
                      const int32_t *placement_host, int32_t *ids, float *w, void *stream);
+
+/* Expert similarity table, paper appendix A.3, Eq. 6-8, built from profiled
+ * router logits H (tokens x Ne) in batches.
+ * occ_similarity_accumulate adds one batch to the Gram matrix of H's columns:
+ *   gram[i][j] += sum over the batch's tokens t of H[t][i] * H[t][j],
+ * in fp64, each entry summed in ascending token order (the fp32 products are
+ * exact in fp64, so the result does not depend on the launch shape).
+ *   T            tokens in this batch (0 is a no-op);  1 <= Ne <= 256.
+ *   logits       T x Ne fp32 (device).
+ *   gram         Ne x Ne fp64 (device, in/out); zero it before the first batch.
+ * Errors: INVALID_ARG for a NULL pointer or a bad size. */
+occ_status occ_similarity_accumulate(int32_t T, int32_t Ne, const float *logits, double *gram,
+                                     void *stream);
+
+/* The table from an accumulated Gram matrix.  Eq. 7 (Eq. 8 equals it: its
+ * 1/N factors cancel): t2[i][j] = gram[i][j]^2 / (gram[i][i] * gram[j][j]),
+ * 0 when either column was all zero.  The paper declares the table integer;
+ * it is read as each row's ranking: rank[i][q] is the q-th most similar
+ * expert to i by t2 descending, ties to the lower index, so every row is a
+ * permutation of 0..Ne-1 (and starts with i unless i's column was zero).
+ *   gram   Ne x Ne fp64 (device);  t2 (out) Ne x Ne fp64 or NULL;
+ *   rank (out) Ne x Ne int32 (device). */
+occ_status occ_similarity_rank(int32_t Ne, const double *gram, double *t2, int32_t *rank,
+                               void *stream);
+
+/* Router with expert-similarity-based collaboration pruning (section 3.3,
+ * see occ_prune_rule).  desc->prune_rule must be OCC_PRUNE_SIMILARITY.
+ * Arguments as occ_route, plus
+ *   sim_rank   Ne x Ne int32 (device), as written by occ_similarity_rank;
+ *              each row must be a permutation of 0..Ne-1 (otherwise the ids
+ *              are unspecified but in range).
+ * ids keep the plain top-k order (a replacement sits at the replaced
+ * expert's place) and w the plain top-k weights. */
+occ_status occ_route_similarity(const occ_layer_desc *desc, const float *logits,
+                                const int32_t *placement_host, const int32_t *sim_rank,
+                                int32_t *ids, float *w, void *stream);
 
 /* BRIM_0 and BRIM_1, paper appendix A.2 (Algorithms 3 and 5), from routing
  * ids/w (T x k, as written by occ_route) and the placement (host, as above).
  * Writes the structures of occ_brim into `workspace` (ws_bytes >=
  * occ_workspace_size) and returns their device addresses in *out_host.
- * dense_brim1 != 0 also writes the dense BRIM_1 matrices.  ids must lie in
- * 0..Ne-1 and be distinct within a token. */
+ * dense_brim1 != 0 also writes the dense BRIM_1 matrices.  The routing is
+ * first copied into the workspace (occ_forward_views: ids, w), where a
+ * token's id outside 0..Ne-1 or repeating an earlier one is replaced by the
+ * lowest expert not in its list, with weight 0; valid routing is copied
+ * unchanged. */
 occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const float *w,
                           const int32_t *placement_host, int dense_brim1, void *workspace,
                           size_t ws_bytes, occ_brim *out_host, void *stream);
@@ -211,6 +261,19 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
                            const void *ws_down, void *y, void *workspace, size_t ws_bytes,
                            void *const *stage_events, void *stream);
 
+/* The layer from a routing computed elsewhere (for instance by
+ * occ_route_similarity): occ_moe_forward without its router stage.
+ *   ids, w   T x k int32 / fp32 (device): each token's experts and weights;
+ *            sanitised into the workspace as for occ_build_brim.
+ * Other arguments as occ_moe_forward; desc->prune_rule is not used.  The
+ * route stage's events time that copy. */
+occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, const int32_t *ids,
+                                  const float *w, const int32_t *placement_host,
+                                  const void *w_gate, const void *w_up, const void *w_down,
+                                  const void *ws_gate, const void *ws_up, const void *ws_down,
+                                  void *y, void *workspace, size_t ws_bytes,
+                                  void *const *stage_events, void *stream);
+
 /* Device addresses of the intermediates occ_moe_forward leaves in a
  * workspace (pure host arithmetic, nothing queued). */
 occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
@@ -226,7 +289,9 @@ occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
  *   ct (out)     1 fp64: CT = n_sfd / T, the mean replicas per token (section
  *                2.2), bounded by Eq. 5: ceil(k*Nd/Ne) <= CT <= min(k, Nd).
  *   intra (out)  1 fp64: share of the off-diagonal co-activations whose two
- *                experts share a group (the Intra / Inter split of Table 1). */
+ *                experts share a group (the Intra / Inter split of Table 1).
+ * ids are expected distinct within a token and in 0..Ne-1; an id out of
+ * range is counted as expert 0 (unspecified statistics, in-bounds writes). */
 occ_status occ_coactivation_stats(const occ_layer_desc *desc, const int32_t *ids,
                                   const int32_t *placement_host, int32_t *C, float *P,
                                   int64_t *n_sfd, double *ct, double *intra, void *stream);

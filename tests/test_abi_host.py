@@ -64,7 +64,8 @@ def _ws(desc):
     (dict(k=65), occ.OCC_ERR_INVALID_ARG),           # k > Ne
     (dict(Nd=7), occ.OCC_ERR_INVALID_ARG),           # Ne % Nd != 0
     (dict(dtype=5), occ.OCC_ERR_INVALID_ARG),
-    (dict(prune_rule=3), occ.OCC_ERR_INVALID_ARG),
+    (dict(prune_rule=4), occ.OCC_ERR_INVALID_ARG),
+    (dict(prune_rule=3, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=1, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=2, prune_groups=1, k=9), occ.OCC_ERR_INVALID_ARG),  # 1 group of 8 < k
     (dict(flags=1), occ.OCC_ERR_INVALID_ARG),
@@ -137,6 +138,36 @@ def test_calls_reject_bad_pointers_and_placements_without_a_gpu(L):
     assert L.occ_place_experts(_null(), 64, 8, fake) == occ.OCC_ERR_INVALID_ARG
     C = np.zeros((64, 64), np.int32)
     assert L.occ_place_experts(hp(C), 64, 7, hp(np.zeros(64, np.int32))) == occ.OCC_ERR_INVALID_ARG
+
+
+def test_similarity_and_routed_calls_validate_without_a_gpu(L):
+    wl = W.OLMOE
+    good = np.ascontiguousarray(synth.contiguous_placement(wl))
+    fake = ctypes.c_void_p(0x1000)
+    hp = lambda a: ctypes.c_void_p(a.ctypes.data)
+    inv = occ.OCC_ERR_INVALID_ARG
+    # table building: sizes and pointers
+    assert L.occ_similarity_accumulate(-1, 64, fake, fake, _null()) == inv
+    assert L.occ_similarity_accumulate(8, 0, fake, fake, _null()) == inv
+    assert L.occ_similarity_accumulate(8, 257, fake, fake, _null()) == inv
+    assert L.occ_similarity_accumulate(8, 64, _null(), fake, _null()) == inv
+    assert L.occ_similarity_accumulate(8, 64, fake, _null(), _null()) == inv
+    assert L.occ_similarity_rank(0, fake, _null(), fake, _null()) == inv
+    assert L.occ_similarity_rank(64, fake, _null(), _null(), _null()) == inv
+    # the similarity rule needs the table; the table needs that rule
+    sim = occ.desc_of(wl, prune_rule=occ.OCC_PRUNE_SIMILARITY, prune_groups=2)
+    plain = occ.desc_of(wl)
+    assert L.occ_route(ctypes.byref(sim), fake, hp(good), fake, fake, _null()) == inv
+    assert L.occ_route_similarity(ctypes.byref(plain), fake, hp(good), fake, fake, fake, _null()) == inv
+    assert L.occ_route_similarity(ctypes.byref(sim), fake, hp(good), _null(), fake, fake, _null()) == inv
+    # forward: the router cannot run the similarity rule; the routed form needs ids and w
+    _, ws = _ws(sim)
+    assert L.occ_moe_forward(ctypes.byref(sim), fake, fake, hp(good), fake, fake, fake, None, None,
+                             None, fake, fake, ws, None, None) == inv
+    routed = lambda ids, w: L.occ_moe_forward_routed(ctypes.byref(plain), fake, ids, w, hp(good),
+                                                     fake, fake, fake, None, None, None, fake,
+                                                     fake, ws, None, None)
+    assert routed(_null(), fake) == inv and routed(fake, _null()) == inv
 
 
 @pytest.mark.parametrize("Ne,Nd,seed", [(64, 8, 0), (60, 4, 1), (8, 2, 2), (16, 16, 3), (12, 1, 4),
