@@ -13,6 +13,8 @@ seed_base + j:
   j=4  shared expert weights, drawn the same way
   j=5, j=6  a profiling batch of router logits drawn like j=0 and j=1 (the
        input of the expert similarity table)
+  j=7  router (gate projection) weights W_r ~ N(0, 1/d), Ne x d, for the
+       workloads that compute their logits as x W_r^T
 
 Values are drawn in fp32 and rounded to the workload's dtype (round to nearest
 even, torch's conversion).  Logits stay fp32.  Weight layouts follow
@@ -83,6 +85,13 @@ def make_shared_weights(w: Workload):
     return _expert_weights(w, w.n_shared, w.F_shared, 4)
 
 
+def make_router_weights(w: Workload) -> torch.Tensor:
+    """Gate projection W_r (Ne, d) in the workload dtype: logits x W_r^T then
+    have unit variance for x ~ N(0, 1)."""
+    wr = torch.randn(w.Ne, w.d, generator=_gen(w, 7), dtype=torch.float32) / np.sqrt(w.d)
+    return wr.to(torch_dtype(w)).contiguous()
+
+
 def contiguous_placement(w: Workload) -> np.ndarray:
     """Group g holds experts g*n .. g*n+n-1, in that order."""
     return np.arange(w.Ne, dtype=np.int32).reshape(w.Nd, w.n)
@@ -92,7 +101,8 @@ def make_all(w: Workload, T: int | None = None) -> dict:
     gate, up, down = make_weights(w)
     sg, su, sd = make_shared_weights(w)
     return dict(logits=make_logits(w, T), x=make_x(w, T), w_gate=gate, w_up=up, w_down=down,
-                ws_gate=sg, ws_up=su, ws_down=sd, placement=contiguous_placement(w))
+                ws_gate=sg, ws_up=su, ws_down=sd, placement=contiguous_placement(w),
+                w_router=make_router_weights(w) if w.gated else None)
 
 
 def sample_rows(T: int, count: int, seed: int = 99) -> np.ndarray:

@@ -41,6 +41,7 @@ class Workload:
     bonus: float = 1.5  # logit bonus on the token's cluster
     prune_rule: int = PRUNE_OFF
     prune_groups: int = 0
+    gated: bool = False  # logits computed on the device as x W_r^T (gate projection)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -76,7 +77,13 @@ QWEN = Workload("qwen_t65536", 5, T=65536, d=2048, Ne=60, k=4, Nd=4, F=1408,
 OLMOE_SIM = Workload("olmoe_sim2_t32768", 6, T=32768, d=2048, Ne=64, k=8, Nd=8, F=1024,
                      n_c=8, bonus=1.5, prune_rule=PRUNE_SIMILARITY, prune_groups=2)
 
-ALL = [TINY_F32, OLMOE, DEEPSEEK, OLMOE_PRUNED, QWEN, OLMOE_SIM]
+# Decode regime: one step of a batch of 512 concurrent requests (the decoding
+# batch of the paper's Figure 10) through the OLMoE-shaped layer, its router
+# logits computed from the tokens by the gate projection.
+OLMOE_DECODE = Workload("olmoe_decode_t512", 7, T=512, d=2048, Ne=64, k=8, Nd=8, F=1024,
+                        n_c=8, bonus=1.5, gated=True)
+
+ALL = [TINY_F32, OLMOE, DEEPSEEK, OLMOE_PRUNED, QWEN, OLMOE_SIM, OLMOE_DECODE]
 BY_NAME = {w.name: w for w in ALL}
 
 

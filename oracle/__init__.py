@@ -123,6 +123,21 @@ def route_similarity(logits: np.ndarray, k: int, placement: np.ndarray, prune_gr
     return ids, w
 
 
+def gate(rows, x, w_router) -> np.ndarray:
+    """Router logits g(x) = x W_r^T (section 2.1) of the listed rows, fp64:
+    (len(rows), Ne)."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    xa, dt = _float_arg(x)
+    wa, dw = _float_arg(w_router)
+    if dt != dw:
+        raise TypeError("x and w_router must share a dtype")
+    d = xa.shape[1]
+    Ne = wa.shape[0]
+    out = np.empty((len(rows), Ne), np.float64)
+    _check(_load().orc_gate(len(rows), _p(rows), d, Ne, dt, _p(xa), _p(wa), _p(out)), "gate")
+    return out
+
+
 def brim0(ids: np.ndarray, Ne: int, placement: np.ndarray):
     """BRIM_0 of Algorithm 3: (Nd, T) int32 and sfd_off (Nd+1) int64."""
     ids = _i32(ids)

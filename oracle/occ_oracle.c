@@ -430,6 +430,26 @@ static void shared_add(const double *x, int n_sh, int F_sh, int d, int dtype, co
 }
 
 /*
+ * Gate projection g(x) (section 2.1: the router logits come from a single
+ * linear layer): logits[t][e] = sum_i x[t][i] * W_r[e][i], fp64, for the
+ * listed rows.  W_r is Ne x d (nn.Linear layout), x and W_r fp32 or bf16.
+ */
+int orc_gate(int nrows, const int64_t *rows, int d, int Ne, int dtype, const void *x,
+             const void *Wr, double *logits)
+{
+    if (nrows < 0 || d < 1 || Ne < 1)
+        return ORC_BAD;
+    for (int i = 0; i < nrows; i++)
+        for (int e = 0; e < Ne; e++) {
+            double s = 0.0;
+            for (int c = 0; c < d; c++)
+                s += elem(x, dtype, (size_t)rows[i] * d + c) * elem(Wr, dtype, (size_t)e * d + c);
+            logits[(size_t)i * Ne + e] = s;
+        }
+    return ORC_OK;
+}
+
+/*
  * Layer output, Eq. 1 (section 2.1): MoE(x) = sum_i R(x)_i E_i(x), the sum
  * running over the k routed experts of the token (the other entries of R are
  * zero), plus the shared experts.  One row per requested token, in fp64.

@@ -165,6 +165,29 @@ def test_route_rejects_infeasible_pruning():
 
 
 # --------------------------------------------------------------------------
+# Gate projection g(x) (section 2.1)
+
+
+def test_gate_matches_float64_matmul_and_unit_rows():
+    wl = W.OLMOE_DECODE
+    x = synth.make_x(wl, 40)
+    wr = synth.make_router_weights(wl)
+    rows = np.array([0, 7, 39, 7], np.int64)
+    got = oracle.gate(rows, as_oracle(x), as_oracle(wr))
+    ref = (x.double() @ wr.double().T).numpy()[rows]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # unit rows pick coordinates of x exactly
+    eye = torch.zeros(5, wl.d, dtype=torch.bfloat16)
+    for e, c in enumerate([0, 3, 2047, 1000, 3]):
+        eye[e, c] = 1.0
+    sel = oracle.gate(np.arange(40), as_oracle(x), as_oracle(eye))
+    assert np.array_equal(sel, x.double().numpy()[:, [0, 3, 2047, 1000, 3]])
+    # the synthetic router weights give logits of about unit variance
+    full = oracle.gate(np.arange(40), as_oracle(x), as_oracle(wr))
+    assert 0.8 < full.std() < 1.2
+
+
+# --------------------------------------------------------------------------
 # Expert similarity table (appendix A.3, Eq. 6-8) and similarity-based
 # pruning (section 3.3)
 
