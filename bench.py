@@ -88,6 +88,11 @@ def main():
         table_ms = e0.elapsed_time(e1)
         log(f"[bench] similarity table from {prof.shape[0]} profiled tokens: {table_ms:.3f} ms")
 
+    if wl.gated:
+        # decode path: the logits come from the tokens (gate projection)
+        g["logits"] = torch.empty(wl.T, wl.Ne, dtype=torch.float32, device=dev)
+        occ.occ_gate(desc, g["x"], g["w_router"], g["logits"])
+
     # --- placement (offline step, untimed): Algorithm 1 on this batch's counts
     L_contig = inp["placement"]
     ids = torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev)
@@ -115,6 +120,11 @@ def main():
     def run(L, steps, events=None, route_events=None):
         for i in range(steps):
             ev = events[i].handles if events is not None else None
+            if wl.gated:
+                occ.occ_moe_forward_gated(desc, g["x"], g["w_router"], L, g["w_gate"], g["w_up"],
+                                          g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], y,
+                                          ws, stage_events=ev)
+                continue
             if not sim:
                 occ.occ_moe_forward(desc, g["x"], g["logits"], L, g["w_gate"], g["w_up"],
                                     g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], y, ws,
@@ -175,15 +185,28 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    # --- roofline of the dominant kernel: the up-projection grouped GEMM
+    # --- roofline of the dominant kernel: the up-projection grouped GEMM.
+    # Algorithmic work per launch: 2*d*2F flops per EPD row (T*k rows); bytes:
+    # the gate and up weights of every expert that has rows, each SFD row
+    # read once and each EPD row written once.  The bound is the one the
+    # kernel's flops per byte put it under (ridge: peak flops / peak HBM).
+    es = 2 if wl.dtype == W.DTYPE_BF16 else 4
     up_ms = stages["gemm_up"]
     flops_up = 2.0 * wl.T * wl.k * wl.d * 2 * wl.F
-    achieved = flops_up / (up_ms / 1e3) / 1e12
-    traffic = profiling.traffic_bytes("k_gemm_up", wl.name, "gemm_bf16.hip")
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "k_gemm_up", "avg_ms": round(up_ms, 5),
-                "flops_per_launch": flops_up}
+    active = int((torch.diagonal(C) > 0).sum().item())
+    bytes_up = (active * 2 * wl.F * wl.d + nsfd_alg1 * wl.d + wl.T * wl.k * wl.F) * es
+    up_kernel = "k_gemm_up_m64" if wl.T * wl.k < 128 * wl.Ne and es == 2 else "k_gemm_up"
+    traffic = profiling.traffic_bytes(up_kernel, wl.name, "gemm_bf16.hip")
+    if flops_up / bytes_up >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops_up / (up_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = bytes_up / (up_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": traffic, "kernel": up_kernel, "avg_ms": round(up_ms, 5),
+                     "flops_per_launch": flops_up, "bytes_per_launch": bytes_up})
 
     # --- CPU baseline: the oracle on a bounded sample of this workload
     cpu = None
@@ -221,12 +244,15 @@ def cpu_baseline(wl, inp, placement, seconds, sim_rank=None):
 
     log("[bench] cpu baseline: oracle route/BRIM/stats on the full batch")
     t0 = time.perf_counter()
+    logits = inp["logits"].numpy()
+    if wl.gated:
+        xb = inp["x"].contiguous().view(torch.int16).numpy().view(np.uint16)
+        wb = inp["w_router"].contiguous().view(torch.int16).numpy().view(np.uint16)
+        logits = oracle.gate(np.arange(wl.T), xb, wb).astype(np.float32)
     if sim_rank is not None:
-        ids, w = oracle.route_similarity(inp["logits"].numpy(), wl.k, placement,
-                                         wl.prune_groups, sim_rank)
+        ids, w = oracle.route_similarity(logits, wl.k, placement, wl.prune_groups, sim_rank)
     else:
-        ids, w = oracle.route(inp["logits"].numpy(), wl.k, placement, wl.prune_rule,
-                              wl.prune_groups)
+        ids, w = oracle.route(logits, wl.k, placement, wl.prune_rule, wl.prune_groups)
     oracle.brim1(ids, w, wl.Ne, placement)
     oracle.coact(ids, wl.Ne, placement)
     t_index = time.perf_counter() - t0

@@ -18,12 +18,26 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 size_t elem_bytes(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? 2 : 4; }
-int tile_rows(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? kGemmBmBf16 : kGemmBmF32; }
+// The grouped GEMM kernels for a shape.  bf16 batches whose experts average
+// fewer than 128 rows (T*k < 128*Ne, e.g. decode steps) take the 64-row
+// tiles: 256-row tiles would spend most of their MFMA work on padding.
+struct GemmOps {
+    hipError_t (*up)(const UpArgs &, size_t, hipStream_t);
+    hipError_t (*down)(const DownArgs &, size_t, hipStream_t);
+    int bm;
+};
+GemmOps gemm_ops(const occ_layer_desc &D) {
+    if (D.dtype != OCC_BF16) return {launch_gemm_up_f32, launch_gemm_down_f32, kGemmBmF32};
+    if (static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne)
+        return {launch_gemm_up_bf16_m64, launch_gemm_down_bf16_m64, kGemmBmBf16Small};
+    return {launch_gemm_up_bf16, launch_gemm_down_bf16, kGemmBmBf16};
+}
+int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
 
 // Byte offsets of every buffer inside the workspace.  Sized for the worst
 // case N_sfd = T * min(k, Nd), so no data-dependent size is read back.
 struct Layout {
-    size_t ids, w, brim0, sfd_off, epd_off, tile_off, tile_off_first, tile_off_rest, first_cnt,
+    size_t logits, ids, w, brim0, sfd_off, epd_off, tile_off, tile_off_first, tile_off_rest, first_cnt,
         chunk_cnt, chunk_base, epd_src, epd_w, tok_epd, down_rows, brim1, brim_end, x_sfd, epd,
         sfd_out, h_sh, y_sh, total;
 };
@@ -39,6 +53,7 @@ Layout layout(const occ_layer_desc &D) {
         o = align_up(o + std::max<size_t>(bytes, 1));
         return r;
     };
+    L.logits = take(T * Ne * 4);
     L.ids = take(nepd * 4);
     L.w = take(nepd * 4);
     L.brim0 = take(Nd * T * 4);
@@ -256,6 +271,7 @@ occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
     if (!workspace || !out_host) return OCC_ERR_INVALID_ARG;
     const Layout L = layout(*desc);
     occ_forward_view v;
+    v.logits = at<float>(workspace, L.logits);
     v.ids = at<int32_t>(workspace, L.ids);
     v.w = at<float>(workspace, L.w);
     v.brim = brim_view(workspace, L);
@@ -268,10 +284,11 @@ occ_status occ_forward_views(const occ_layer_desc *desc, void *workspace,
     return OCC_OK;
 }
 
-// The layer's stage sequence.  Stage 0 routes `logits` (the desc's rule) or,
-// with logits NULL, copies the caller's routing ids_in / w_in.
+// The layer's stage sequence.  Stage 0 routes `logits` (the desc's rule),
+// or first computes them as x w_router^T when w_router is given, or, with
+// neither, copies the caller's routing ids_in / w_in.
 static occ_status forward(const occ_layer_desc *desc, const void *x, const float *logits,
-                          const int32_t *ids_in, const float *w_in,
+                          const void *w_router, const int32_t *ids_in, const float *w_in,
                           const int32_t *placement_host, const void *w_gate, const void *w_up,
                           const void *w_down, const void *ws_gate, const void *ws_up,
                           const void *ws_down, void *y, void *workspace, size_t ws_bytes,
@@ -279,7 +296,8 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     OCC_TRY(check_desc(desc));
     const occ_layer_desc &D = *desc;
     if (!x || !w_gate || !w_up || !w_down || !y) return OCC_ERR_INVALID_ARG;
-    if (logits ? D.prune_rule == OCC_PRUNE_SIMILARITY : (!ids_in || !w_in))
+    const bool routes = logits || w_router;
+    if (routes ? D.prune_rule == OCC_PRUNE_SIMILARITY : (!ids_in || !w_in))
         return OCC_ERR_INVALID_ARG;
     if (D.n_shared > 0 && (!ws_gate || !ws_up || !ws_down)) return OCC_ERR_INVALID_ARG;
     if (stage_events)
@@ -305,12 +323,19 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     float *sfd_out = at<float>(workspace, L.sfd_out);
     float *y_sh = D.n_shared > 0 ? at<float>(workspace, L.y_sh) : nullptr;
     const size_t T = D.T;
-    const size_t bm = tile_rows(D);
+    const GemmOps ops = gemm_ops(D);
+    const size_t bm = ops.bm;
     const size_t routed_tiles = (T * D.k + bm - 1) / bm + D.Ne;
     const size_t shared_tiles = (T + bm - 1) / bm;
 
     OCC_TRY(mark(0));
-    // Eq. 2: router (or the caller's routing, checked)
+    // Eq. 2: router, behind the gate projection g(x) when its weights are
+    // given (or the caller's routing, checked)
+    if (w_router) {
+        float *lg = at<float>(workspace, L.logits);
+        OCC_HIP(launch_gate(x, w_router, D.T, D.d, D.Ne, bf16, lg, s));
+        logits = lg;
+    }
     if (logits)
         OCC_HIP(launch_route(logits, D.T, D.Ne, D.k, D.prune_rule, D.prune_groups, tab, nullptr,
                              ids, w, s));
@@ -345,9 +370,8 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         sd.Ne = 1;
         sd.k_split = D.F_shared;
         sd.tab = tab;
-        OCC_HIP(bf16 ? launch_gemm_up_bf16(su, shared_tiles, s) : launch_gemm_up_f32(su, shared_tiles, s));
-        OCC_HIP(bf16 ? launch_gemm_down_bf16(sd, shared_tiles, s)
-                     : launch_gemm_down_f32(sd, shared_tiles, s));
+        OCC_HIP(ops.up(su, shared_tiles, s));
+        OCC_HIP(ops.down(sd, shared_tiles, s));
     }
     OCC_TRY(mark(4));
     // Algorithms 6-7: SFD -> EPD, SwiGLU, weight modulation
@@ -365,7 +389,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     up.N = D.F;
     up.Ne = D.Ne;
     up.tab = tab;
-    OCC_HIP(bf16 ? launch_gemm_up_bf16(up, routed_tiles, s) : launch_gemm_up_f32(up, routed_tiles, s));
+    OCC_HIP(ops.up(up, routed_tiles, s));
     OCC_TRY(mark(5));
     // Algorithm 8: EPD -> SFD, summed inside each group in fp32.  The first
     // contributor to every SFD row stores (so no zero-fill is needed), then
@@ -386,11 +410,11 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     dn.tab = tab;
     dn.phase = 1;
     dn.tile_off = bb.tile_off_first;
-    OCC_HIP(bf16 ? launch_gemm_down_bf16(dn, routed_tiles, s) : launch_gemm_down_f32(dn, routed_tiles, s));
+    OCC_HIP(ops.down(dn, routed_tiles, s));
     OCC_TRY(mark(6));
     dn.phase = 2;
     dn.tile_off = bb.tile_off_rest;
-    OCC_HIP(bf16 ? launch_gemm_down_bf16(dn, routed_tiles, s) : launch_gemm_down_f32(dn, routed_tiles, s));
+    OCC_HIP(ops.down(dn, routed_tiles, s));
     OCC_TRY(mark(7));
     // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once
     OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
@@ -404,8 +428,28 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
                            const void *ws_down, void *y, void *workspace, size_t ws_bytes,
                            void *const *stage_events, void *stream) {
     if (!logits) return OCC_ERR_INVALID_ARG;
-    return forward(desc, x, logits, nullptr, nullptr, placement_host, w_gate, w_up, w_down,
-                   ws_gate, ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+    return forward(desc, x, logits, nullptr, nullptr, nullptr, placement_host, w_gate, w_up,
+                   w_down, ws_gate, ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+}
+
+occ_status occ_moe_forward_gated(const occ_layer_desc *desc, const void *x, const void *w_router,
+                                 const int32_t *placement_host, const void *w_gate,
+                                 const void *w_up, const void *w_down, const void *ws_gate,
+                                 const void *ws_up, const void *ws_down, void *y,
+                                 void *workspace, size_t ws_bytes, void *const *stage_events,
+                                 void *stream) {
+    if (!w_router) return OCC_ERR_INVALID_ARG;
+    return forward(desc, x, nullptr, w_router, nullptr, nullptr, placement_host, w_gate, w_up,
+                   w_down, ws_gate, ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+}
+
+occ_status occ_gate(const occ_layer_desc *desc, const void *x, const void *w_router,
+                    float *logits, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!x || !w_router || !logits) return OCC_ERR_INVALID_ARG;
+    OCC_HIP(launch_gate(x, w_router, desc->T, desc->d, desc->Ne, desc->dtype == OCC_BF16, logits,
+                        static_cast<hipStream_t>(stream)));
+    return OCC_OK;
 }
 
 occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, const int32_t *ids,
@@ -415,7 +459,7 @@ occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, con
                                   void *y, void *workspace, size_t ws_bytes,
                                   void *const *stage_events, void *stream) {
     if (!ids || !w) return OCC_ERR_INVALID_ARG;
-    return forward(desc, x, nullptr, ids, w, placement_host, w_gate, w_up, w_down, ws_gate,
+    return forward(desc, x, nullptr, nullptr, ids, w, placement_host, w_gate, w_up, w_down, ws_gate,
                    ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
 }
 

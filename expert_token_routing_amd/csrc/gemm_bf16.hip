@@ -53,7 +53,19 @@ typedef f32x4 f32x4_t;
 #ifndef OCC_XCD_MAP
 #define OCC_XCD_MAP 1
 #endif
-constexpr int BM = kGemmBmBf16;   // rows (tokens) per tile
+// One source, two row-tile sizes: this file builds the kGemmBmBf16-row
+// kernels; gemm_bf16_m64.hip includes it with 64-row tiles and suffixed
+// kernel and launcher names.
+#ifndef OCC_GEMM_TILE_M
+#define OCC_GEMM_TILE_M kGemmBmBf16
+#endif
+#ifndef OCC_GEMM_SUFFIX
+#define OCC_GEMM_SUFFIX
+#endif
+#define OCC_CAT2(a, b) a##b
+#define OCC_CAT(a, b) OCC_CAT2(a, b)
+#define OCC_NAMED(name) OCC_CAT(name, OCC_GEMM_SUFFIX)
+constexpr int BM = OCC_GEMM_TILE_M;  // rows (tokens) per tile
 constexpr int BN = 256;           // MFMA columns per tile
 constexpr int BK = OCC_GEMM_BK;   // K slice
 #ifndef OCC_GEMM_NT
@@ -311,7 +323,7 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
 #endif
 
 // Second bound: waves per SIMD = workgroups per CU x NT / 256.
-__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void k_gemm_up(UpArgs a) {
+__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k_gemm_up)(UpArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void k_gemm_up(U
     }
 }
 
-__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void k_gemm_down(DownArgs a) {
+__global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k_gemm_down)(DownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t, a.first_cnt,
@@ -459,17 +471,17 @@ unsigned grid_for(size_t m_tiles, size_t n_tiles) {
 
 }  // namespace
 
-hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
+hipError_t OCC_NAMED(launch_gemm_up_bf16)(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
     const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, 128));
     if (grid == 0) return hipSuccess;
-    k_gemm_up<<<grid, NT, 0, s>>>(a);
+    OCC_NAMED(k_gemm_up)<<<grid, NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
+hipError_t OCC_NAMED(launch_gemm_down_bf16)(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
     const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, BN));
     if (grid == 0) return hipSuccess;
-    k_gemm_down<<<grid, NT, 0, s>>>(a);
+    OCC_NAMED(k_gemm_down)<<<grid, NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -18,6 +18,11 @@ hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rul
 hipError_t launch_sanitize_ids(const int32_t *ids_in, const float *w_in, int T, int k, int Ne,
                                int32_t *ids, float *w, hipStream_t s);
 
+// --- gate projection (gate.hip) ---
+// logits (T x Ne fp32) = x (T x d) . w_router (Ne x d)^T, bf16 or fp32 inputs.
+hipError_t launch_gate(const void *x, const void *w_router, int T, int d, int Ne, int bf16,
+                       float *logits, hipStream_t s);
+
 // --- expert similarity table (similarity.hip) ---
 // gram += H^T H (fp64, tokens ascending); H is T x Ne fp32.
 hipError_t launch_sim_gram(const float *H, int T, int Ne, double *gram, hipStream_t s);
@@ -82,6 +87,10 @@ struct DownArgs {
     PlaceTab tab;
 };
 hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+// The same with 64-row tiles (gemm_bf16_m64.hip).
+constexpr int kGemmBmBf16Small = 64;
+hipError_t launch_gemm_up_bf16_m64(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
+hipError_t launch_gemm_down_bf16_m64(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 
 // --- the same two GEMMs in fp32 on the vector ALUs (gemm_f32.hip) ---
 hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s);

@@ -29,7 +29,8 @@ OCC_STAGE_COUNT = len(STAGES)
 
 EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route",
             "occ_similarity_accumulate", "occ_similarity_rank", "occ_route_similarity",
-            "occ_build_brim", "occ_moe_forward", "occ_moe_forward_routed", "occ_forward_views",
+            "occ_build_brim", "occ_moe_forward", "occ_moe_forward_routed", "occ_gate",
+            "occ_moe_forward_gated", "occ_forward_views",
             "occ_coactivation_stats", "occ_place_experts", "occ_events_create",
             "occ_events_destroy", "occ_event_elapsed_ms"]
 
@@ -55,7 +56,8 @@ class Brim(ctypes.Structure):
 
 
 class ForwardView(ctypes.Structure):
-    _fields_ = [("ids", ctypes.c_void_p), ("w", ctypes.c_void_p), ("brim", Brim),
+    _fields_ = [("logits", ctypes.c_void_p), ("ids", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("brim", Brim),
                 ("x_sfd", ctypes.c_void_p), ("epd", ctypes.c_void_p),
                 ("sfd_out", ctypes.c_void_p), ("h_shared", ctypes.c_void_p),
                 ("y_shared", ctypes.c_void_p)]
@@ -86,6 +88,9 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_int),
             "occ_moe_forward_routed": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         vp, vp], ctypes.c_int),
+            "occ_gate": ([dp, vp, vp, vp, vp], ctypes.c_int),
+            "occ_moe_forward_gated": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp],
+                                      ctypes.c_int),
             "occ_forward_views": ([dp, vp, ctypes.POINTER(ForwardView)], ctypes.c_int),
             "occ_coactivation_stats": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "occ_place_experts": ([vp, i32, i32, vp], ctypes.c_int),
@@ -252,6 +257,37 @@ def occ_moe_forward_routed(desc: LayerDesc, x, ids, w, placement, w_gate, w_up, 
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
         "occ_moe_forward_routed")
+
+
+def occ_gate(desc: LayerDesc, x, w_router, logits, stream=None):
+    T, d, Ne = desc.T, desc.d, desc.Ne
+    dt = torch.bfloat16 if desc.dtype == OCC_BF16 else torch.float32
+    _check(lib().occ_gate(ctypes.byref(desc), _dev(x, "x", dt, (T, d)),
+                          _dev(w_router, "w_router", dt, (Ne, d)),
+                          _dev(logits, "logits", torch.float32, (T, Ne)), _stream(stream)),
+           "occ_gate")
+
+
+def occ_moe_forward_gated(desc: LayerDesc, x, w_router, placement, w_gate, w_up, w_down, ws_gate,
+                          ws_up, ws_down, y, workspace, stage_events=None, stream=None):
+    T, d, Ne, F = desc.T, desc.d, desc.Ne, desc.F
+    dt = torch.bfloat16 if desc.dtype == OCC_BF16 else torch.float32
+    L = _host_i32(placement, "placement", (desc.Nd, Ne // desc.Nd))
+    nsh, Fsh = desc.n_shared, desc.F_shared
+    sh = [None, None, None]
+    if nsh > 0:
+        sh = [_dev(ws_gate, "ws_gate", dt, (nsh, Fsh, d)), _dev(ws_up, "ws_up", dt, (nsh, Fsh, d)),
+              _dev(ws_down, "ws_down", dt, (nsh, d, Fsh))]
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * (OCC_STAGE_COUNT + 1))(*stage_events)
+    _check(lib().occ_moe_forward_gated(
+        ctypes.byref(desc), _dev(x, "x", dt, (T, d)), _dev(w_router, "w_router", dt, (Ne, d)),
+        _hp(L), _dev(w_gate, "w_gate", dt, (Ne, F, d)), _dev(w_up, "w_up", dt, (Ne, F, d)),
+        _dev(w_down, "w_down", dt, (Ne, d, F)), *sh, _dev(y, "y", dt, (T, d)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
+        "occ_moe_forward_gated")
 
 
 def occ_forward_views(desc: LayerDesc, workspace) -> ForwardView:

@@ -133,12 +133,15 @@ typedef struct occ_brim {
 } occ_brim;
 
 /* Where occ_moe_forward leaves its intermediate tensors in the workspace.
+ *   logits    T x Ne fp32: the router logits, written only by
+ *             occ_moe_forward_gated.
  *   ids, w    T x k routing result (int32 / fp32).
  *   x_sfd     N_sfd x d, dtype: the dispatched replicas (ORI -> SFD).
  *   epd       T*k x F, dtype: modulated SwiGLU hidden states (SFD -> EPD).
  *   sfd_out   N_sfd x d, fp32: stage-one sums inside each group (EPD -> SFD).
  *   h_shared  T x n_shared*F_shared, dtype; y_shared T x d, fp32 (or NULL). */
 typedef struct occ_forward_view {
+    float *logits;
     int32_t *ids;
     float *w;
     occ_brim brim;
@@ -260,6 +263,27 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
                            const void *w_down, const void *ws_gate, const void *ws_up,
                            const void *ws_down, void *y, void *workspace, size_t ws_bytes,
                            void *const *stage_events, void *stream);
+
+/* Gate projection g(x) of the router (section 2.1: a single linear layer):
+ *   logits[t][e] = sum_i x[t][i] * w_router[e][i], accumulated in fp32
+ * (bf16: matrix-core products of the exact bf16 inputs, one accumulation
+ * chain per logit in fixed order).
+ *   x          T x d (dtype, device);  w_router Ne x d (dtype, device).
+ *   logits     (out) T x Ne fp32 (device). */
+occ_status occ_gate(const occ_layer_desc *desc, const void *x, const void *w_router,
+                    float *logits, void *stream);
+
+/* The layer with the gate projection in front of the router (the decode
+ * path: logits are not an input): occ_gate into the workspace (view
+ * `logits`), then occ_moe_forward on those logits.  The route stage's events
+ * time both.  Arguments as occ_moe_forward, with w_router (Ne x d, dtype)
+ * in place of logits; the SIMILARITY rule is not available here. */
+occ_status occ_moe_forward_gated(const occ_layer_desc *desc, const void *x, const void *w_router,
+                                 const int32_t *placement_host, const void *w_gate,
+                                 const void *w_up, const void *w_down, const void *ws_gate,
+                                 const void *ws_up, const void *ws_down, void *y,
+                                 void *workspace, size_t ws_bytes, void *const *stage_events,
+                                 void *stream);
 
 /* The layer from a routing computed elsewhere (for instance by
  * occ_route_similarity): occ_moe_forward without its router stage.

@@ -1,0 +1,121 @@
+"""GPU parity of the decode path: the gate projection g(x) (paper section
+2.1) against the fp64 oracle within fp32 accumulation's error bound, routing
+on the device's own logits bit for bit, the gated layer to the layer
+tolerance, and both GEMM tile sizes around the point where the library
+switches between them (64-row tiles when T*k < 128*Ne)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_amd import occ, synth, workloads as W
+
+from gpu_common import TOL, W_RTOL, bits, inputs, oracle_rows, row_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    occ.lib()
+
+
+def gpu_gate(wl, x, wr):
+    desc = occ.desc_of(wl, T=x.shape[0])
+    lg = torch.empty(x.shape[0], wl.Ne, dtype=torch.float32, device="cuda")
+    occ.occ_gate(desc, x.cuda(), wr.cuda(), lg)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy()
+
+
+def check_gate(wl, T):
+    x = synth.make_x(wl, T)
+    wr = synth.make_router_weights(wl)
+    got = gpu_gate(wl, x, wr)
+    ref = oracle.gate(np.arange(T), bits(x), bits(wr))
+    # fp32 accumulation of d exact products: |err| <= d u / (1 - d u) sum |x_i w_i|
+    u = 2.0 ** -24
+    mag = np.abs(x.double().numpy()) @ np.abs(wr.double().numpy()).T
+    bound = wl.d * u / (1 - wl.d * u) * mag
+    assert np.all(np.abs(got - ref) <= bound)
+    return x, wr, got
+
+
+@pytest.mark.parametrize("wl,T", [
+    (W.OLMOE_DECODE, 512),
+    (W.OLMOE_DECODE, 37),                                            # ragged token block
+    (W.scaled(W.QWEN, 100, name="qwen_gate_T100", gated=True), 100),  # Ne = 60
+    (W.scaled(W.OLMOE, 50, name="ne256_gate_T50", Ne=256, Nd=16, gated=True), 50),
+    (W.scaled(W.TINY_F32, 70, name="tiny_gate_T70", gated=True), 70),  # fp32 path
+], ids=["decode512", "ragged37", "ne60", "ne256", "fp32"])
+def test_gate_matches_oracle(wl, T):
+    check_gate(wl, T)
+
+
+def gated_forward(wl, dev, L):
+    desc = occ.desc_of(wl)
+    ws = occ.alloc_workspace(desc)
+    y = torch.empty(wl.T, wl.d, dtype=synth.torch_dtype(wl), device="cuda")
+    occ.occ_moe_forward_gated(desc, dev["x"], dev["w_router"], L, dev["w_gate"], dev["w_up"],
+                              dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    torch.cuda.synchronize()
+    v = occ.occ_forward_views(desc, ws)
+    lg = occ.ws_view(ws, v.logits, (wl.T, wl.Ne), torch.float32).cpu().numpy()
+    ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy()
+    return y, lg, ids, w
+
+
+@pytest.mark.parametrize("wl", [W.OLMOE_DECODE, W.scaled(W.DEEPSEEK, 261)],
+                         ids=["olmoe_decode", "deepseek_shared"])
+def test_gated_forward_matches_oracle(wl):
+    inp = inputs(wl)  # the DeepSeek case shares the plain forward tests' tensors
+    if inp["w_router"] is None:
+        inp = dict(inp, w_router=synth.make_router_weights(wl))
+    dev = to_dev(inp)
+    L = inp["placement"]
+    y, lg, ids, w = gated_forward(wl, dev, L)
+    # the logits in the workspace are occ_gate's
+    assert np.array_equal(lg, gpu_gate(wl, inp["x"], inp["w_router"]))
+    # routing decided on the device's fp32 logits, by the oracle, bit for bit
+    ids_o, w_o = oracle.route(lg, wl.k, L)
+    assert np.array_equal(ids, ids_o)
+    np.testing.assert_allclose(w, w_o, rtol=W_RTOL)
+    ref = oracle_rows(wl, inp, np.arange(wl.T), ids, w.astype(np.float64))
+    assert row_err(y.float().cpu().numpy(), ref).max() <= TOL[wl.dtype]
+    # the same layer through occ_moe_forward on those logits: identical output
+    desc = occ.desc_of(wl)
+    ws = occ.alloc_workspace(desc)
+    y2 = torch.empty_like(y)
+    occ.occ_moe_forward(desc, dev["x"], torch.from_numpy(lg).cuda(), L, dev["w_gate"],
+                        dev["w_up"], dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"],
+                        y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("T", [1023, 1024], ids=["m64_tiles", "m256_tiles"])
+def test_forward_on_both_sides_of_the_tile_switch(T):
+    """OLMoE shape: T*k < 128*Ne below 1024 tokens (64-row tiles), not at 1024
+    (256-row tiles); both against the oracle on sampled rows."""
+    wl = W.scaled(W.OLMOE, T)
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    desc = occ.desc_of(wl)
+    ws = occ.alloc_workspace(desc)
+    y = torch.empty(wl.T, wl.d, dtype=torch.bfloat16, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], inp["placement"], dev["w_gate"],
+                        dev["w_up"], dev["w_down"], None, None, None, y, ws)
+    torch.cuda.synchronize()
+    v = occ.occ_forward_views(desc, ws)
+    ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
+    tile_off = occ.ws_view(ws, v.brim.tile_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
+    epd_off = occ.ws_view(ws, v.brim.epd_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
+    bm = 64 if T * wl.k < 128 * wl.Ne else 256
+    assert np.array_equal(np.diff(tile_off), (np.diff(epd_off) + bm - 1) // bm)
+    rows = synth.sample_rows(wl.T, 128, seed=T)
+    ref = oracle_rows(wl, inp, rows, ids, w)
+    assert row_err(y.float().cpu().numpy()[rows], ref).max() <= TOL[wl.dtype]
