@@ -393,7 +393,11 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     OCC_TRY(mark(5));
     // Algorithm 8: EPD -> SFD, summed inside each group in fp32.  The first
     // contributor to every SFD row stores (so no zero-fill is needed), then
-    // the other rows of the group add with atomics.
+    // the other rows of the group add with atomics.  Small batches (the same
+    // rule as the 64-row tiles) are bound by reading the weights, which the
+    // two launches would read twice: there the SFD rows are zeroed and one
+    // launch adds every row.
+    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
     DownArgs dn{};
     dn.A = epd;
     dn.W = w_down;
@@ -408,13 +412,22 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     dn.Ne = D.Ne;
     dn.k_split = D.F;
     dn.tab = tab;
-    dn.phase = 1;
-    dn.tile_off = bb.tile_off_first;
-    OCC_HIP(ops.down(dn, routed_tiles, s));
-    OCC_TRY(mark(6));
-    dn.phase = 2;
-    dn.tile_off = bb.tile_off_rest;
-    OCC_HIP(ops.down(dn, routed_tiles, s));
+    if (one_launch) {
+        const size_t nsfd_max = static_cast<size_t>(D.T) * std::min(D.k, D.Nd);
+        OCC_HIP(launch_fill_i32(reinterpret_cast<int32_t *>(sfd_out), nsfd_max * D.d, 0, s));
+        dn.phase = 0;
+        dn.tile_off = bb.tile_off;
+        OCC_HIP(ops.down(dn, routed_tiles, s));
+        OCC_TRY(mark(6));
+    } else {
+        dn.phase = 1;
+        dn.tile_off = bb.tile_off_first;
+        OCC_HIP(ops.down(dn, routed_tiles, s));
+        OCC_TRY(mark(6));
+        dn.phase = 2;
+        dn.tile_off = bb.tile_off_rest;
+        OCC_HIP(ops.down(dn, routed_tiles, s));
+    }
     OCC_TRY(mark(7));
     // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once
     OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));

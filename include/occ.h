@@ -159,8 +159,10 @@ enum {
     OCC_STAGE_DISPATCH = 2,
     OCC_STAGE_SHARED = 3,
     OCC_STAGE_GEMM_UP = 4,
-    OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores */
-    OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds */
+    OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores (one-launch
+                                      merge: the zero-fill and every row) */
+    OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds (one-launch
+                                      merge: empty) */
     OCC_STAGE_COMBINE = 7,
     OCC_STAGE_COUNT = 8
 };
@@ -245,7 +247,8 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const 
  *   SwiGLU up-projection SFD->EPD with the routing weight applied to the
  *   hidden state (Alg. 6-7) -> down-projection EPD->SFD summed inside each
  *   group in fp32 (Alg. 8: the first contributor to each SFD row stores, the
- *   others add) -> combine SFD->ORI summed across groups (Alg. 9).
+ *   others add; when T*k < 128*Ne the SFD rows are zeroed and every row
+ *   adds, in one launch) -> combine SFD->ORI summed across groups (Alg. 9).
  * Without pruning the result equals the plain top-k MoE output (section 3.2).
  *   x          T x d (dtype);  logits T x Ne fp32;  placement_host as above.
  *   w_gate     Ne x F x d;  w_up Ne x F x d;  w_down Ne x d x F (dtype).

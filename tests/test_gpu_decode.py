@@ -93,7 +93,8 @@ def test_gated_forward_matches_oracle(wl):
                         dev["w_up"], dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"],
                         y2, ws)
     torch.cuda.synchronize()
-    assert torch.equal(y, y2)
+    # equal up to the order of the fp32 atomic adds inside groups
+    assert row_err(y2.float().cpu().numpy(), y.float().cpu().numpy()).max() <= 1e-2
 
 
 @pytest.mark.parametrize("T", [1023, 1024], ids=["m64_tiles", "m256_tiles"])

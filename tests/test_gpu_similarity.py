@@ -177,7 +177,8 @@ def test_forward_routed_equals_forward_on_the_same_routing():
     ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).clone()
     w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).clone()
     y2, _, _ = routed_forward(wl, dev, ids, w, L)
-    assert torch.equal(y, y2)
+    # equal up to the order of the fp32 atomic adds inside groups
+    assert row_err(y2.float().cpu().numpy(), y.float().cpu().numpy()).max() <= 1e-2
 
 
 def test_similarity_forward_full_size_sampled_rows():
