@@ -215,6 +215,47 @@ def moe_rows(rows, x, ids, w, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws
     return y
 
 
+def moe_backward(x, ids, w, dy, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
+                 logits=None) -> dict:
+    """Gradients of Eq. 1 (routing ids fixed) for upstream gradient dy (T, d):
+    dx, dW_gate, dW_up, dW_down (and the shared experts'), dw (T, k) and,
+    when logits are given, dlogits through the full softmax.  fp64."""
+    xa, dt = _float_arg(x)
+    T, d = xa.shape
+    ids = _i32(ids)
+    k = ids.shape[1]
+    wv = np.ascontiguousarray(w, dtype=np.float64)
+    dyv = np.ascontiguousarray(dy, dtype=np.float64)
+    g, _ = _float_arg(w_gate)
+    u, _ = _float_arg(w_up)
+    dn, _ = _float_arg(w_down)
+    Ne, F = g.shape[0], g.shape[1]
+    n_sh, F_sh = 0, 0
+    sg = su = sd = None
+    if ws_gate is not None:
+        sg, _ = _float_arg(ws_gate)
+        su, _ = _float_arg(ws_up)
+        sd, _ = _float_arg(ws_down)
+        n_sh, F_sh = sg.shape[0], sg.shape[1]
+    out = dict(dx=np.empty((T, d)), dW_gate=np.empty((Ne, F, d)), dW_up=np.empty((Ne, F, d)),
+               dW_down=np.empty((Ne, d, F)), dw=np.empty((T, k)))
+    if n_sh:
+        out.update(dWs_gate=np.empty((n_sh, F_sh, d)), dWs_up=np.empty((n_sh, F_sh, d)),
+                   dWs_down=np.empty((n_sh, d, F_sh)))
+    lg = None if logits is None else np.ascontiguousarray(logits, dtype=np.float32)
+    if lg is not None:
+        out["dlogits"] = np.empty((T, Ne))
+    nul = ctypes.c_void_p(0)
+    opt = lambda a: _p(a) if a is not None else nul
+    rc = _load().orc_moe_backward(
+        T, d, Ne, k, F, n_sh, F_sh, dt, _p(xa), _p(ids), _p(wv), opt(lg), _p(g), _p(u), _p(dn),
+        opt(sg), opt(su), opt(sd), _p(dyv), _p(out["dx"]), _p(out["dW_gate"]), _p(out["dW_up"]),
+        _p(out["dW_down"]), opt(out.get("dWs_gate")), opt(out.get("dWs_up")),
+        opt(out.get("dWs_down")), _p(out["dw"]), opt(out.get("dlogits")))
+    _check(rc, "moe_backward")
+    return out
+
+
 def threads(nthreads: int = 0) -> int:
     """How many threads moe_rows runs with for this request."""
     return int(_load().orc_threads(nthreads))

@@ -490,6 +490,173 @@ int orc_moe_rows(int nrows, const int64_t *rows, int d, int k, int F, int n_sh, 
     return ORC_OK;
 }
 
+/*
+ * Backward pass of the layer (the gradients the paper's training runs need,
+ * sections 1 and 4.3; the pages give no formulas, these are the derivatives
+ * of Eq. 1 with the routing ids held fixed).  For token t and its j-th
+ * expert e with weight w = R(x)_e and SwiGLU pre-activations g = W_g x,
+ * u = W_u x, activation a = silu(g) u and upstream gradient dy:
+ *   dh = W_d^T dy                   (gradient of the modulated state w a)
+ *   dw = <dh, a>                    (gradient of the routing weight)
+ *   da = w dh,  dg = da u silu'(g),  du = da silu(g),
+ *   silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g)
+ *   dW_d[e] += dy (w a)^T,  dW_g[e] += dg x^T,  dW_u[e] += du x^T,
+ *   dx += W_g^T dg + W_u^T du.
+ * Shared experts are the same with w = 1 and no dw.  The logits' gradient
+ * goes through Eq. 2's full softmax p (the k weights are p at the chosen
+ * experts, not renormalised):
+ *   dlogits[i] = p_i ([i chosen] dw_i - sum_j dw_j p_(e_j)).
+ * All in fp64; dlogits is skipped when logits is NULL.  The weight
+ * gradients are accumulated expert by expert, the input gradient token by
+ * token over j in order, then the shared experts.
+ */
+int orc_moe_backward(int T, int d, int Ne, int k, int F, int n_sh, int F_sh, int dtype,
+                     const void *x, const int32_t *ids, const double *w, const float *logits,
+                     const void *Wg, const void *Wu, const void *Wd, const void *Wsg,
+                     const void *Wsu, const void *Wsd, const double *dy, double *dx,
+                     double *dWg, double *dWu, double *dWd, double *dWsg, double *dWsu,
+                     double *dWsd, double *dw, double *dlogits)
+{
+    if (T < 1 || d < 1 || Ne < 1 || k < 1 || F < 1 || n_sh < 0)
+        return ORC_BAD;
+    for (size_t i = 0; i < (size_t)T * k; i++)
+        if (ids[i] < 0 || ids[i] >= Ne)
+            return ORC_BAD;
+    /* per (t, j) input-gradient contributions, summed per token afterwards */
+    double *dxp = calloc((size_t)T * k * d, sizeof(double));
+    memset(dWg, 0, sizeof(double) * (size_t)Ne * F * d);
+    memset(dWu, 0, sizeof(double) * (size_t)Ne * F * d);
+    memset(dWd, 0, sizeof(double) * (size_t)Ne * d * F);
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        double *xt = malloc(sizeof(double) * d), *g = malloc(sizeof(double) * F);
+        double *u = malloc(sizeof(double) * F), *dg = malloc(sizeof(double) * F);
+        double *du = malloc(sizeof(double) * F);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int e = 0; e < Ne; e++) {
+            size_t wb = (size_t)e * F * d, db = (size_t)e * d * F;
+            for (int t = 0; t < T; t++)
+                for (int j = 0; j < k; j++) {
+                    if (ids[(size_t)t * k + j] != e)
+                        continue;
+                    double wt = w[(size_t)t * k + j], dwt = 0.0;
+                    const double *dyt = dy + (size_t)t * d;
+                    for (int c = 0; c < d; c++)
+                        xt[c] = elem(x, dtype, (size_t)t * d + c);
+                    for (int f = 0; f < F; f++) {
+                        double gf = 0.0, uf = 0.0, dh = 0.0;
+                        for (int c = 0; c < d; c++) {
+                            gf += elem(Wg, dtype, wb + (size_t)f * d + c) * xt[c];
+                            uf += elem(Wu, dtype, wb + (size_t)f * d + c) * xt[c];
+                            dh += elem(Wd, dtype, db + (size_t)c * F + f) * dyt[c];
+                        }
+                        double sg = 1.0 / (1.0 + exp(-gf)), a = gf * sg * uf;
+                        dwt += dh * a;
+                        double da = wt * dh;
+                        dg[f] = da * uf * sg * (1.0 + gf * (1.0 - sg));
+                        du[f] = da * gf * sg;
+                        for (int c = 0; c < d; c++)
+                            dWd[db + (size_t)c * F + f] += dyt[c] * (wt * a);
+                    }
+                    for (int f = 0; f < F; f++)
+                        for (int c = 0; c < d; c++) {
+                            dWg[wb + (size_t)f * d + c] += dg[f] * xt[c];
+                            dWu[wb + (size_t)f * d + c] += du[f] * xt[c];
+                        }
+                    double *dxt = dxp + ((size_t)t * k + j) * d;
+                    for (int c = 0; c < d; c++) {
+                        double s = 0.0;
+                        for (int f = 0; f < F; f++)
+                            s += elem(Wg, dtype, wb + (size_t)f * d + c) * dg[f] +
+                                 elem(Wu, dtype, wb + (size_t)f * d + c) * du[f];
+                        dxt[c] = s;
+                    }
+                    dw[(size_t)t * k + j] = dwt;
+                }
+        }
+        free(xt); free(g); free(u); free(dg); free(du);
+    }
+    for (int t = 0; t < T; t++)
+        for (int c = 0; c < d; c++) {
+            double s = 0.0;
+            for (int j = 0; j < k; j++)
+                s += dxp[((size_t)t * k + j) * d + c];
+            dx[(size_t)t * d + c] = s;
+        }
+    free(dxp);
+
+    if (n_sh > 0) {
+        memset(dWsg, 0, sizeof(double) * (size_t)n_sh * F_sh * d);
+        memset(dWsu, 0, sizeof(double) * (size_t)n_sh * F_sh * d);
+        memset(dWsd, 0, sizeof(double) * (size_t)n_sh * d * F_sh);
+        double *xt = malloc(sizeof(double) * d), *dg = malloc(sizeof(double) * F_sh);
+        double *du = malloc(sizeof(double) * F_sh);
+        for (int sx = 0; sx < n_sh; sx++) {
+            size_t wb = (size_t)sx * F_sh * d, db = (size_t)sx * d * F_sh;
+            for (int t = 0; t < T; t++) {
+                const double *dyt = dy + (size_t)t * d;
+                for (int c = 0; c < d; c++)
+                    xt[c] = elem(x, dtype, (size_t)t * d + c);
+                for (int f = 0; f < F_sh; f++) {
+                    double gf = 0.0, uf = 0.0, dh = 0.0;
+                    for (int c = 0; c < d; c++) {
+                        gf += elem(Wsg, dtype, wb + (size_t)f * d + c) * xt[c];
+                        uf += elem(Wsu, dtype, wb + (size_t)f * d + c) * xt[c];
+                        dh += elem(Wsd, dtype, db + (size_t)c * F_sh + f) * dyt[c];
+                    }
+                    double sg = 1.0 / (1.0 + exp(-gf)), a = gf * sg * uf;
+                    dg[f] = dh * uf * sg * (1.0 + gf * (1.0 - sg));
+                    du[f] = dh * gf * sg;
+                    for (int c = 0; c < d; c++)
+                        dWsd[db + (size_t)c * F_sh + f] += dyt[c] * a;
+                }
+                for (int f = 0; f < F_sh; f++)
+                    for (int c = 0; c < d; c++) {
+                        dWsg[wb + (size_t)f * d + c] += dg[f] * xt[c];
+                        dWsu[wb + (size_t)f * d + c] += du[f] * xt[c];
+                    }
+                for (int c = 0; c < d; c++) {
+                    double s = 0.0;
+                    for (int f = 0; f < F_sh; f++)
+                        s += elem(Wsg, dtype, wb + (size_t)f * d + c) * dg[f] +
+                             elem(Wsu, dtype, wb + (size_t)f * d + c) * du[f];
+                    dx[(size_t)t * d + c] += s;
+                }
+            }
+        }
+        free(xt); free(dg); free(du);
+    }
+
+    if (logits) {
+        double *p = malloc(sizeof(double) * Ne);
+        for (int t = 0; t < T; t++) {
+            const float *l = logits + (size_t)t * Ne;
+            double m = l[0], s = 0.0, acc = 0.0;
+            for (int e = 1; e < Ne; e++)
+                if (l[e] > m)
+                    m = l[e];
+            for (int e = 0; e < Ne; e++)
+                s += exp((double)l[e] - m);
+            for (int e = 0; e < Ne; e++)
+                p[e] = exp((double)l[e] - m) / s;
+            for (int j = 0; j < k; j++)
+                acc += dw[(size_t)t * k + j] * p[ids[(size_t)t * k + j]];
+            for (int e = 0; e < Ne; e++)
+                dlogits[(size_t)t * Ne + e] = -p[e] * acc;
+            for (int j = 0; j < k; j++) {
+                int e = ids[(size_t)t * k + j];
+                dlogits[(size_t)t * Ne + e] += p[e] * dw[(size_t)t * k + j];
+            }
+        }
+        free(p);
+    }
+    return ORC_OK;
+}
+
 /* Number of threads orc_moe_rows runs with when asked for nthreads. */
 int orc_threads(int nthreads)
 {

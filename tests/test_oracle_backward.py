@@ -1,0 +1,152 @@
+"""Pins of the oracle's backward pass (derivatives of Eq. 1 with the routing
+ids fixed, through Eq. 2's softmax for the logits) against things other than
+itself: central finite differences of the oracle's forward, torch autograd
+on an independent float64 forward, linearity and the zero gradient."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_amd import synth, workloads as W
+
+
+def small(dtype=W.DTYPE_F32, n_shared=0, T=6, d=16, Ne=6, k=2, F=8):
+    return W.Workload(f"bwd_{dtype}_{n_shared}", 9, T=T, d=d, Ne=Ne, k=k, Nd=2, F=F,
+                      n_shared=n_shared, F_shared=8 if n_shared else 0, dtype=dtype, n_c=2,
+                      bonus=1.0)
+
+
+def setup(wl, scale=1.0):
+    inp = synth.make_all(wl)
+    # weights of order 0.3 so that every term of the gradient matters
+    for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        if inp[key] is not None:
+            inp[key] = (inp[key].float() * (15.0 * scale)).to(inp[key].dtype)
+    logits = inp["logits"].numpy()
+    ids, _ = oracle.route(logits, wl.k, inp["placement"])
+    dy = torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(3), dtype=torch.float64)
+    return inp, logits, ids, dy.numpy()
+
+
+def view(t):
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
+
+
+def probs(logits, ids):
+    p = torch.softmax(torch.from_numpy(logits).double(), 1).numpy()
+    return np.take_along_axis(p, ids.astype(np.int64), 1)
+
+
+def backward(inp, logits, ids, dy):
+    w = probs(logits, ids)
+    return oracle.moe_backward(view(inp["x"]), ids, w, dy, view(inp["w_gate"]), view(inp["w_up"]),
+                               view(inp["w_down"]), view(inp["ws_gate"]), view(inp["ws_up"]),
+                               view(inp["ws_down"]), logits=logits)
+
+
+def loss(inp, logits, ids, dy, over=None):
+    """<dy, y> with y from the oracle's forward (Eq. 1), optionally with one
+    tensor replaced."""
+    t = dict(inp)
+    if over:
+        t.update(over)
+    w = probs(t.get("logits_np", logits), ids)
+    y = oracle.moe_rows(np.arange(dy.shape[0]), view(t["x"]), ids, w, view(t["w_gate"]),
+                        view(t["w_up"]), view(t["w_down"]), view(t["ws_gate"]),
+                        view(t["ws_up"]), view(t["ws_down"]))
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_backward_matches_central_differences(n_shared):
+    wl = small(n_shared=n_shared)
+    inp, logits, ids, dy = setup(wl)
+    g = backward(inp, logits, ids, dy)
+    rng = np.random.default_rng(1)
+    checks = [("x", "dx"), ("w_gate", "dW_gate"), ("w_up", "dW_up"), ("w_down", "dW_down")]
+    if n_shared:
+        checks += [("ws_gate", "dWs_gate"), ("ws_up", "dWs_up"), ("ws_down", "dWs_down")]
+    eps = 2.0 ** -12
+    for key, gkey in checks:
+        base = inp[key]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(n)) for n in base.shape)
+            vals = []
+            for sgn in (1, -1):
+                pert = base.clone()
+                pert[idx] = pert[idx] + sgn * eps      # fp32: the step actually taken
+                step = float(pert[idx]) - float(base[idx])
+                vals.append((loss(inp, logits, ids, dy, {key: pert}), step))
+            fd = (vals[0][0] - vals[1][0]) / (vals[0][1] - vals[1][1])
+            an = g[gkey][idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, idx, fd, an)
+    # logits: through the softmax weights, ids held fixed
+    for _ in range(8):
+        t, e = int(rng.integers(wl.T)), int(rng.integers(wl.Ne))
+        vals = []
+        for sgn in (1, -1):
+            lp = logits.copy()
+            lp[t, e] += sgn * np.float32(eps)
+            vals.append(loss(inp, logits, ids, dy, {"logits_np": lp}))
+        fd = (vals[0] - vals[1]) / (2 * eps)
+        assert abs(fd - g["dlogits"][t, e]) <= 1e-6 * max(1.0, abs(fd)), (t, e)
+    # routing weights: the loss is linear in them, so the check is exact up to rounding
+    w = probs(logits, ids)
+    for j in range(wl.k):
+        onehot = np.zeros_like(w)
+        onehot[:, j] = 1.0
+        y = oracle.moe_rows(np.arange(wl.T), view(inp["x"]), ids, onehot, view(inp["w_gate"]),
+                            view(inp["w_up"]), view(inp["w_down"]))
+        np.testing.assert_allclose(g["dw"][:, j], (y * dy).sum(1), rtol=1e-10, atol=1e-12)
+
+
+def torch_reference(inp, logits, ids, dy):
+    """Eq. 1 written with torch float64 ops; gradients by autograd."""
+    f = lambda t: None if t is None else t.double().clone().requires_grad_(True)
+    x, wg, wu, wd = f(inp["x"]), f(inp["w_gate"]), f(inp["w_up"]), f(inp["w_down"])
+    sg, su, sd = f(inp["ws_gate"]), f(inp["ws_up"]), f(inp["ws_down"])
+    lg = torch.from_numpy(logits).double().requires_grad_(True)
+    idx = torch.from_numpy(ids.astype(np.int64))
+    w = torch.softmax(lg, 1).gather(1, idx)
+    y = torch.zeros_like(x)
+    for j in range(idx.shape[1]):
+        e = idx[:, j]
+        g = torch.einsum("tfd,td->tf", wg[e], x)
+        u = torch.einsum("tfd,td->tf", wu[e], x)
+        h = torch.nn.functional.silu(g) * u
+        y = y + w[:, j:j + 1] * torch.einsum("tdf,tf->td", wd[e], h)
+    if sg is not None:
+        for s in range(sg.shape[0]):
+            h = torch.nn.functional.silu(x @ sg[s].T) * (x @ su[s].T)
+            y = y + h @ sd[s].T
+    (y * torch.from_numpy(dy)).sum().backward()
+    out = dict(dx=x.grad, dW_gate=wg.grad, dW_up=wu.grad, dW_down=wd.grad, dlogits=lg.grad)
+    if sg is not None:
+        out.update(dWs_gate=sg.grad, dWs_up=su.grad, dWs_down=sd.grad)
+    return {k: v.numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("wl", [small(W.DTYPE_BF16, T=9, d=32, Ne=8, k=3, F=16),
+                                small(W.DTYPE_BF16, n_shared=2, T=7, d=32, Ne=8, k=2, F=16)],
+                         ids=["routed", "shared"])
+def test_backward_matches_torch_autograd(wl):
+    inp, logits, ids, dy = setup(wl, scale=0.5)
+    g = backward(inp, logits, ids, dy)
+    ref = torch_reference(inp, logits, ids, dy)
+    for key, val in ref.items():
+        np.testing.assert_allclose(g[key], val, rtol=1e-10, atol=1e-12, err_msg=key)
+
+
+def test_backward_is_linear_in_dy_and_zero_at_zero():
+    wl = small(n_shared=1)
+    inp, logits, ids, dy = setup(wl)
+    g1 = backward(inp, logits, ids, dy)
+    g2 = backward(inp, logits, ids, -2.0 * dy)
+    g0 = backward(inp, logits, ids, 0.0 * dy)
+    for key in g1:
+        np.testing.assert_allclose(g2[key], -2.0 * g1[key], rtol=1e-12, atol=1e-14)
+        assert np.all(g0[key] == 0.0), key
