@@ -39,8 +39,16 @@ int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
 struct Layout {
     size_t logits, ids, w, brim0, sfd_off, epd_off, tile_off, tile_off_first, tile_off_rest, first_cnt,
         chunk_cnt, chunk_base, epd_src, epd_w, tok_epd, down_rows, brim1, brim_end, x_sfd, epd,
-        sfd_out, h_sh, y_sh, total;
+        sfd_out, h_sh, y_sh;
+    // training only (flags & OCC_FLAG_TRAIN): saved pre-activations and the
+    // backward pass's buffers
+    size_t gu, gu_sh, dy_sfd, dgu, dx_sfd, dw_part, zero_row, bt_all, bt_first, bt_rest, dgu_sh,
+        dx_sh, dense_seg, dense_tile;
+    int dw_stride;
+    size_t total;
 };
+
+constexpr int kBwdTile = 256;  // rows and columns of a backward GEMM tile
 
 Layout layout(const occ_layer_desc &D) {
     const size_t T = D.T, k = D.k, Nd = D.Nd, Ne = D.Ne, d = D.d, F = D.F, es = elem_bytes(D);
@@ -74,9 +82,29 @@ Layout layout(const occ_layer_desc &D) {
     L.x_sfd = take(nsfd_max * d * es);
     L.epd = take(nepd * F * es);
     L.sfd_out = take(nsfd_max * d * 4);
+    const size_t Nsh = static_cast<size_t>(D.n_shared) * D.F_shared;
     if (D.n_shared > 0) {
-        L.h_sh = take(T * static_cast<size_t>(D.n_shared) * D.F_shared * es);
+        L.h_sh = take(T * Nsh * es);
         L.y_sh = take(T * d * 4);
+    }
+    if (D.flags & OCC_FLAG_TRAIN) {
+        L.dw_stride = 2 * static_cast<int>((F + kBwdTile - 1) / kBwdTile);
+        L.gu = take(nepd * 2 * F * es);
+        L.dy_sfd = take(nsfd_max * d * es);
+        L.dgu = take(nepd * 2 * F * es);
+        L.dx_sfd = take(nsfd_max * d * 4);
+        L.dw_part = take(nepd * L.dw_stride * 4);
+        L.zero_row = take(std::max<size_t>({d, 2 * F, 2 * Nsh, kBwdTile}) * es);
+        L.bt_all = take((Ne + 1) * 4);
+        L.bt_first = take((Ne + 1) * 4);
+        L.bt_rest = take((Ne + 1) * 4);
+        L.dense_seg = take(2 * 4);
+        L.dense_tile = take(2 * 4);
+        if (D.n_shared > 0) {
+            L.gu_sh = take(T * 2 * Nsh * es);
+            L.dgu_sh = take(T * 2 * Nsh * es);
+            L.dx_sh = take(T * d * 4);
+        }
     }
     L.total = o;
     return L;
@@ -95,7 +123,13 @@ occ_status check_desc(const occ_layer_desc *D) {
         (D->prune_groups < 1 ||
          static_cast<int64_t>(D->prune_groups) * (D->Ne / D->Nd) < D->k))
         return OCC_ERR_INVALID_ARG;
-    if (D->flags != 0) return OCC_ERR_INVALID_ARG;
+    if (D->flags & ~OCC_FLAG_TRAIN) return OCC_ERR_INVALID_ARG;
+    // training keeps bf16 pre-activations for the bf16 backward GEMMs, whose
+    // 256-wide tiles need d, F (and F_shared) of at least 256
+    if ((D->flags & OCC_FLAG_TRAIN) &&
+        (D->dtype != OCC_BF16 || D->d < kBwdTile || D->F < kBwdTile ||
+         (D->n_shared > 0 && D->F_shared < kBwdTile)))
+        return OCC_ERR_UNSUPPORTED;
     if (D->Ne > kMaxNe || D->Nd > kMaxNd || D->k > kMaxK) return OCC_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(D->T) * D->k >= (1ll << 31) ||
         static_cast<int64_t>(D->T) * D->Nd >= (1ll << 31))
@@ -355,6 +389,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         su.Wg = ws_gate;
         su.Wu = ws_up;
         su.out = at<void>(workspace, L.h_sh);
+        su.gu_out = (D.flags & OCC_FLAG_TRAIN) ? at<void>(workspace, L.gu_sh) : nullptr;
         su.M = D.T;
         su.K = D.d;
         su.N = D.n_shared * D.F_shared;
@@ -384,6 +419,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     up.tile_off = bb.tile_off;
     up.row_w = bb.epd_w;
     up.out = epd;
+    up.gu_out = (D.flags & OCC_FLAG_TRAIN) ? at<void>(workspace, L.gu) : nullptr;
     up.M = D.T * D.k;
     up.K = D.d;
     up.N = D.F;
@@ -474,6 +510,256 @@ occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, con
     if (!ids || !w) return OCC_ERR_INVALID_ARG;
     return forward(desc, x, nullptr, nullptr, ids, w, placement_host, w_gate, w_up, w_down, ws_gate,
                    ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+}
+
+occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const void *x,
+                            const float *logits, const int32_t *placement_host,
+                            const void *w_gate, const void *w_up, const void *w_down,
+                            const void *ws_gate, const void *ws_up, const void *ws_down,
+                            void *dx, float *dw_gate, float *dw_up, float *dw_down,
+                            float *dws_gate, float *dws_up, float *dws_down, float *dw,
+                            float *dlogits, void *workspace, size_t ws_bytes,
+                            void *const *stage_events, void *stream) {
+    OCC_TRY(check_desc(desc));
+    const occ_layer_desc &D = *desc;
+    if (!(D.flags & OCC_FLAG_TRAIN)) return OCC_ERR_INVALID_ARG;
+    if (!dy || !x || !w_gate || !w_up || !w_down || !dx || !dw_gate || !dw_up || !dw_down)
+        return OCC_ERR_INVALID_ARG;
+    if (D.n_shared > 0 && (!ws_gate || !ws_up || !ws_down || !dws_gate || !dws_up || !dws_down))
+        return OCC_ERR_INVALID_ARG;
+    if (dlogits && !logits) return OCC_ERR_INVALID_ARG;
+    if (stage_events)
+        for (int i = 0; i <= OCC_BSTAGE_COUNT; i++)
+            if (!stage_events[i]) return OCC_ERR_INVALID_ARG;
+    PlaceTab tab;
+    OCC_TRY(make_tab(D, placement_host, &tab));
+    const Layout L = layout(D);
+    OCC_TRY(check_ws(D, workspace, ws_bytes, L.total));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> occ_status {
+        if (!stage_events) return OCC_OK;
+        return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s));
+    };
+    const size_t es = elem_bytes(D), T = D.T, d = D.d, F = D.F;
+    const size_t Nsh = static_cast<size_t>(D.n_shared) * D.F_shared;
+    const BrimBufs bb = brim_bufs(workspace, L);
+    const void *x_sfd = at<void>(workspace, L.x_sfd);
+    const void *h = at<void>(workspace, L.epd);
+    void *dy_sfd = at<void>(workspace, L.dy_sfd);
+    void *dgu = at<void>(workspace, L.dgu);
+    float *dx_sfd = at<float>(workspace, L.dx_sfd);
+    float *dw_part = at<float>(workspace, L.dw_part);
+    void *zero_row = at<void>(workspace, L.zero_row);
+    int32_t *bt_all = at<int32_t>(workspace, L.bt_all);
+    int32_t *bt_first = at<int32_t>(workspace, L.bt_first);
+    int32_t *bt_rest = at<int32_t>(workspace, L.bt_rest);
+    float *dx_sh = D.n_shared > 0 ? at<float>(workspace, L.dx_sh) : nullptr;
+    const size_t routed_tiles = (T * D.k + kBwdTile - 1) / kBwdTile + D.Ne;
+    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
+
+    OCC_TRY(mark(0));
+    // schedules for 256-row tiles, a zero row for the tails of K-major operands
+    const size_t zero_elems = std::max<size_t>({d, 2 * F, 2 * Nsh, kBwdTile});
+    OCC_HIP(launch_fill_i32(static_cast<int32_t *>(zero_row), zero_elems * es / 4, 0, s));
+    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdTile, bt_all, bt_first, bt_rest,
+                              s));
+    // dy ORI -> SFD: the combine's transpose copies dy into each replica
+    OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s));
+    OCC_TRY(mark(1));
+    // dh = dy W_d for every EPD row (its SFD row's gradient, BRIM_1), then
+    // the SwiGLU and modulation backward
+    BwdDgradArgs g1{};
+    g1.A = dy_sfd;
+    g1.a_rows = bb.epd_src;
+    g1.lda = D.d;
+    g1.B1 = w_down;
+    g1.seg_off = bb.epd_off;
+    g1.tile_off = bt_all;
+    g1.first_cnt = bb.first_cnt;
+    g1.gu = at<void>(workspace, L.gu);
+    g1.gu_ld = 2 * D.F;
+    g1.gu_uoff = D.F;
+    g1.row_w = bb.epd_w;
+    g1.out = dgu;
+    g1.out_ld = 2 * D.F;
+    g1.out_uoff = D.F;
+    g1.dw_part = dw_part;
+    g1.dw_stride = L.dw_stride;
+    g1.N = D.F;
+    g1.K = D.d;
+    g1.ksplit = D.d;
+    g1.Ne = D.Ne;
+    g1.epilogue = BWD_EPI_SWIGLU;
+    g1.tab = tab;
+    OCC_HIP(launch_bwd_dgrad(g1, routed_tiles, s));
+    OCC_TRY(mark(2));
+    // dx_epd = dg W_g + du W_u, merged into SFD rows inside each group (fp32)
+    BwdDgradArgs g2{};
+    g2.A = dgu;
+    g2.a_rows = bb.down_rows;
+    g2.lda = 2 * D.F;
+    g2.B1 = w_gate;
+    g2.B2 = w_up;
+    g2.seg_off = bb.epd_off;
+    g2.first_cnt = bb.first_cnt;
+    g2.dst_rows = bb.epd_src;
+    g2.merge_out = dx_sfd;
+    g2.N = D.d;
+    g2.K = 2 * D.F;
+    g2.ksplit = D.F;
+    g2.Ne = D.Ne;
+    g2.epilogue = BWD_EPI_MERGE;
+    g2.tab = tab;
+    if (one_launch) {
+        const size_t nsfd_max = T * std::min(D.k, D.Nd);
+        OCC_HIP(launch_fill_i32(reinterpret_cast<int32_t *>(dx_sfd), nsfd_max * d, 0, s));
+        g2.phase = 0;
+        g2.tile_off = bt_all;
+        g2.merge_store = 0;
+        OCC_HIP(launch_bwd_dgrad(g2, routed_tiles, s));
+    } else {
+        g2.phase = 1;
+        g2.tile_off = bt_first;
+        g2.merge_store = 1;
+        OCC_HIP(launch_bwd_dgrad(g2, routed_tiles, s));
+        g2.phase = 2;
+        g2.tile_off = bt_rest;
+        g2.merge_store = 0;
+        OCC_HIP(launch_bwd_dgrad(g2, routed_tiles, s));
+    }
+    OCC_TRY(mark(3));
+    // shared experts: dense over the T tokens, one expert at a time for the
+    // input gradients, all at once for the weight gradients
+    if (D.n_shared > 0) {
+        int32_t *dseg = at<int32_t>(workspace, L.dense_seg);
+        int32_t *dtile = at<int32_t>(workspace, L.dense_tile);
+        OCC_HIP(launch_dense_sched(D.T, kBwdTile, dseg, dtile, s));
+        const size_t dense_tiles = (T + kBwdTile - 1) / kBwdTile;
+        PlaceTab one{};
+        one.Ne = 1;
+        one.Nd = 1;
+        one.n = 1;
+        void *dgu_sh = at<void>(workspace, L.dgu_sh);
+        for (int sx = 0; sx < D.n_shared; sx++) {
+            const size_t Fs = D.F_shared;
+            BwdDgradArgs s1{};
+            s1.A = dy;
+            s1.lda = D.d;
+            s1.B1 = static_cast<const char *>(ws_down) + sx * d * Fs * es;
+            s1.seg_off = dseg;
+            s1.tile_off = dtile;
+            s1.gu = at<void>(workspace, L.gu_sh);
+            s1.gu_ld = static_cast<int>(2 * Nsh);
+            s1.gu_col = static_cast<int>(sx * Fs);
+            s1.gu_uoff = static_cast<int>(Nsh);
+            s1.out = dgu_sh;
+            s1.out_ld = static_cast<int>(2 * Nsh);
+            s1.out_col = static_cast<int>(sx * 2 * Fs);
+            s1.out_uoff = static_cast<int>(Fs);
+            s1.N = D.F_shared;
+            s1.K = D.d;
+            s1.ksplit = D.d;
+            s1.Ne = 1;
+            s1.epilogue = BWD_EPI_SWIGLU;
+            s1.tab = one;
+            OCC_HIP(launch_bwd_dgrad(s1, dense_tiles, s));
+            BwdDgradArgs s2{};
+            s2.A = dgu_sh;
+            s2.lda = static_cast<int>(2 * Nsh);
+            s2.a_col = static_cast<int>(sx * 2 * Fs);
+            s2.B1 = static_cast<const char *>(ws_gate) + sx * Fs * d * es;
+            s2.B2 = static_cast<const char *>(ws_up) + sx * Fs * d * es;
+            s2.seg_off = dseg;
+            s2.tile_off = dtile;
+            s2.merge_out = dx_sh;
+            s2.merge_store = sx == 0;
+            s2.N = D.d;
+            s2.K = static_cast<int>(2 * Fs);
+            s2.ksplit = D.F_shared;
+            s2.Ne = 1;
+            s2.epilogue = BWD_EPI_MERGE;
+            s2.tab = one;
+            OCC_HIP(launch_bwd_dgrad(s2, dense_tiles, s));
+        }
+        BwdWgradArgs w3{};
+        w3.A = dy;
+        w3.lda = D.d;
+        w3.B = at<void>(workspace, L.h_sh);
+        w3.ldb = static_cast<int>(Nsh);
+        w3.b_col_grp = D.F_shared;
+        w3.zero_row = zero_row;
+        w3.C1 = dws_down;
+        w3.M = D.d;
+        w3.N = D.F_shared;
+        w3.msplit = D.d;
+        w3.n_groups = D.n_shared;
+        w3.rows = D.T;
+        w3.tab = one;
+        OCC_HIP(launch_bwd_wgrad(w3, s));
+        BwdWgradArgs w4{};
+        w4.A = dgu_sh;
+        w4.lda = static_cast<int>(2 * Nsh);
+        w4.a_col_grp = 2 * D.F_shared;
+        w4.B = x;
+        w4.ldb = D.d;
+        w4.zero_row = zero_row;
+        w4.C1 = dws_gate;
+        w4.C2 = dws_up;
+        w4.M = 2 * D.F_shared;
+        w4.N = D.d;
+        w4.msplit = D.F_shared;
+        w4.n_groups = D.n_shared;
+        w4.rows = D.T;
+        w4.tab = one;
+        OCC_HIP(launch_bwd_wgrad(w4, s));
+    }
+    OCC_TRY(mark(4));
+    // dx: SFD -> ORI, summed across groups (the dispatch's transpose), plus
+    // the shared experts' part, cast once
+    OCC_HIP(launch_combine(dx_sfd, bb.brim0, dx_sh, D.T, D.Nd, D.d, D.dtype == OCC_BF16, dx, s));
+    OCC_TRY(mark(5));
+    // dW_d[e] = sum over e's rows of dy_sfd[row's SFD row] (x) h[row]
+    BwdWgradArgs w1{};
+    w1.A = dy_sfd;
+    w1.a_rows = bb.epd_src;
+    w1.lda = D.d;
+    w1.B = h;
+    w1.ldb = D.F;
+    w1.seg_off = bb.epd_off;
+    w1.zero_row = zero_row;
+    w1.C1 = dw_down;
+    w1.M = D.d;
+    w1.N = D.F;
+    w1.msplit = D.d;
+    w1.n_groups = D.Ne;
+    w1.tab = tab;
+    OCC_HIP(launch_bwd_wgrad(w1, s));
+    OCC_TRY(mark(6));
+    // [dW_g; dW_u][e] = sum over e's rows of [dg; du] (x) x_sfd[row's SFD row]
+    BwdWgradArgs w2{};
+    w2.A = dgu;
+    w2.lda = 2 * D.F;
+    w2.B = x_sfd;
+    w2.b_rows = bb.epd_src;
+    w2.ldb = D.d;
+    w2.seg_off = bb.epd_off;
+    w2.zero_row = zero_row;
+    w2.C1 = dw_gate;
+    w2.C2 = dw_up;
+    w2.M = 2 * D.F;
+    w2.N = D.d;
+    w2.msplit = D.F;
+    w2.n_groups = D.Ne;
+    w2.tab = tab;
+    OCC_HIP(launch_bwd_wgrad(w2, s));
+    OCC_TRY(mark(7));
+    // routing-weight and logit gradients
+    if (dw || dlogits)
+        OCC_HIP(launch_route_backward(logits, at<int32_t>(workspace, L.ids), bb.tok_epd, dw_part,
+                                      L.dw_stride, L.dw_stride, D.T, D.Ne, D.k, dw, dlogits, s));
+    OCC_TRY(mark(8));
+    return OCC_OK;
 }
 
 occ_status occ_coactivation_stats(const occ_layer_desc *desc, const int32_t *ids,

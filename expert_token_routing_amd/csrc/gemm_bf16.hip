@@ -376,6 +376,16 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
                 const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];
                 const float h = g / (1.f + __expf(-g)) * u * wr;
                 smem[r * OUT_PITCH + wn * 64 + ni * 16 + (l & 15)] = f32_to_bf16_bits(h);
+                if (a.gu_out && r < t.rows) {
+                    // training: keep the pre-activations for the backward pass
+                    uint16_t *gu = static_cast<uint16_t *>(a.gu_out) +
+                                   (static_cast<size_t>(t.seg) + t.m0 + r) * 2 * N;
+                    const int f = t.n0 + wn * 64 + ni * 16 + (l & 15);
+                    if (f < N) {
+                        gu[f] = f32_to_bf16_bits(g);
+                        gu[N + f] = f32_to_bf16_bits(u);
+                    }
+                }
             }
         }
     __syncthreads();

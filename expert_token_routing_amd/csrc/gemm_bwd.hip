@@ -1,0 +1,385 @@
+// Grouped GEMMs of the backward pass on the bf16 matrix cores of gfx950
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation): the transposed sparse
+// matrix multiplications that the Occult paper builds "for both forward and
+// backward passes" (section 1; its appendix A.2 gives the forward ones).
+//
+// Every backward product has an operand whose contraction index is the
+// strided one: the weights in the input gradients (dh = dy W_d contracts over
+// W_d's rows) and both token-row operands in the weight gradients (dW = sum
+// over an expert's rows).  Such "K-major" operands are loaded as they lie in
+// memory -- each global row is one k, 256 contiguous columns of it are a
+// 512-byte LDS row -- and gfx950's LDS transpose read (ds_read_b64_tr_b16)
+// turns them into MFMA fragments: in each 16-lane group, lane 4a+b names the
+// 8 bytes at row k0+a, columns c0+4b..c0+4b+3, and lane i receives the four
+// values of column c0+i from rows k0..k0+3.  Two such reads give a lane its
+// 8 consecutive k.  The 16-byte chunks of a K-major LDS row are XOR-swizzled
+// by key(k) = 2 ((k mod 8) xor (4 * bit 3 of k)), which keeps each read's 16
+// rows x 32 bytes on distinct bank windows (two 256-byte cycles, the
+// minimum); "K-contiguous" operands use the forward kernels' layout.
+//
+// Tiles are 256 x 256 outputs per 512-thread workgroup (8 waves of 64 x 128),
+// K in 64-deep slices through two LDS buffers filled by direct global->LDS
+// loads, as in the forward GEMMs.
+//   k_bwd_dgrad  A = gathered K-contiguous rows, B = an expert's weights read
+//                K-major; routed row tiles over expert segments.  Epilogues:
+//                SwiGLU backward (dh -> dg, du and the routing-weight
+//                gradient's per-tile partial sums) or the fp32 merge of EPD
+//                rows into their SFD rows (first contributors store, the rest
+//                add).
+//   k_bwd_wgrad  A and B both K-major token rows of one expert; K = that
+//                expert's rows (tail rows read a zero row); the fp32 tile is
+//                stored into the expert's weight gradient.
+#include "launch.h"
+
+namespace occ {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int NT = 512;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WAVES_M = NT / kWave / 2;            // 4
+constexpr int WM = BM / WAVES_M, WN = BN / 2;      // 64 x 128 per wave
+constexpr int MI = WM / 16, NI = WN / 16;          // 4 x 8 MFMA blocks
+constexpr int CHUNKS = BK / 8;                     // 16-byte chunks per K-contiguous row
+constexpr int OP = BM * BK;                        // bf16 elements per operand tile
+constexpr int STAGE = 2 * OP;
+constexpr int NSTAGE = 2;
+static_assert(BM == BN, "both operand tiles share one size");
+static_assert(NSTAGE * STAGE * 2 <= 160 * 1024, "LDS");
+
+// ---- K-contiguous operand tiles: rows of 64 k, chunk c at c ^ ((r >> 1) & 7)
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * BK + ((chunk ^ ((row >> 1) & (CHUNKS - 1))) << 3);
+}
+
+// ---- K-major operand tiles: rows of 256 columns for one k each
+__device__ __forceinline__ int kkey(int k) { return ((k & 7) ^ ((k >> 1) & 4)) << 1; }
+__device__ __forceinline__ int kmaj(int k, int col) {
+    return k * BM + ((((col >> 3) ^ kkey(k))) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0)
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
+// MFMA fragment (8 consecutive k of column c0 + (lane & 15), k chunk lane >> 4
+// of the 32-deep step at kb) from a K-major tile, by two transpose reads.
+__device__ __forceinline__ bf16x8_t kmaj_frag(const uint16_t *tile, int kb, int c0) {
+    const int l = lane_id(), G = l >> 4, a = (l >> 2) & 3, b = l & 3;
+    const int k1 = kb + 8 * G + a, col = c0 + 4 * b;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tile + kmaj(k1, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tile + kmaj(k1 + 4, col)));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// MFMA fragment from a K-contiguous tile: row r, chunk (ks * 4 + lane >> 4).
+__device__ __forceinline__ bf16x8_t rows_frag(const uint16_t *tile, int r, int ks) {
+    return *reinterpret_cast<const bf16x8_t *>(tile + swz(r, ks * 4 + (lane_id() >> 4)));
+}
+
+// Workgroup -> (row tile, column tile), each XCD taking a contiguous range
+// (workgroup b runs on XCD b % 8), column tiles fastest.
+__device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int &tn) {
+    const int total = m_tiles * n_tiles;
+    const int per = (total + 7) >> 3;
+    const int b = blockIdx.x, idx = b >> 3;
+    if (idx >= per) return false;
+    const int logical = (b & 7) * per + idx;
+    if (logical >= total) return false;
+    tm = logical / n_tiles;
+    tn = logical - tm * n_tiles;
+    return true;
+}
+
+__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
+    int lo = 0, hi = Ne;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_off[mid] <= tm) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Issues the direct loads of one K-major operand slice: 64 k-rows of 256
+// columns.  Wave w, load i moves slice rows 2 (8 i + w) and +1, lane l the
+// physical chunk l & 31 of row l >> 5; row[i] points at column 0 of the
+// slice's columns in the global row of slice row 2 (8 i + w) + (l >> 5).
+__device__ __forceinline__ int kmajor_row(int i, int w) { return 2 * (8 * i + w) + (lane_id() >> 5); }
+
+__device__ __forceinline__ void issue_kmajor(uint32_t lds, const uint16_t *const (&row)[4], int w) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int c = (l & 31) ^ kkey(kmajor_row(i, w));
+        dma16(row[i] + 8 * c, __builtin_amdgcn_readfirstlane(lds + (8 * i + w) * 1024));
+    }
+}
+
+__device__ __forceinline__ void mfma_tile(const bf16x8_t (&a)[MI], const bf16x8_t (&b)[NI],
+                                          f32x4 (&acc)[MI][NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- dgrad ----
+
+__global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    int tm, tn;
+    const int m_tiles = a.tile_off[a.Ne], n_tiles = (a.N + BN - 1) / BN;
+    if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
+    const int p = find_pos(a.tile_off, a.Ne, tm);
+    const int seg0 = a.seg_off[p], len = a.seg_off[p + 1] - seg0;
+    const int nf = a.phase ? a.first_cnt[p] : 0;
+    const int seg = a.phase == 2 ? seg0 + nf : seg0;
+    const int m0 = (tm - a.tile_off[p]) * BM;
+    const int rows = min(BM, (a.phase == 1 ? nf : len - nf) - m0);
+    const int e = a.tab.expert[p];
+    const int n0 = tn * BN;
+
+    const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    // A: K-contiguous gathered rows, thread rows r0 + 64 i, chunk slot tid & 7
+    const uint16_t *a_src[4];
+    {
+        const int r0 = tid / CHUNKS;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = min(r0 + 64 * i, rows - 1);
+            const int pos = seg + m0 + r;
+            const int src = a.a_rows ? a.a_rows[pos] : pos;
+            const int ch = (tid % CHUNKS) ^ (((r0 + 64 * i) >> 1) & (CHUNKS - 1));
+            a_src[i] = A + static_cast<size_t>(src) * a.lda + a.a_col + 8 * ch;
+        }
+    }
+    // B: rows k of expert e's weights, from B1 for k < ksplit, else B2
+    const uint16_t *B1 = static_cast<const uint16_t *>(a.B1) + static_cast<size_t>(e) * a.ksplit * a.N;
+    const uint16_t *B2 = a.B2 ? static_cast<const uint16_t *>(a.B2) +
+                                    static_cast<size_t>(e) * (a.K - a.ksplit) * a.N
+                              : nullptr;
+    const int ncol = min(n0, a.N - BN);  // N >= BN; the last tile may overlap the previous one
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
+    const int nk = a.K / BK;
+
+    const int wm = w >> 1, wn = w & 1;
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt <= nk; kt++) {
+        // slice kt is issued in iteration kt, consumed in iteration kt + 1
+        if (kt > 0) {
+            wait_all_loads();
+            __syncthreads();
+        }
+        if (kt < nk) {
+            const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
+            const int k0 = kt * BK;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (8 * i + w) * 1024));
+            const uint16_t *brow[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kk = k0 + kmajor_row(i, w);
+                brow[i] = (kk < a.ksplit ? B1 + static_cast<size_t>(kk) * a.N
+                                         : B2 + static_cast<size_t>(kk - a.ksplit) * a.N) + ncol;
+            }
+            issue_kmajor(st + OP * 2, brow, w);
+        }
+        if (kt == 0) continue;
+        const uint16_t *sA = smem + ((kt - 1) % NSTAGE) * STAGE, *sB = sA + OP;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ks++) {
+            bf16x8_t fa[MI], fb[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) fa[mi] = rows_frag(sA, wm * WM + mi * 16 + (l & 15), ks);
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
+            mfma_tile(fa, fb, acc);
+        }
+    }
+
+    // column of acc[.][ni] for this lane, relative to the loaded columns
+    const int cbase = wn * WN + (l & 15);
+    if (a.epilogue == BWD_EPI_SWIGLU) {
+        // dh -> dg, du (bf16) and this tile half's share of dw = <dh, a>
+        const uint16_t *gu = static_cast<const uint16_t *>(a.gu);
+        uint16_t *out = static_cast<uint16_t *>(a.out);
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+                const bool ok = r < rows;
+                const int pos = seg + m0 + min(r, rows - 1);
+                const float wr = a.row_w ? a.row_w[pos] : 1.f;
+                const uint16_t *gr = gu + static_cast<size_t>(pos) * a.gu_ld + a.gu_col;
+                uint16_t *orow = out + static_cast<size_t>(pos) * a.out_ld + a.out_col;
+                float part = 0.f;
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) {
+                    const int f = ncol + cbase + ni * 16;
+                    if (f < n0) continue;  // overlapped columns belong to the previous tile
+                    const float g = bf16_bits_to_f32(gr[f]);
+                    const float u = bf16_bits_to_f32(gr[a.gu_uoff + f]);
+                    const float sg = 1.f / (1.f + __expf(-g));
+                    const float dh = acc[mi][ni][v];
+                    part += dh * (g * sg * u);
+                    const float da = wr * dh;
+                    if (ok) {
+                        orow[f] = f32_to_bf16_bits(da * u * sg * (1.f + g * (1.f - sg)));
+                        orow[a.out_uoff + f] = f32_to_bf16_bits(da * g * sg);
+                    }
+                }
+                // sum over the 16 lanes holding this row, then one write per wave half
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
+                if (a.dw_part && ok && (l & 15) == 0)
+                    a.dw_part[static_cast<size_t>(pos) * a.dw_stride + 2 * tn + wn] = part;
+            }
+    } else {
+        // merge into SFD rows (or dense rows): store, or add
+        float *out = a.merge_out;
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+                if (r >= rows) continue;
+                const int pos = seg + m0 + r;
+                const int erow = a.a_rows ? a.a_rows[pos] : pos;
+                const size_t dst = static_cast<size_t>(a.dst_rows ? a.dst_rows[erow] : erow) * a.N;
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) {
+                    const int c = ncol + cbase + ni * 16;
+                    if (c < n0) continue;
+                    if (a.merge_store) out[dst + c] = acc[mi][ni][v];
+                    else unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------- wgrad ----
+
+__global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
+    int tq, tn;
+    if (!map_tile(a.n_groups * m_tiles, n_tiles, tq, tn)) return;
+    const int grp = tq / m_tiles, tm = tq - grp * m_tiles;
+    const int seg = a.seg_off ? a.seg_off[grp] : 0;
+    const int len = a.seg_off ? a.seg_off[grp + 1] - seg : a.rows;
+    const int e = a.seg_off ? a.tab.expert[grp] : grp;
+    // M, N >= 256: the last tile of a dimension may overlap the previous one
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int mload = min(m0, a.M - BM), nload = min(n0, a.N - BN);
+
+    const int w = threadIdx.x / kWave, l = lane_id();
+    const uint16_t *A = static_cast<const uint16_t *>(a.A);
+    const uint16_t *B = static_cast<const uint16_t *>(a.B);
+    const uint16_t *Z = static_cast<const uint16_t *>(a.zero_row);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
+    const int nk = (len + BK - 1) / BK;
+    const int acol = a.a_col0 + grp * a.a_col_grp + mload;
+    const int bcol = a.b_col0 + grp * a.b_col_grp + nload;
+
+    const int wm = w >> 1, wn = w & 1;
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt <= nk; kt++) {
+        // slice kt is issued in iteration kt, consumed in iteration kt + 1
+        if (kt > 0) {
+            wait_all_loads();
+            __syncthreads();
+        }
+        if (kt < nk) {
+            const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
+            const uint16_t *arow[4], *brow[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kk = kt * BK + kmajor_row(i, w);
+                if (kk < len) {
+                    const int pos = seg + kk;
+                    const int ra = a.a_rows ? a.a_rows[pos] : pos;
+                    const int rb = a.b_rows ? a.b_rows[pos] : pos;
+                    arow[i] = A + static_cast<size_t>(ra) * a.lda + acol;
+                    brow[i] = B + static_cast<size_t>(rb) * a.ldb + bcol;
+                } else {
+                    arow[i] = Z;
+                    brow[i] = Z;
+                }
+            }
+            issue_kmajor(st, arow, w);
+            issue_kmajor(st + OP * 2, brow, w);
+        }
+        if (kt == 0) continue;
+        const uint16_t *sA = smem + ((kt - 1) % NSTAGE) * STAGE, *sB = sA + OP;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ks++) {
+            bf16x8_t fa[MI], fb[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) fa[mi] = kmaj_frag(sA, 32 * ks, wm * WM + mi * 16);
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
+            mfma_tile(fa, fb, acc);
+        }
+    }
+
+    // C[e] rows m < msplit -> C1, the rest -> C2 (gate and up halves)
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int m = mload + wm * WM + mi * 16 + 4 * (l >> 4) + v;
+            if (m < m0) continue;
+            float *row = m < a.msplit
+                             ? a.C1 + (static_cast<size_t>(e) * a.msplit + m) * a.N
+                             : a.C2 + (static_cast<size_t>(e) * (a.M - a.msplit) + (m - a.msplit)) * a.N;
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++) {
+                const int n = nload + wn * WN + ni * 16 + (l & 15);
+                if (n >= n0) row[n] = acc[mi][ni][v];
+            }
+        }
+}
+
+unsigned grid_for(size_t tiles) { return static_cast<unsigned>(8 * ((tiles + 7) / 8)); }
+
+}  // namespace
+
+hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream_t s) {
+    const unsigned grid = grid_for(max_m_tiles * ((a.N + BN - 1) / BN));
+    if (grid == 0) return hipSuccess;
+    k_bwd_dgrad<<<grid, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad(const BwdWgradArgs &a, hipStream_t s) {
+    const unsigned grid = grid_for(static_cast<size_t>(a.n_groups) * ((a.M + BM - 1) / BM) *
+                                   ((a.N + BN - 1) / BN));
+    if (grid == 0) return hipSuccess;
+    k_bwd_wgrad<<<grid, NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace occ

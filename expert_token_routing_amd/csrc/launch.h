@@ -56,6 +56,8 @@ hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t s);
 // a_r = A[a_rows[r]] (or A[r] when a_rows is NULL).  Routed mode walks the
 // segments [seg_off[p], seg_off[p+1]) of each placement position p with the
 // tile schedule tile_off; shared mode (seg_off NULL) is one segment of M rows.
+// gu_out (optional, training): the pre-activations are also stored, row r
+// holding bf16 g = a_r . Wg[e] in columns [0, N) and u in [N, 2N).
 struct UpArgs {
     const void *A;
     const int32_t *a_rows;
@@ -63,6 +65,7 @@ struct UpArgs {
     const int32_t *seg_off, *tile_off;
     const float *row_w;
     void *out;
+    void *gu_out;
     int M, K, N, Ne;
     PlaceTab tab;
 };
@@ -95,6 +98,70 @@ hipError_t launch_gemm_down_bf16_m64(const DownArgs &a, size_t max_m_tiles, hipS
 // --- the same two GEMMs in fp32 on the vector ALUs (gemm_f32.hip) ---
 hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+
+// --- backward grouped GEMMs, bf16 MFMA (gemm_bwd.hip) ---
+// Input-gradient GEMM over row tiles of 256 (tile_off over the segments
+// seg_off of placement positions; first_cnt and phase select rows as in
+// DownArgs):  C[pos, :] = A_row . B_e, K contracted, with A_row the K values
+// at column a_col of row a_rows[pos] (or pos) of A (rows lda apart), and row
+// k of B_e = B1[e] row k for k < ksplit, else B2[e] row k - ksplit (both N
+// wide, so B is read K-major; e = tab.expert[p]).  N >= 256.
+// Epilogue SWIGLU: C is dh; with g = gu[pos*gu_ld + gu_col + f], u at
+// + gu_uoff, and w = row_w[pos] (1 if NULL), writes bf16 dg, du to
+// out[pos*out_ld + out_col + f] and + out_uoff, and (dw_part non-NULL)
+// dw_part[pos * dw_stride + q] = this tile half's sum of dh * silu(g) u.
+// Epilogue MERGE: C goes to merge_out[dst_rows[a_rows[pos]]] (identity
+// without dst_rows / a_rows), N wide fp32: stored (merge_store) or added.
+enum { BWD_EPI_SWIGLU = 0, BWD_EPI_MERGE = 1 };
+struct BwdDgradArgs {
+    const void *A;
+    const int32_t *a_rows;
+    const void *B1, *B2;
+    const int32_t *seg_off, *tile_off, *first_cnt, *dst_rows;
+    const void *gu;
+    const float *row_w;
+    void *out;
+    float *dw_part;
+    float *merge_out;
+    int N, K, ksplit, Ne, phase, epilogue, dw_stride, merge_store;
+    int lda, a_col, gu_ld, gu_col, gu_uoff, out_ld, out_col, out_uoff;
+    PlaceTab tab;
+};
+hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream_t s);
+
+// Weight-gradient GEMM, one group of K rows per expert (routed: the expert
+// segments seg_off, placement position order, e = tab.expert[p]; dense:
+// seg_off NULL, n_groups blocks of `rows` rows, e = block):
+//   C_e[m, n] = sum over the group's rows pos of A[a_rows[pos]][a_col + m] *
+//               B[b_rows[pos]][b_col + n],   a_col = a_col0 + group * a_col_grp
+// both operands K-major (rows lda / ldb elements apart).  Rows m < msplit go
+// to C1[e] (msplit x N), the rest to C2[e].  M, N >= 256; tail rows of a
+// group read zero_row (at least 256 zero elements).
+struct BwdWgradArgs {
+    const void *A, *B;
+    const int32_t *a_rows, *b_rows, *seg_off;
+    const void *zero_row;
+    float *C1, *C2;
+    int M, N, msplit, lda, ldb, a_col0, a_col_grp, b_col0, b_col_grp, n_groups, rows;
+    PlaceTab tab;
+};
+hipError_t launch_bwd_wgrad(const BwdWgradArgs &a, hipStream_t s);
+
+// Row-tile schedules for `tile_rows`-row tiles from the expert segments
+// epd_off and first-contributor counts first_cnt (all rows, first, rest).
+hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, int Ne,
+                             int tile_rows, int32_t *tile_off, int32_t *tile_off_first,
+                             int32_t *tile_off_rest, hipStream_t s);
+// A one-segment schedule for a dense GEMM over T rows: seg_off = {0, T},
+// tile_off = {0, ceil(T / tile_rows)}.
+hipError_t launch_dense_sched(int T, int tile_rows, int32_t *seg_off, int32_t *tile_off,
+                              hipStream_t s);
+// Routing-weight and logit gradients: dw[t, j] = sum of dw_part over the
+// EPD row tok_epd[t*k + j]'s nparts partials (in order); dlogits through the
+// full softmax of the logits (logits may be NULL: dw only).
+hipError_t launch_route_backward(const float *logits, const int32_t *ids, const int32_t *tok_epd,
+                                 const float *dw_part, int nparts, int dw_stride, int T, int Ne,
+                                 int k, float *dw, float *dlogits, hipStream_t s);
 
 // --- co-activation statistics (coact.hip) ---
 hipError_t launch_coact(const int32_t *ids, int T, int k, const PlaceTab &tab, int32_t *C,

@@ -23,6 +23,10 @@ LIB_PATH = os.path.join(HERE, "libocc.so")
 OCC_OK, OCC_ERR_INVALID_ARG, OCC_ERR_UNSUPPORTED, OCC_ERR_WORKSPACE, OCC_ERR_HIP = range(5)
 OCC_F32, OCC_BF16 = 0, 1
 OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM, OCC_PRUNE_SIMILARITY = 0, 1, 2, 3
+OCC_FLAG_TRAIN = 1
+BSTAGES = ["dispatch", "dgrad_down", "dgrad_up", "shared", "combine", "wgrad_down", "wgrad_up",
+           "route"]
+OCC_BSTAGE_COUNT = len(BSTAGES)
 STAGES = ["route", "brim", "dispatch", "shared", "gemm_up", "gemm_down_first", "gemm_down_rest",
           "combine"]
 OCC_STAGE_COUNT = len(STAGES)
@@ -30,7 +34,7 @@ OCC_STAGE_COUNT = len(STAGES)
 EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route",
             "occ_similarity_accumulate", "occ_similarity_rank", "occ_route_similarity",
             "occ_build_brim", "occ_moe_forward", "occ_moe_forward_routed", "occ_gate",
-            "occ_moe_forward_gated", "occ_forward_views",
+            "occ_moe_forward_gated", "occ_moe_backward", "occ_forward_views",
             "occ_coactivation_stats", "occ_place_experts", "occ_events_create",
             "occ_events_destroy", "occ_event_elapsed_ms"]
 
@@ -89,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "occ_moe_forward_routed": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         vp, vp], ctypes.c_int),
             "occ_gate": ([dp, vp, vp, vp, vp], ctypes.c_int),
+            "occ_moe_backward": ([dp] + [vp] * 20 + [sz, vp, vp], ctypes.c_int),
             "occ_moe_forward_gated": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp],
                                       ctypes.c_int),
             "occ_forward_views": ([dp, vp, ctypes.POINTER(ForwardView)], ctypes.c_int),
@@ -290,6 +295,37 @@ def occ_moe_forward_gated(desc: LayerDesc, x, w_router, placement, w_gate, w_up,
         "occ_moe_forward_gated")
 
 
+def occ_moe_backward(desc: LayerDesc, dy, x, logits, placement, w_gate, w_up, w_down, ws_gate,
+                     ws_up, ws_down, dx, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
+                     dw, dlogits, workspace, stage_events=None, stream=None):
+    """Backward pass; the workspace must hold a training forward's state."""
+    T, d, Ne, F, k = desc.T, desc.d, desc.Ne, desc.F, desc.k
+    dt = torch.bfloat16 if desc.dtype == OCC_BF16 else torch.float32
+    f32 = torch.float32
+    L = _host_i32(placement, "placement", (desc.Nd, Ne // desc.Nd))
+    nsh, Fsh = desc.n_shared, desc.F_shared
+    sh = [None] * 6
+    if nsh > 0:
+        sh = [_dev(ws_gate, "ws_gate", dt, (nsh, Fsh, d)), _dev(ws_up, "ws_up", dt, (nsh, Fsh, d)),
+              _dev(ws_down, "ws_down", dt, (nsh, d, Fsh)),
+              _dev(dws_gate, "dws_gate", f32, (nsh, Fsh, d)),
+              _dev(dws_up, "dws_up", f32, (nsh, Fsh, d)),
+              _dev(dws_down, "dws_down", f32, (nsh, d, Fsh))]
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * (OCC_BSTAGE_COUNT + 1))(*stage_events)
+    _check(lib().occ_moe_backward(
+        ctypes.byref(desc), _dev(dy, "dy", dt, (T, d)), _dev(x, "x", dt, (T, d)),
+        _dev(logits, "logits", f32, (T, Ne)), _hp(L),
+        _dev(w_gate, "w_gate", dt, (Ne, F, d)), _dev(w_up, "w_up", dt, (Ne, F, d)),
+        _dev(w_down, "w_down", dt, (Ne, d, F)), *sh[:3], _dev(dx, "dx", dt, (T, d)),
+        _dev(dw_gate, "dw_gate", f32, (Ne, F, d)), _dev(dw_up, "dw_up", f32, (Ne, F, d)),
+        _dev(dw_down, "dw_down", f32, (Ne, d, F)), *sh[3:], _dev(dw, "dw", f32, (T, k)),
+        _dev(dlogits, "dlogits", f32, (T, Ne)), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+        _stream(stream)), "occ_moe_backward")
+
+
 def occ_forward_views(desc: LayerDesc, workspace) -> ForwardView:
     out = ForwardView()
     _check(lib().occ_forward_views(ctypes.byref(desc), _dev(workspace, "workspace", torch.uint8),
@@ -319,10 +355,11 @@ def occ_place_experts(C, Nd: int) -> np.ndarray:
 
 
 class StageEvents:
-    """OCC_STAGE_COUNT+1 HIP events for occ_moe_forward's stage timing."""
+    """stages+1 HIP events for a call's stage timing (occ_moe_forward's by
+    default; OCC_BSTAGE_COUNT for occ_moe_backward)."""
 
-    def __init__(self):
-        self.n = OCC_STAGE_COUNT + 1
+    def __init__(self, stages: int = OCC_STAGE_COUNT):
+        self.n = stages + 1
         self.arr = (ctypes.c_void_p * self.n)()
         _check(lib().occ_events_create(self.n, self.arr), "occ_events_create")
 
@@ -332,7 +369,7 @@ class StageEvents:
 
     def elapsed_ms(self) -> list[float]:
         out = []
-        for i in range(OCC_STAGE_COUNT):
+        for i in range(self.n - 1):
             ms = ctypes.c_float(0)
             _check(lib().occ_event_elapsed_ms(self.arr[i], self.arr[i + 1], ctypes.byref(ms)),
                    "occ_event_elapsed_ms")

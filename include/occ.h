@@ -69,6 +69,12 @@ typedef enum occ_prune_rule {
     OCC_PRUNE_SIMILARITY = 3
 } occ_prune_rule;
 
+/* Training: the forward also keeps what occ_moe_backward needs in the
+ * workspace (the SwiGLU pre-activations), and the workspace grows by the
+ * backward pass's buffers.  Needs bf16, d >= 256, F >= 256 (and F_shared >=
+ * 256 when there are shared experts): OCC_ERR_UNSUPPORTED otherwise. */
+#define OCC_FLAG_TRAIN 1
+
 /* Shape of one MoE layer.  Limits of this build:
  *   1 <= T, T*k < 2^31;  1 <= Ne <= 256;  1 <= k <= min(Ne, 32);
  *   1 <= Nd <= 64 and Nd divides Ne (n = Ne/Nd experts per group);
@@ -87,7 +93,7 @@ typedef struct occ_layer_desc {
     int32_t prune_rule;   /* occ_prune_rule */
     int32_t prune_groups; /* groups a token may use when pruning */
     int32_t dtype;        /* occ_dtype of x, weights and y */
-    int32_t flags;        /* reserved, must be 0 */
+    int32_t flags;        /* 0, or OCC_FLAG_TRAIN */
 } occ_layer_desc;
 
 /* Index structures of the paper's appendix A.2, as left in the workspace by
@@ -300,6 +306,58 @@ occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, con
                                   const void *ws_gate, const void *ws_up, const void *ws_down,
                                   void *y, void *workspace, size_t ws_bytes,
                                   void *const *stage_events, void *stream);
+
+/* Stages timed by occ_moe_backward when given events. */
+enum {
+    OCC_BSTAGE_DISPATCH = 0,    /* dy ORI -> SFD (BRIM_0) */
+    OCC_BSTAGE_DGRAD_DOWN = 1,  /* dh = dy W_d per EPD row, SwiGLU backward */
+    OCC_BSTAGE_DGRAD_UP = 2,    /* dg W_g + du W_u, merged EPD -> SFD in fp32 */
+    OCC_BSTAGE_SHARED = 3,      /* the shared experts' four products */
+    OCC_BSTAGE_COMBINE = 4,     /* dx SFD -> ORI across groups (+ shared) */
+    OCC_BSTAGE_WGRAD_DOWN = 5,  /* dW_d = sum dy h^T per expert */
+    OCC_BSTAGE_WGRAD_UP = 6,    /* dW_g, dW_u = sum [dg; du] x^T per expert */
+    OCC_BSTAGE_ROUTE = 7,       /* routing-weight and logit gradients */
+    OCC_BSTAGE_COUNT = 8
+};
+
+/* Backward pass of the layer (the training the paper runs, sections 1 and
+ * 4.3; its sparse matrix products serve "both forward and backward passes").
+ * The routing ids are held fixed; with dy the gradient of the loss in y:
+ *   per EPD row (token t, expert e, weight w, a = silu(g) u):
+ *     dh = W_d[e]^T dy_t,  dw = <dh, a>,  dg = w dh u silu'(g),
+ *     du = w dh silu(g),   dx_t += W_g[e]^T dg + W_u[e]^T du,
+ *     dW_d[e] += dy_t (w a)^T,  dW_g[e] += dg x_t^T,  dW_u[e] += du x_t^T;
+ *   shared experts likewise with w = 1;
+ *   dlogits[t][i] = p_i ([i chosen] dw_i - sum_j dw_j p_(e_j)), p the full
+ *   softmax of Eq. 2 (the weights are not renormalised).
+ * The Occult structure runs in reverse: dy is dispatched to the SFD rows
+ * (BRIM_0), each EPD row gathers its SFD row's gradient (BRIM_1), the input
+ * gradients of a group's experts are merged into SFD rows in fp32 (first
+ * contributor stores, the rest add) and summed across groups into dx.
+ *   workspace   must hold the state of an occ_moe_forward / _gated / _routed
+ *               call made with desc->flags = OCC_FLAG_TRAIN on the same x,
+ *               weights and placement (nothing else may run in between).
+ *   dy          T x d (dtype).  x, weights, placement_host: as the forward.
+ *   logits      T x Ne fp32 of that forward (the gated forward's are in its
+ *               workspace, see occ_forward_views), or NULL: then dlogits
+ *               must be NULL.
+ *   dx (out)    T x d (dtype), fp32 sums cast once.
+ *   dw_gate, dw_up (out)  Ne x F x d fp32;  dw_down (out) Ne x d x F fp32.
+ *   dws_gate, dws_up, dws_down (out)  the shared experts' (n_shared x ...),
+ *               fp32; NULL when n_shared = 0.
+ *   dw (out)    T x k fp32 routing-weight gradients, or NULL.
+ *   dlogits (out)  T x Ne fp32, or NULL.
+ *   stage_events  NULL or OCC_BSTAGE_COUNT+1 events, as for the forward.
+ * Errors: INVALID_ARG (missing pointers, flags without OCC_FLAG_TRAIN),
+ * UNSUPPORTED, WORKSPACE, HIP. */
+occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const void *x,
+                            const float *logits, const int32_t *placement_host,
+                            const void *w_gate, const void *w_up, const void *w_down,
+                            const void *ws_gate, const void *ws_up, const void *ws_down,
+                            void *dx, float *dw_gate, float *dw_up, float *dw_down,
+                            float *dws_gate, float *dws_up, float *dws_down, float *dw,
+                            float *dlogits, void *workspace, size_t ws_bytes,
+                            void *const *stage_events, void *stream);
 
 /* Device addresses of the intermediates occ_moe_forward leaves in a
  * workspace (pure host arithmetic, nothing queued). */

@@ -68,7 +68,9 @@ def _ws(desc):
     (dict(prune_rule=3, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=1, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=2, prune_groups=1, k=9), occ.OCC_ERR_INVALID_ARG),  # 1 group of 8 < k
-    (dict(flags=1), occ.OCC_ERR_INVALID_ARG),
+    (dict(flags=2), occ.OCC_ERR_INVALID_ARG),
+    (dict(flags=1, dtype=0), occ.OCC_ERR_UNSUPPORTED),  # training is bf16 only
+    (dict(flags=1, F=192), occ.OCC_ERR_UNSUPPORTED),    # backward tiles need F >= 256
     (dict(n_shared=1, F_shared=0), occ.OCC_ERR_INVALID_ARG),
     (dict(d=2000), occ.OCC_ERR_UNSUPPORTED),          # bf16 needs multiples of 64
     (dict(F=1000), occ.OCC_ERR_UNSUPPORTED),
@@ -168,6 +170,34 @@ def test_similarity_and_routed_calls_validate_without_a_gpu(L):
                                                      fake, fake, fake, None, None, None, fake,
                                                      fake, ws, None, None)
     assert routed(_null(), fake) == inv and routed(fake, _null()) == inv
+
+
+def test_backward_validates_without_a_gpu(L):
+    wl = W.OLMOE
+    good = np.ascontiguousarray(synth.contiguous_placement(wl))
+    fake = ctypes.c_void_p(0x1000)
+    hp = lambda a: ctypes.c_void_p(a.ctypes.data)
+    inv = occ.OCC_ERR_INVALID_ARG
+    train = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    plain = occ.desc_of(wl)
+    _, ws = _ws(train)
+    _, ws_plain = _ws(plain)
+    assert ws > ws_plain  # the training buffers
+
+    def bwd(desc, dy=fake, logits=fake, dlogits=fake, ws_bytes=ws, dws=None):
+        return L.occ_moe_backward(ctypes.byref(desc), dy, fake, logits, hp(good), fake, fake, fake,
+                                  None, None, None, fake, fake, fake, fake, dws, dws, dws, fake,
+                                  dlogits, fake, ws_bytes, None, None)
+    assert bwd(plain) == inv                      # needs the training flag
+    assert bwd(train, dy=_null()) == inv
+    assert bwd(train, logits=_null()) == inv      # dlogits needs the logits
+    assert bwd(train, ws_bytes=ws - 256) == occ.OCC_ERR_WORKSPACE
+    ds = occ.desc_of(W.DEEPSEEK, flags=occ.OCC_FLAG_TRAIN)
+    _, wsd = _ws(ds)
+    g3 = np.ascontiguousarray(synth.contiguous_placement(W.DEEPSEEK))
+    assert L.occ_moe_backward(ctypes.byref(ds), fake, fake, fake, hp(g3), fake, fake, fake,
+                              fake, fake, fake, fake, fake, fake, fake, None, None, None, fake,
+                              fake, fake, wsd, None, None) == inv  # shared gradients missing
 
 
 @pytest.mark.parametrize("Ne,Nd,seed", [(64, 8, 0), (60, 4, 1), (8, 2, 2), (16, 16, 3), (12, 1, 4),

@@ -1,0 +1,135 @@
+"""GPU parity of the backward pass (occ_moe_backward after a training
+forward) against the oracle's fp64 gradients: dx, the routed and shared
+expert weight gradients, the routing-weight and logit gradients.  Shapes
+cover both merge schedules (one launch after a zero-fill, first/rest),
+dimensions that are not multiples of the 256-wide tiles, shared experts and
+the OLMoE expert shape.
+
+Tolerances: dy, x and the weights are exact bf16 values; the device rounds
+the saved pre-activations g, u, the modulated state h and the SwiGLU
+gradients dg, du to bf16 (2^-9 relative each) and accumulates in fp32, and
+dx is rounded to bf16 once.  Each gradient therefore carries a few 2^-9 of
+relative error: 2e-2, measured normwise (per row for dx and per expert
+matrix for the weights, where single elements of a cancelling sum are
+meaningless) and 5e-2 of the tensor's scale element-wise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_amd import occ, synth, workloads as W
+
+from gpu_common import bits, row_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 2e-2
+ELEM_TOL = 5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    occ.lib()
+
+
+def shape(name, T, d, F, Ne=8, k=2, Nd=4, n_shared=0, F_shared=0, index=11):
+    return W.Workload(name, index, T=T, d=d, Ne=Ne, k=k, Nd=Nd, F=F, n_shared=n_shared,
+                      F_shared=F_shared, n_c=2, bonus=1.0)
+
+
+def run(wl, placement=None, with_logits=True):
+    inp = synth.make_all(wl)
+    dev = to_dev(inp)
+    L = inp["placement"] if placement is None else placement
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(wl.index)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = dict(dx=torch.empty(wl.T, wl.d, dtype=dt, device="cuda"),
+               dW_gate=torch.empty(wl.Ne, wl.F, wl.d, **f32),
+               dW_up=torch.empty(wl.Ne, wl.F, wl.d, **f32),
+               dW_down=torch.empty(wl.Ne, wl.d, wl.F, **f32),
+               dw=torch.empty(wl.T, wl.k, **f32),
+               dlogits=torch.empty(wl.T, wl.Ne, **f32) if with_logits else None)
+    sh = dict(dWs_gate=None, dWs_up=None, dWs_down=None)
+    if wl.n_shared:
+        sh = dict(dWs_gate=torch.empty(wl.n_shared, wl.F_shared, wl.d, **f32),
+                  dWs_up=torch.empty(wl.n_shared, wl.F_shared, wl.d, **f32),
+                  dWs_down=torch.empty(wl.n_shared, wl.d, wl.F_shared, **f32))
+    out.update(sh)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"] if with_logits else None, L,
+                         dev["w_gate"], dev["w_up"], dev["w_down"], dev["ws_gate"], dev["ws_up"],
+                         dev["ws_down"], out["dx"], out["dW_gate"], out["dW_up"], out["dW_down"],
+                         out["dWs_gate"], out["dWs_up"], out["dWs_down"], out["dw"],
+                         out["dlogits"], ws)
+    torch.cuda.synchronize()
+    v = occ.occ_forward_views(desc, ws)
+    ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
+    got = {k2: (None if t is None else t.float().cpu().numpy()) for k2, t in out.items()}
+    ref = oracle.moe_backward(bits(inp["x"]), ids, w, dy.double().numpy(), bits(inp["w_gate"]),
+                              bits(inp["w_up"]), bits(inp["w_down"]), bits(inp["ws_gate"]),
+                              bits(inp["ws_up"]), bits(inp["ws_down"]),
+                              logits=inp["logits"].numpy() if with_logits else None)
+    return got, ref
+
+
+def normwise(a, b):
+    den = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (den if den > 0 else 1.0)
+
+
+def check(got, ref, keys):
+    assert row_err(got["dx"], ref["dx"]).max() <= NORM_TOL
+    for key in keys:
+        g, r = got[key], ref[key]
+        for e in range(r.shape[0]):       # per expert matrix
+            assert normwise(g[e], r[e]) <= NORM_TOL, (key, e, normwise(g[e], r[e]))
+            scale = np.abs(r[e]).max()
+            assert np.abs(g[e] - r[e]).max() <= ELEM_TOL * scale, (key, e)
+    for key in ("dw", "dlogits"):
+        if got.get(key) is None:
+            continue
+        assert normwise(got[key], ref[key]) <= NORM_TOL, (key, normwise(got[key], ref[key]))
+        assert np.abs(got[key] - ref[key]).max() <= ELEM_TOL * np.abs(ref[key]).max(), key
+
+
+ROUTED = ["dW_gate", "dW_up", "dW_down"]
+SHARED = ["dWs_gate", "dWs_up", "dWs_down"]
+
+
+@pytest.mark.parametrize("wl", [
+    shape("bwd_one_launch", T=300, d=256, F=256),              # T*k < 128*Ne: zero-fill merge
+    shape("bwd_two_phase", T=1100, d=256, F=256, index=12),    # first / rest merge
+    shape("bwd_ragged", T=700, d=384, F=320, k=3, Nd=2, index=13),  # overlapping tiles
+], ids=lambda w: w.name)
+def test_backward_matches_oracle(wl):
+    got, ref = run(wl)
+    check(got, ref, ROUTED)
+
+
+def test_backward_with_shared_experts():
+    wl = shape("bwd_shared", T=500, d=256, F=256, n_shared=2, F_shared=320, index=14)
+    got, ref = run(wl)
+    check(got, ref, ROUTED + SHARED)
+
+
+def test_backward_olmoe_expert_shape():
+    """d = 2048, F = 1024 (32 K slices in the input gradients, full-width
+    weight tiles), fewer experts so that the fp64 oracle stays small."""
+    wl = shape("bwd_olmoe_dims", T=256, d=2048, F=1024, Ne=8, k=2, Nd=4, index=15)
+    got, ref = run(wl)
+    check(got, ref, ROUTED)
+
+
+def test_backward_rescheduled_placement_and_no_logits():
+    wl = shape("bwd_placement", T=900, d=256, F=256, Ne=16, k=4, Nd=4, index=16)
+    L = np.random.default_rng(3).permutation(16).astype(np.int32).reshape(4, 4)
+    got, ref = run(wl, placement=L, with_logits=False)
+    check(got, ref, ROUTED)
