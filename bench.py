@@ -40,6 +40,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contiguous", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training step (forward with saved state + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     return ap.parse_args()
@@ -208,6 +210,12 @@ def main():
     roofline.update({"traffic": traffic, "kernel": up_kernel, "avg_ms": round(up_ms, 5),
                      "flops_per_launch": flops_up, "bytes_per_launch": bytes_up})
 
+    # --- training step: forward keeping the backward's state, then backward
+    train = None
+    if (not args.no_train and wl.dtype == W.DTYPE_BF16 and not sim and not wl.gated
+            and wl.d >= 256 and wl.F >= 256 and (wl.n_shared == 0 or wl.F_shared >= 256)):
+        train = train_leg(args, wl, g, L_alg1, stream)
+
     # --- CPU baseline: the oracle on a bounded sample of this workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -227,10 +235,79 @@ def main():
         "stages_ms": {s: round(v, 5) for s, v in stages.items()},
         "contiguous": res_contig,
     }
+    if train is not None:
+        out["train"] = train
     if sim:
         out["config"]["pruning"] = f"similarity, {wl.prune_groups} groups"
         out["similarity_table_ms"] = round(table_ms, 4)
     print(json.dumps(out), flush=True)
+
+
+def train_leg(args, wl, g, L, stream):
+    """Time forward (OCC_FLAG_TRAIN) + backward steps on the same inputs; the
+    backward GEMMs' achieved TFLOP/s from HIP events around each stage."""
+    import numpy as np
+    import torch
+
+    from expert_token_routing_amd import occ
+
+    dev = torch.device("cuda:0")
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    ws = occ.alloc_workspace(desc, dev)
+    dt = torch.bfloat16
+    f32 = dict(dtype=torch.float32, device=dev)
+    y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(77)) * 0.5).to(dt).to(dev)
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    dws = [None, None, None]
+    if wl.n_shared:
+        dws = [torch.empty(wl.n_shared, wl.F_shared, wl.d, **f32),
+               torch.empty(wl.n_shared, wl.F_shared, wl.d, **f32),
+               torch.empty(wl.n_shared, wl.d, wl.F_shared, **f32)]
+    dw = torch.empty(wl.T, wl.k, **f32)
+    dl = torch.empty(wl.T, wl.Ne, **f32)
+
+    def step(fev=None, bev=None):
+        occ.occ_moe_forward(desc, g["x"], g["logits"], L, g["w_gate"], g["w_up"], g["w_down"],
+                            g["ws_gate"], g["ws_up"], g["ws_down"], y, ws, stage_events=fev)
+        occ.occ_moe_backward(desc, dy, g["x"], g["logits"], L, g["w_gate"], g["w_up"],
+                             g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], dx, dWg, dWu,
+                             dWd, *dws, dw, dl, ws, stage_events=bev)
+
+    log(f"[bench] training step: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fev = [occ.StageEvents() for _ in range(args.steps)]
+    bev = [occ.StageEvents(occ.OCC_BSTAGE_COUNT) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(fev[i].handles, bev[i].handles)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    fst = np.array([e.elapsed_ms() for e in fev]).mean(0)
+    bst = np.array([e.elapsed_ms() for e in bev]).mean(0)
+    for e in fev + bev:
+        e.close()
+    bstages = {s: float(v) for s, v in zip(occ.BSTAGES, bst)}
+    rows = wl.T * wl.k
+    flops = {"dgrad_down": 2.0 * rows * wl.d * wl.F, "dgrad_up": 2.0 * rows * 2 * wl.F * wl.d,
+             "wgrad_down": 2.0 * rows * wl.d * wl.F, "wgrad_up": 2.0 * rows * 2 * wl.F * wl.d}
+    gemms = {k: {"ms": round(bstages[k], 5),
+                 "tflops": round(f / (bstages[k] / 1e3) / 1e12, 1),
+                 "frac": round(f / (bstages[k] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+             for k, f in flops.items()}
+    log(f"[bench] training step: {ms:.4f} ms (forward {fst.sum():.4f}, backward {bst.sum():.4f})")
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.T / (ms / 1e3), 1),
+            "forward_ms": round(float(fst.sum()), 5), "backward_ms": round(float(bst.sum()), 5),
+            "backward_stages_ms": {k: round(v, 5) for k, v in bstages.items()},
+            "backward_gemms": gemms}
 
 
 def cpu_baseline(wl, inp, placement, seconds, sim_rank=None):

@@ -256,6 +256,62 @@ def moe_backward(x, ids, w, dy, w_gate, w_up, w_down, ws_gate=None, ws_up=None, 
     return out
 
 
+def moe_backward_rows(rows, x, ids, w, dy, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
+                      ws_down=None, logits=None) -> dict:
+    """The per-token parts of moe_backward for the listed rows: dx, dw and
+    (with logits) dlogits rows."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    xa, dt = _float_arg(x)
+    T, d = xa.shape
+    ids = _i32(ids)
+    k = ids.shape[1]
+    g, _ = _float_arg(w_gate)
+    u, _ = _float_arg(w_up)
+    dn, _ = _float_arg(w_down)
+    Ne, F = g.shape[0], g.shape[1]
+    n_sh, F_sh = 0, 0
+    sg = su = sd = None
+    if ws_gate is not None:
+        sg, _ = _float_arg(ws_gate)
+        su, _ = _float_arg(ws_up)
+        sd, _ = _float_arg(ws_down)
+        n_sh, F_sh = sg.shape[0], sg.shape[1]
+    lg = None if logits is None else np.ascontiguousarray(logits, dtype=np.float32)
+    out = dict(dx=np.empty((len(rows), d)), dw=np.empty((len(rows), k)))
+    if lg is not None:
+        out["dlogits"] = np.empty((len(rows), Ne))
+    nul = ctypes.c_void_p(0)
+    opt = lambda a: _p(a) if a is not None else nul
+    rc = _load().orc_moe_backward_rows(
+        len(rows), _p(rows), d, Ne, k, F, n_sh, F_sh, dt, _p(xa), _p(ids),
+        _p(np.ascontiguousarray(w, dtype=np.float64)), opt(lg), _p(g), _p(u), _p(dn), opt(sg),
+        opt(su), opt(sd), _p(np.ascontiguousarray(dy, dtype=np.float64)), _p(out["dx"]),
+        _p(out["dw"]), opt(out.get("dlogits")))
+    _check(rc, "moe_backward_rows")
+    return out
+
+
+def moe_wgrad_rows(x, ids, w, dy, w_gate, w_up, w_down, e: int, f_rows, n_rows) -> dict:
+    """Rows f_rows of dW_gate[e], dW_up[e] and rows n_rows of dW_down[e]."""
+    xa, dt = _float_arg(x)
+    T, d = xa.shape
+    ids = _i32(ids)
+    k = ids.shape[1]
+    g, _ = _float_arg(w_gate)
+    u, _ = _float_arg(w_up)
+    dn, _ = _float_arg(w_down)
+    F = g.shape[1]
+    fs, ns = _i32(f_rows), _i32(n_rows)
+    out = dict(dW_gate=np.empty((len(fs), d)), dW_up=np.empty((len(fs), d)),
+               dW_down=np.empty((len(ns), F)))
+    rc = _load().orc_moe_wgrad_rows(
+        T, d, k, F, dt, _p(xa), _p(ids), _p(np.ascontiguousarray(w, dtype=np.float64)), _p(g),
+        _p(u), _p(dn), _p(np.ascontiguousarray(dy, dtype=np.float64)), int(e), len(fs), _p(fs),
+        len(ns), _p(ns), _p(out["dW_gate"]), _p(out["dW_up"]), _p(out["dW_down"]))
+    _check(rc, "moe_wgrad_rows")
+    return out
+
+
 def threads(nthreads: int = 0) -> int:
     """How many threads moe_rows runs with for this request."""
     return int(_load().orc_threads(nthreads))

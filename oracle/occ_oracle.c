@@ -491,6 +491,61 @@ int orc_moe_rows(int nrows, const int64_t *rows, int d, int k, int F, int n_sh, 
 }
 
 /*
+ * One token's backward through one expert (see orc_moe_backward below for
+ * the formulas): from x_t and dy_t, the expert's activation a (F), the
+ * gradients dg, du of its pre-activations (F, already scaled by the
+ * routing weight wt) and the routing-weight gradient <dh, a>.
+ */
+static double expert_backward(const double *xt, const double *dyt, const void *Wg,
+                              const void *Wu, const void *Wd, int dtype, size_t wb, size_t db,
+                              int F, int d, double wt, double *a_out, double *dg, double *du)
+{
+    double dwt = 0.0;
+    for (int f = 0; f < F; f++) {
+        double gf = 0.0, uf = 0.0, dh = 0.0;
+        for (int c = 0; c < d; c++) {
+            gf += elem(Wg, dtype, wb + (size_t)f * d + c) * xt[c];
+            uf += elem(Wu, dtype, wb + (size_t)f * d + c) * xt[c];
+            dh += elem(Wd, dtype, db + (size_t)c * F + f) * dyt[c];
+        }
+        double sg = 1.0 / (1.0 + exp(-gf)), a = gf * sg * uf;
+        dwt += dh * a;
+        double da = wt * dh;
+        dg[f] = da * uf * sg * (1.0 + gf * (1.0 - sg));
+        du[f] = da * gf * sg;
+        if (a_out)
+            a_out[f] = a;
+    }
+    return dwt;
+}
+
+/* dx contribution W_g^T dg + W_u^T du of one expert. */
+static void expert_dx(const void *Wg, const void *Wu, int dtype, size_t wb, int F, int d,
+                      const double *dg, const double *du, double *out)
+{
+    for (int c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int f = 0; f < F; f++)
+            s += elem(Wg, dtype, wb + (size_t)f * d + c) * dg[f] +
+                 elem(Wu, dtype, wb + (size_t)f * d + c) * du[f];
+        out[c] = s;
+    }
+}
+
+/* Full softmax of one token's logits into p. */
+static void softmax_row(const float *l, int Ne, double *p)
+{
+    double m = l[0], s = 0.0;
+    for (int e = 1; e < Ne; e++)
+        if (l[e] > m)
+            m = l[e];
+    for (int e = 0; e < Ne; e++)
+        s += exp((double)l[e] - m);
+    for (int e = 0; e < Ne; e++)
+        p[e] = exp((double)l[e] - m) / s;
+}
+
+/*
  * Backward pass of the layer (the gradients the paper's training runs need,
  * sections 1 and 4.3; the pages give no formulas, these are the derivatives
  * of Eq. 1 with the routing ids held fixed).  For token t and its j-th
@@ -543,38 +598,19 @@ int orc_moe_backward(int T, int d, int Ne, int k, int F, int n_sh, int F_sh, int
                 for (int j = 0; j < k; j++) {
                     if (ids[(size_t)t * k + j] != e)
                         continue;
-                    double wt = w[(size_t)t * k + j], dwt = 0.0;
+                    double wt = w[(size_t)t * k + j];
                     const double *dyt = dy + (size_t)t * d;
                     for (int c = 0; c < d; c++)
                         xt[c] = elem(x, dtype, (size_t)t * d + c);
-                    for (int f = 0; f < F; f++) {
-                        double gf = 0.0, uf = 0.0, dh = 0.0;
-                        for (int c = 0; c < d; c++) {
-                            gf += elem(Wg, dtype, wb + (size_t)f * d + c) * xt[c];
-                            uf += elem(Wu, dtype, wb + (size_t)f * d + c) * xt[c];
-                            dh += elem(Wd, dtype, db + (size_t)c * F + f) * dyt[c];
-                        }
-                        double sg = 1.0 / (1.0 + exp(-gf)), a = gf * sg * uf;
-                        dwt += dh * a;
-                        double da = wt * dh;
-                        dg[f] = da * uf * sg * (1.0 + gf * (1.0 - sg));
-                        du[f] = da * gf * sg;
-                        for (int c = 0; c < d; c++)
-                            dWd[db + (size_t)c * F + f] += dyt[c] * (wt * a);
-                    }
+                    double dwt = expert_backward(xt, dyt, Wg, Wu, Wd, dtype, wb, db, F, d, wt, g,
+                                                 dg, du);
                     for (int f = 0; f < F; f++)
                         for (int c = 0; c < d; c++) {
+                            dWd[db + (size_t)c * F + f] += dyt[c] * (wt * g[f]);
                             dWg[wb + (size_t)f * d + c] += dg[f] * xt[c];
                             dWu[wb + (size_t)f * d + c] += du[f] * xt[c];
                         }
-                    double *dxt = dxp + ((size_t)t * k + j) * d;
-                    for (int c = 0; c < d; c++) {
-                        double s = 0.0;
-                        for (int f = 0; f < F; f++)
-                            s += elem(Wg, dtype, wb + (size_t)f * d + c) * dg[f] +
-                                 elem(Wu, dtype, wb + (size_t)f * d + c) * du[f];
-                        dxt[c] = s;
-                    }
+                    expert_dx(Wg, Wu, dtype, wb, F, d, dg, du, dxp + ((size_t)t * k + j) * d);
                     dw[(size_t)t * k + j] = dwt;
                 }
         }
@@ -594,55 +630,34 @@ int orc_moe_backward(int T, int d, int Ne, int k, int F, int n_sh, int F_sh, int
         memset(dWsu, 0, sizeof(double) * (size_t)n_sh * F_sh * d);
         memset(dWsd, 0, sizeof(double) * (size_t)n_sh * d * F_sh);
         double *xt = malloc(sizeof(double) * d), *dg = malloc(sizeof(double) * F_sh);
-        double *du = malloc(sizeof(double) * F_sh);
+        double *du = malloc(sizeof(double) * F_sh), *a = malloc(sizeof(double) * F_sh);
+        double *dxs = malloc(sizeof(double) * d);
         for (int sx = 0; sx < n_sh; sx++) {
             size_t wb = (size_t)sx * F_sh * d, db = (size_t)sx * d * F_sh;
             for (int t = 0; t < T; t++) {
                 const double *dyt = dy + (size_t)t * d;
                 for (int c = 0; c < d; c++)
                     xt[c] = elem(x, dtype, (size_t)t * d + c);
-                for (int f = 0; f < F_sh; f++) {
-                    double gf = 0.0, uf = 0.0, dh = 0.0;
-                    for (int c = 0; c < d; c++) {
-                        gf += elem(Wsg, dtype, wb + (size_t)f * d + c) * xt[c];
-                        uf += elem(Wsu, dtype, wb + (size_t)f * d + c) * xt[c];
-                        dh += elem(Wsd, dtype, db + (size_t)c * F_sh + f) * dyt[c];
-                    }
-                    double sg = 1.0 / (1.0 + exp(-gf)), a = gf * sg * uf;
-                    dg[f] = dh * uf * sg * (1.0 + gf * (1.0 - sg));
-                    du[f] = dh * gf * sg;
-                    for (int c = 0; c < d; c++)
-                        dWsd[db + (size_t)c * F_sh + f] += dyt[c] * a;
-                }
+                expert_backward(xt, dyt, Wsg, Wsu, Wsd, dtype, wb, db, F_sh, d, 1.0, a, dg, du);
                 for (int f = 0; f < F_sh; f++)
                     for (int c = 0; c < d; c++) {
+                        dWsd[db + (size_t)c * F_sh + f] += dyt[c] * a[f];
                         dWsg[wb + (size_t)f * d + c] += dg[f] * xt[c];
                         dWsu[wb + (size_t)f * d + c] += du[f] * xt[c];
                     }
-                for (int c = 0; c < d; c++) {
-                    double s = 0.0;
-                    for (int f = 0; f < F_sh; f++)
-                        s += elem(Wsg, dtype, wb + (size_t)f * d + c) * dg[f] +
-                             elem(Wsu, dtype, wb + (size_t)f * d + c) * du[f];
-                    dx[(size_t)t * d + c] += s;
-                }
+                expert_dx(Wsg, Wsu, dtype, wb, F_sh, d, dg, du, dxs);
+                for (int c = 0; c < d; c++)
+                    dx[(size_t)t * d + c] += dxs[c];
             }
         }
-        free(xt); free(dg); free(du);
+        free(xt); free(dg); free(du); free(a); free(dxs);
     }
 
     if (logits) {
         double *p = malloc(sizeof(double) * Ne);
         for (int t = 0; t < T; t++) {
-            const float *l = logits + (size_t)t * Ne;
-            double m = l[0], s = 0.0, acc = 0.0;
-            for (int e = 1; e < Ne; e++)
-                if (l[e] > m)
-                    m = l[e];
-            for (int e = 0; e < Ne; e++)
-                s += exp((double)l[e] - m);
-            for (int e = 0; e < Ne; e++)
-                p[e] = exp((double)l[e] - m) / s;
+            double acc = 0.0;
+            softmax_row(logits + (size_t)t * Ne, Ne, p);
             for (int j = 0; j < k; j++)
                 acc += dw[(size_t)t * k + j] * p[ids[(size_t)t * k + j]];
             for (int e = 0; e < Ne; e++)
@@ -654,6 +669,148 @@ int orc_moe_backward(int T, int d, int Ne, int k, int F, int n_sh, int F_sh, int
         }
         free(p);
     }
+    return ORC_OK;
+}
+
+/*
+ * The per-token parts of orc_moe_backward for the listed token rows only
+ * (dy is the full T x d gradient): dx rows (nrows x d), routing-weight
+ * gradient rows (nrows x k) and, when logits is non-NULL, dlogits rows
+ * (nrows x Ne).  Same arithmetic and order as the full pass.
+ */
+int orc_moe_backward_rows(int nrows, const int64_t *rows, int d, int Ne, int k, int F, int n_sh,
+                          int F_sh, int dtype, const void *x, const int32_t *ids, const double *w,
+                          const float *logits, const void *Wg, const void *Wu, const void *Wd,
+                          const void *Wsg, const void *Wsu, const void *Wsd, const double *dy,
+                          double *dx, double *dw, double *dlogits)
+{
+    int Fmax = F > F_sh ? F : F_sh;
+    int rc = ORC_OK;
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        double *xt = malloc(sizeof(double) * d), *dg = malloc(sizeof(double) * Fmax);
+        double *du = malloc(sizeof(double) * Fmax), *part = malloc(sizeof(double) * d);
+        double *p = malloc(sizeof(double) * Ne);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int i = 0; i < nrows; i++) {
+            int64_t t = rows[i];
+            const double *dyt = dy + (size_t)t * d;
+            double *dxt = dx + (size_t)i * d;
+            for (int c = 0; c < d; c++) {
+                xt[c] = elem(x, dtype, (size_t)t * d + c);
+                dxt[c] = 0.0;
+            }
+            for (int j = 0; j < k; j++) {
+                int e = ids[(size_t)t * k + j];
+                if (e < 0 || e >= Ne) {
+                    rc = ORC_BAD;
+                    continue;
+                }
+                dw[(size_t)i * k + j] =
+                    expert_backward(xt, dyt, Wg, Wu, Wd, dtype, (size_t)e * F * d,
+                                    (size_t)e * d * F, F, d, w[(size_t)t * k + j], NULL, dg, du);
+                expert_dx(Wg, Wu, dtype, (size_t)e * F * d, F, d, dg, du, part);
+                for (int c = 0; c < d; c++)
+                    dxt[c] += part[c];
+            }
+            for (int sx = 0; sx < n_sh; sx++) {
+                expert_backward(xt, dyt, Wsg, Wsu, Wsd, dtype, (size_t)sx * F_sh * d,
+                                (size_t)sx * d * F_sh, F_sh, d, 1.0, NULL, dg, du);
+                expert_dx(Wsg, Wsu, dtype, (size_t)sx * F_sh * d, F_sh, d, dg, du, part);
+                for (int c = 0; c < d; c++)
+                    dxt[c] += part[c];
+            }
+            if (logits) {
+                double acc = 0.0;
+                softmax_row(logits + (size_t)t * Ne, Ne, p);
+                for (int j = 0; j < k; j++)
+                    acc += dw[(size_t)i * k + j] * p[ids[(size_t)t * k + j]];
+                for (int e = 0; e < Ne; e++)
+                    dlogits[(size_t)i * Ne + e] = -p[e] * acc;
+                for (int j = 0; j < k; j++) {
+                    int e = ids[(size_t)t * k + j];
+                    dlogits[(size_t)i * Ne + e] += p[e] * dw[(size_t)i * k + j];
+                }
+            }
+        }
+        free(xt); free(dg); free(du); free(part); free(p);
+    }
+    return rc;
+}
+
+/*
+ * Rows of one routed expert's weight gradients, summed over every token
+ * routed to it (t ascending, as in orc_moe_backward): rows fs[0..nf) of
+ * dW_g[e] and dW_u[e] (d values each) and rows ns[0..nn) of dW_d[e] (F
+ * values each).
+ */
+int orc_moe_wgrad_rows(int T, int d, int k, int F, int dtype, const void *x, const int32_t *ids,
+                       const double *w, const void *Wg, const void *Wu, const void *Wd,
+                       const double *dy, int e, int nf, const int32_t *fs, int nn,
+                       const int32_t *ns, double *dWg, double *dWu, double *dWd)
+{
+    int cnt = 0;
+    for (size_t i = 0; i < (size_t)T * k; i++)
+        cnt += ids[i] == e;
+    int64_t *tok = malloc(sizeof(int64_t) * (cnt + 1));
+    double *wts = malloc(sizeof(double) * (cnt + 1));
+    int q = 0;
+    for (int t = 0; t < T; t++)
+        for (int j = 0; j < k; j++)
+            if (ids[(size_t)t * k + j] == e) {
+                tok[q] = t;
+                wts[q++] = w[(size_t)t * k + j];
+            }
+    /* per token: dg, du at the sampled f and the modulated activation */
+    double *sdg = malloc(sizeof(double) * ((size_t)cnt * nf + 1));
+    double *sdu = malloc(sizeof(double) * ((size_t)cnt * nf + 1));
+    double *sh = malloc(sizeof(double) * ((size_t)cnt * F + 1));
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        double *xt = malloc(sizeof(double) * d), *dg = malloc(sizeof(double) * F);
+        double *du = malloc(sizeof(double) * F), *a = malloc(sizeof(double) * F);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+        for (int i = 0; i < cnt; i++) {
+            for (int c = 0; c < d; c++)
+                xt[c] = elem(x, dtype, (size_t)tok[i] * d + c);
+            expert_backward(xt, dy + (size_t)tok[i] * d, Wg, Wu, Wd, dtype, (size_t)e * F * d,
+                            (size_t)e * d * F, F, d, wts[i], a, dg, du);
+            for (int r = 0; r < nf; r++) {
+                sdg[(size_t)i * nf + r] = dg[fs[r]];
+                sdu[(size_t)i * nf + r] = du[fs[r]];
+            }
+            for (int f = 0; f < F; f++)
+                sh[(size_t)i * F + f] = wts[i] * a[f];
+        }
+        free(xt); free(dg); free(du); free(a);
+    }
+    for (int r = 0; r < nf; r++)
+        for (int c = 0; c < d; c++) {
+            double sg = 0.0, su = 0.0;
+            for (int i = 0; i < cnt; i++) {
+                double xv = elem(x, dtype, (size_t)tok[i] * d + c);
+                sg += sdg[(size_t)i * nf + r] * xv;
+                su += sdu[(size_t)i * nf + r] * xv;
+            }
+            dWg[(size_t)r * d + c] = sg;
+            dWu[(size_t)r * d + c] = su;
+        }
+    for (int r = 0; r < nn; r++)
+        for (int f = 0; f < F; f++) {
+            double s = 0.0;
+            for (int i = 0; i < cnt; i++)
+                s += dy[(size_t)tok[i] * d + ns[r]] * sh[(size_t)i * F + f];
+            dWd[(size_t)r * F + f] = s;
+        }
+    free(tok); free(wts); free(sdg); free(sdu); free(sh);
     return ORC_OK;
 }
 

@@ -133,3 +133,55 @@ def test_backward_rescheduled_placement_and_no_logits():
     L = np.random.default_rng(3).permutation(16).astype(np.int32).reshape(4, 4)
     got, ref = run(wl, placement=L, with_logits=False)
     check(got, ref, ROUTED)
+
+
+def test_backward_full_size_sampled():
+    """The OLMoE-shaped layer at the size bench.py runs (T = 8192), training
+    forward + backward in the benchmark's launch configuration; sampled dx,
+    dw and dlogits rows and sampled rows of two experts' weight gradients
+    against the oracle computed one by one."""
+    from gpu_common import inputs
+    wl = W.OLMOE
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], None, None, None, y, ws)
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(8)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    dw = torch.empty(wl.T, wl.k, **f32)
+    dl = torch.empty(wl.T, wl.Ne, **f32)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                         dev["w_down"], None, None, None, dx, dWg, dWu, dWd, None, None, None, dw,
+                         dl, ws)
+    torch.cuda.synchronize()
+    v = occ.occ_forward_views(desc, ws)
+    ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
+    dyd = dy.double().numpy()
+    rows = synth.sample_rows(wl.T, 32, seed=21)
+    r = oracle.moe_backward_rows(rows, bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                 bits(inp["w_up"]), bits(inp["w_down"]),
+                                 logits=inp["logits"].numpy())
+    assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
+    for key, got in (("dw", dw), ("dlogits", dl)):
+        g = got.cpu().numpy()[rows]
+        assert normwise(g, r[key]) <= NORM_TOL, key
+        assert np.abs(g - r[key]).max() <= ELEM_TOL * np.abs(r[key]).max(), key
+    fs, ns = np.array([0, 517, wl.F - 1]), np.array([0, 1000, wl.d - 1])
+    for e in (5, 60):
+        q = oracle.moe_wgrad_rows(bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                  bits(inp["w_up"]), bits(inp["w_down"]), e, fs, ns)
+        for key, got, sel in (("dW_gate", dWg, fs), ("dW_up", dWu, fs), ("dW_down", dWd, ns)):
+            g = got[e].cpu().numpy()[sel]
+            for i in range(len(sel)):
+                assert normwise(g[i], q[key][i]) <= NORM_TOL, (key, e, sel[i])
+                assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max()

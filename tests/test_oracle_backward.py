@@ -150,3 +150,25 @@ def test_backward_is_linear_in_dy_and_zero_at_zero():
     for key in g1:
         np.testing.assert_allclose(g2[key], -2.0 * g1[key], rtol=1e-12, atol=1e-14)
         assert np.all(g0[key] == 0.0), key
+
+
+def test_sampled_backward_equals_the_full_pass():
+    """The per-row and per-expert-row functions (used at full sizes, where
+    the full pass is too large) give the full pass's values."""
+    wl = small(W.DTYPE_BF16, n_shared=1, T=11, d=32, Ne=6, k=3, F=16)
+    inp, logits, ids, dy = setup(wl, scale=0.5)
+    g = backward(inp, logits, ids, dy)
+    w = probs(logits, ids)
+    rows = np.array([0, 5, 10, 5])
+    r = oracle.moe_backward_rows(rows, view(inp["x"]), ids, w, dy, view(inp["w_gate"]),
+                                 view(inp["w_up"]), view(inp["w_down"]), view(inp["ws_gate"]),
+                                 view(inp["ws_up"]), view(inp["ws_down"]), logits=logits)
+    for key in ("dx", "dw", "dlogits"):
+        np.testing.assert_allclose(r[key], g[key][rows], rtol=1e-13, atol=1e-15, err_msg=key)
+    for e in (0, 3):
+        fs, ns = np.array([0, 7, 15]), np.array([1, 31])
+        q = oracle.moe_wgrad_rows(view(inp["x"]), ids, w, dy, view(inp["w_gate"]),
+                                  view(inp["w_up"]), view(inp["w_down"]), e, fs, ns)
+        np.testing.assert_allclose(q["dW_gate"], g["dW_gate"][e][fs], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(q["dW_up"], g["dW_up"][e][fs], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(q["dW_down"], g["dW_down"][e][ns], rtol=1e-13, atol=1e-15)
