@@ -126,17 +126,29 @@ __device__ __forceinline__ void issue_kmajor(uint32_t lds, const uint16_t *const
     }
 }
 
+// The MFMA is issued with the operands' roles swapped (it computes the
+// transposed 16 x 16 block), so that lane l holds output row (l & 15) of
+// the mi block and the 4 consecutive columns 4 (l >> 4) .. +3 of the ni
+// block: the epilogues then move 8- and 16-byte row pieces.
+// SWAP = false keeps the plain layout: lane l holds rows 4 (l >> 4) .. +3 of
+// column (l & 15), so 16 lanes cover 64 contiguous bytes of a row -- the
+// better shape for the fp32 atomic adds of the merge.
+template <bool SWAP>
 __device__ __forceinline__ void mfma_tile(const bf16x8_t (&a)[MI], const bf16x8_t (&b)[NI],
                                           f32x4 (&acc)[MI][NI]) {
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
         for (int ni = 0; ni < NI; ni++)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
 }
+
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- dgrad ----
 
+template <int EPI>
 __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     int tm, tn;
@@ -211,48 +223,55 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             for (int mi = 0; mi < MI; mi++) fa[mi] = rows_frag(sA, wm * WM + mi * 16 + (l & 15), ks);
 #pragma unroll
             for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
-            mfma_tile(fa, fb, acc);
+            mfma_tile<EPI == BWD_EPI_SWIGLU>(fa, fb, acc);
         }
     }
 
-    // column of acc[.][ni] for this lane, relative to the loaded columns
-    const int cbase = wn * WN + (l & 15);
-    if (a.epilogue == BWD_EPI_SWIGLU) {
+    // SWIGLU: acc[mi][ni][v] is row wm*WM + mi*16 + (l & 15), column
+    // (relative to the loaded columns) wn*WN + ni*16 + 4*(l >> 4) + v.
+    // MERGE: row wm*WM + mi*16 + 4*(l >> 4) + v, column wn*WN + ni*16 + (l & 15).
+    const int rloc = wm * WM + (l & 15), cloc = wn * WN + 4 * (l >> 4);
+    if constexpr (EPI == BWD_EPI_SWIGLU) {
         // dh -> dg, du (bf16) and this tile half's share of dw = <dh, a>
         const uint16_t *gu = static_cast<const uint16_t *>(a.gu);
         uint16_t *out = static_cast<uint16_t *>(a.out);
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+        for (int mi = 0; mi < MI; mi++) {
+            const int r = rloc + mi * 16;
+            const bool ok = r < rows;
+            const int pos = seg + m0 + min(r, rows - 1);
+            const float wr = a.row_w ? a.row_w[pos] : 1.f;
+            const uint16_t *gr = gu + static_cast<size_t>(pos) * a.gu_ld + a.gu_col;
+            uint16_t *orow = out + static_cast<size_t>(pos) * a.out_ld + a.out_col;
+            float part = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
-                const bool ok = r < rows;
-                const int pos = seg + m0 + min(r, rows - 1);
-                const float wr = a.row_w ? a.row_w[pos] : 1.f;
-                const uint16_t *gr = gu + static_cast<size_t>(pos) * a.gu_ld + a.gu_col;
-                uint16_t *orow = out + static_cast<size_t>(pos) * a.out_ld + a.out_col;
-                float part = 0.f;
+            for (int ni = 0; ni < NI; ni++) {
+                const int f = ncol + cloc + ni * 16;  // 4 consecutive features f..f+3
+                if (f < n0) continue;  // overlapped columns belong to the previous tile
+                const u16x4 g4 = *reinterpret_cast<const u16x4 *>(gr + f);
+                const u16x4 u4 = *reinterpret_cast<const u16x4 *>(gr + a.gu_uoff + f);
+                u16x4 dg4, du4;
 #pragma unroll
-                for (int ni = 0; ni < NI; ni++) {
-                    const int f = ncol + cbase + ni * 16;
-                    if (f < n0) continue;  // overlapped columns belong to the previous tile
-                    const float g = bf16_bits_to_f32(gr[f]);
-                    const float u = bf16_bits_to_f32(gr[a.gu_uoff + f]);
+                for (int v = 0; v < 4; v++) {
+                    const float g = bf16_bits_to_f32(g4[v]), u = bf16_bits_to_f32(u4[v]);
                     const float sg = 1.f / (1.f + __expf(-g));
                     const float dh = acc[mi][ni][v];
                     part += dh * (g * sg * u);
                     const float da = wr * dh;
-                    if (ok) {
-                        orow[f] = f32_to_bf16_bits(da * u * sg * (1.f + g * (1.f - sg)));
-                        orow[a.out_uoff + f] = f32_to_bf16_bits(da * g * sg);
-                    }
+                    dg4[v] = f32_to_bf16_bits(da * u * sg * (1.f + g * (1.f - sg)));
+                    du4[v] = f32_to_bf16_bits(da * g * sg);
                 }
-                // sum over the 16 lanes holding this row, then one write per wave half
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
-                if (a.dw_part && ok && (l & 15) == 0)
-                    a.dw_part[static_cast<size_t>(pos) * a.dw_stride + 2 * tn + wn] = part;
+                if (ok) {
+                    *reinterpret_cast<u16x4 *>(orow + f) = dg4;
+                    *reinterpret_cast<u16x4 *>(orow + a.out_uoff + f) = du4;
+                }
             }
+            // the 4 lanes holding this row (l >> 4 = 0..3) sum, one write per wave half
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (a.dw_part && ok && l < 16)
+                a.dw_part[static_cast<size_t>(pos) * a.dw_stride + 2 * tn + wn] = part;
+        }
     } else {
         // merge into SFD rows (or dense rows): store, or add
         float *out = a.merge_out;
@@ -264,13 +283,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
                 if (r >= rows) continue;
                 const int pos = seg + m0 + r;
                 const int erow = a.a_rows ? a.a_rows[pos] : pos;
-                const size_t dst = static_cast<size_t>(a.dst_rows ? a.dst_rows[erow] : erow) * a.N;
+                float *drow = out + static_cast<size_t>(a.dst_rows ? a.dst_rows[erow] : erow) * a.N;
 #pragma unroll
                 for (int ni = 0; ni < NI; ni++) {
-                    const int c = ncol + cbase + ni * 16;
+                    const int c = ncol + wn * WN + ni * 16 + (l & 15);
                     if (c < n0) continue;
-                    if (a.merge_store) out[dst + c] = acc[mi][ni][v];
-                    else unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                    if (a.merge_store) drow[c] = acc[mi][ni][v];
+                    else unsafeAtomicAdd(drow + c, acc[mi][ni][v]);
                 }
             }
     }
@@ -341,26 +360,25 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
             for (int mi = 0; mi < MI; mi++) fa[mi] = kmaj_frag(sA, 32 * ks, wm * WM + mi * 16);
 #pragma unroll
             for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
-            mfma_tile(fa, fb, acc);
+            mfma_tile<true>(fa, fb, acc);
         }
     }
 
-    // C[e] rows m < msplit -> C1, the rest -> C2 (gate and up halves)
+    // C[e] rows m < msplit -> C1, the rest -> C2 (gate and up halves); each
+    // lane stores 4 consecutive columns of a row
 #pragma unroll
-    for (int mi = 0; mi < MI; mi++)
+    for (int mi = 0; mi < MI; mi++) {
+        const int m = mload + wm * WM + mi * 16 + (l & 15);
+        if (m < m0) continue;
+        float *row = m < a.msplit
+                         ? a.C1 + (static_cast<size_t>(e) * a.msplit + m) * a.N
+                         : a.C2 + (static_cast<size_t>(e) * (a.M - a.msplit) + (m - a.msplit)) * a.N;
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int m = mload + wm * WM + mi * 16 + 4 * (l >> 4) + v;
-            if (m < m0) continue;
-            float *row = m < a.msplit
-                             ? a.C1 + (static_cast<size_t>(e) * a.msplit + m) * a.N
-                             : a.C2 + (static_cast<size_t>(e) * (a.M - a.msplit) + (m - a.msplit)) * a.N;
-#pragma unroll
-            for (int ni = 0; ni < NI; ni++) {
-                const int n = nload + wn * WN + ni * 16 + (l & 15);
-                if (n >= n0) row[n] = acc[mi][ni][v];
-            }
+        for (int ni = 0; ni < NI; ni++) {
+            const int n = nload + wn * WN + ni * 16 + 4 * (l >> 4);
+            if (n >= n0) *reinterpret_cast<f32x4 *>(row + n) = acc[mi][ni];
         }
+    }
 }
 
 unsigned grid_for(size_t tiles) { return static_cast<unsigned>(8 * ((tiles + 7) / 8)); }
@@ -370,7 +388,8 @@ unsigned grid_for(size_t tiles) { return static_cast<unsigned>(8 * ((tiles + 7) 
 hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream_t s) {
     const unsigned grid = grid_for(max_m_tiles * ((a.N + BN - 1) / BN));
     if (grid == 0) return hipSuccess;
-    k_bwd_dgrad<<<grid, NT, 0, s>>>(a);
+    if (a.epilogue == BWD_EPI_SWIGLU) k_bwd_dgrad<BWD_EPI_SWIGLU><<<grid, NT, 0, s>>>(a);
+    else k_bwd_dgrad<BWD_EPI_MERGE><<<grid, NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
