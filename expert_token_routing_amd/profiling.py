@@ -145,8 +145,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd:
              "|---|---|---|---|"]
     recs = []
     for k in sorted(set(f) | set(w)):
-        if k == "copy":
-            continue
+        if k == "copy" or not k.startswith("k_"):
+            continue  # the calibration copy and the harness's own torch kernels
         fv, wv = f.get(k, [0.0]), w.get(k, [0.0])
         fb, wb = f_scale * sum(fv) / len(fv), w_scale * sum(wv) / len(wv)
         lines.append(f"| {k} | {len(fv)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
