@@ -17,61 +17,102 @@
 //                 giving each (chunk, bin) its first row, plus sfd_off,
 //                 epd_off, first-contributor counts and GEMM tile schedules;
 //   k_brim_fill   per chunk: a token's rank inside a bin is the popcount of
-//                 the lower lanes' bits in a per-wave 64-bit mask (built with
-//                 LDS atomic OR, so the result does not depend on timing)
-//                 plus the counts of the earlier waves.
+//                 the lower tokens' bits in its 64-token block's mask for
+//                 that bin (built with LDS atomic OR, so the result does not
+//                 depend on timing) plus the counts of the earlier blocks.
+// Count and fill give each routing entry (token, j) its own thread, so a
+// thread's work is one entry, not a token's k of them.
 // The result is identical, entry by entry, to the serial counters.
 #include "launch.h"
 
 namespace occ {
 namespace {
 
-constexpr int kWavesPerChunk = kBrimChunk / kWave;
+constexpr int kBlocksPerChunk = kBrimChunk / kWave;  // 64-token blocks of a chunk
+constexpr int kBrimThreads = 1024;  // count and fill: one thread per routing entry
+constexpr int kScanLds = 14336;     // (chunk, bin) counts the scan keeps in LDS
 
-__device__ __forceinline__ bool has_pos(const uint64_t (&em)[4], int p) {
+// Is any position in [lo, hi) set in the 256-bit position mask em?
+__device__ __forceinline__ bool any_in(const uint64_t *em, int lo, int hi) {
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const int a = max(lo - 64 * w, 0), b = min(hi - 64 * w, 64);
+        if (a < b) {
+            const uint64_t hi_mask = b == 64 ? ~0ull : (1ull << b) - 1ull;
+            any |= (em[w] & hi_mask & ~((1ull << a) - 1ull)) != 0ull;
+        }
+    }
+    return any;
+}
+
+__device__ __forceinline__ bool has_pos(const uint64_t *em, int p) {
     return (em[p >> 6] >> (p & 63)) & 1ull;
 }
 
-// Is placement position p (one of the token's experts, mask em) the token's
-// lowest position inside p's group?  Positions g*n .. g*n+n-1 form group g.
-__device__ __forceinline__ bool first_in_group(const uint64_t (&em)[4], int p, int n) {
-    for (int q = (p / n) * n; q < p; q++)
-        if (has_pos(em, q)) return false;
-    return true;
-}
+// Shared state of one chunk: its ids (s_id[token * k + j]), placement
+// tables, and per token the 256-bit mask of its placement positions and
+// the mask of its groups.
+struct ChunkIds {
+    uint8_t id[kBrimChunk * kMaxK];
+    uint64_t em[kBrimChunk][4];
+    uint64_t gm[kBrimChunk];
+    uint8_t grp[kMaxNe];
+    int16_t pos[kMaxNe];
+};
 
-__global__ __launch_bounds__(kBrimChunk) void k_brim_count(const int32_t *__restrict__ ids, int T,
-                                                           int k, PlaceTab tab,
-                                                           int32_t *__restrict__ chunk_cnt) {
-    __shared__ int cnt[kMaxBins];
-    __shared__ uint8_t s_grp[kMaxNe];
-    __shared__ int16_t s_pos[kMaxNe];
-    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
-    for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
-    for (int e = threadIdx.x; e < Ne; e += blockDim.x) {
-        s_grp[e] = tab.grp[e];
-        s_pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
+// Coalesced load of the chunk's ids and the placement tables; then, one
+// thread per token, the position and group masks.  Ends with a barrier.
+__device__ __forceinline__ void load_chunk(const int32_t *__restrict__ ids, int t0, int nt, int k,
+                                           const PlaceTab &tab, ChunkIds &c) {
+    const int n = tab.n;
+    const size_t base = static_cast<size_t>(t0) * k;
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x)
+        c.id[i] = static_cast<uint8_t>(ids[base + i]);
+    for (int e = threadIdx.x; e < tab.Ne; e += blockDim.x) {
+        c.grp[e] = tab.grp[e];
+        c.pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
     }
     __syncthreads();
-    const int t = blockIdx.x * kBrimChunk + threadIdx.x;
-    if (t < T) {
-        uint64_t gmask = 0, em[4] = {0, 0, 0, 0};
+    if (threadIdx.x < nt) {
+        const int tok = threadIdx.x;
+        uint64_t em[4] = {0, 0, 0, 0}, gm = 0;
         for (int j = 0; j < k; j++) {
-            const int e = ids[static_cast<size_t>(t) * k + j];
-            const int p = s_pos[e];
-            em[p >> 6] |= 1ull << (p & 63);
-            atomicAdd(&cnt[Nd + p], 1);
-            gmask |= 1ull << s_grp[e];
+            const int e = c.id[tok * k + j];
+            const int q = c.pos[e];
+            em[q >> 6] |= 1ull << (q & 63);
+            gm |= 1ull << c.grp[e];
         }
-        for (int j = 0; j < k; j++) {
-            const int p = s_pos[ids[static_cast<size_t>(t) * k + j]];
-            if (first_in_group(em, p, n)) atomicAdd(&cnt[Nd + Ne + p], 1);
-        }
-        while (gmask) {
-            const int g = __ffsll(static_cast<unsigned long long>(gmask)) - 1;
-            atomicAdd(&cnt[g], 1);
-            gmask &= gmask - 1;
-        }
+#pragma unroll
+        for (int w = 0; w < 4; w++) c.em[tok][w] = em[w];
+        c.gm[tok] = gm;
+    }
+    __syncthreads();
+}
+
+// Entry (tok, j) with placement position q is its token's first contributor
+// to its group's SFD row when no lower position of that group is set.
+__device__ __forceinline__ bool first_contrib(const ChunkIds &c, int tok, int q, int n) {
+    return !any_in(c.em[tok], (q / n) * n, q);
+}
+
+__global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__restrict__ ids,
+                                                             int T, int k, PlaceTab tab,
+                                                             int32_t *__restrict__ chunk_cnt) {
+    __shared__ int cnt[kMaxBins];
+    __shared__ ChunkIds c;
+    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
+    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
+    load_chunk(ids, t0, nt, k, tab, c);
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int tok = i / k, q = c.pos[c.id[i]];
+        atomicAdd(&cnt[Nd + q], 1);
+        if (first_contrib(c, tok, q, n)) atomicAdd(&cnt[Nd + Ne + q], 1);
+    }
+    for (int i = threadIdx.x; i < nt * Nd; i += blockDim.x) {
+        const int g = i / nt, tok = i - g * nt;
+        if ((c.gm[tok] >> g) & 1ull) atomicAdd(&cnt[g], 1);
     }
     __syncthreads();
     for (int b = threadIdx.x; b < NB; b += blockDim.x)
@@ -89,17 +130,30 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ tile_off_rest) {
     __shared__ int total[kMaxBins];
     __shared__ int binoff[kMaxBins];
+    __shared__ int s_cc[kScanLds];
     const int NB = Nd + 2 * Ne;
     const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    const size_t n = static_cast<size_t>(nchunks) * NB;
+    // the (chunk, bin) counts come in with one coalesced pass when they fit
+    const bool staged = n <= static_cast<size_t>(kScanLds);
+    if (staged) {
+        for (size_t i = threadIdx.x; i < n; i += blockDim.x) s_cc[i] = chunk_cnt[i];
+        __syncthreads();
+    }
 
-    // 1. per bin, exclusive scan over chunks (64 chunks per wave step)
+    // 1. per bin, exclusive scan over chunks (64 chunks per wave step);
+    //    staged scans stay in LDS until step 3
     for (int b = wv; b < NB; b += nw) {
         int run = 0;
         for (int c0 = 0; c0 < nchunks; c0 += kWave) {
             const int c = c0 + lane;
-            const int v = c < nchunks ? chunk_cnt[static_cast<size_t>(c) * NB + b] : 0;
+            const size_t o = static_cast<size_t>(c) * NB + b;
+            const int v = c < nchunks ? (staged ? s_cc[o] : chunk_cnt[o]) : 0;
             const int incl = wave_incl_scan(v);
-            if (c < nchunks) chunk_base[static_cast<size_t>(c) * NB + b] = run + incl - v;
+            if (c < nchunks) {
+                if (staged) s_cc[o] = run + incl - v;
+                else chunk_base[o] = run + incl - v;
+            }
             run += __shfl(incl, kWave - 1);
         }
         if (lane == 0) total[b] = run;
@@ -152,95 +206,96 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     __syncthreads();
 
     // 3. each (chunk, bin) start = start of the bin + rows of earlier chunks
-    const size_t n = static_cast<size_t>(nchunks) * NB;
-    for (size_t i = threadIdx.x; i < n; i += blockDim.x) chunk_base[i] += binoff[i % NB];
+    for (size_t i = threadIdx.x; i < n; i += blockDim.x)
+        chunk_base[i] = (staged ? s_cc[i] : chunk_base[i]) + binoff[i % NB];
 }
 
-__global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
+__global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
     const int32_t *__restrict__ ids, const float *__restrict__ w, int T, int k, PlaceTab tab,
     const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ sfd_off,
     const int32_t *__restrict__ epd_off, const int32_t *__restrict__ first_cnt, int dense,
     int32_t *__restrict__ brim0, int32_t *__restrict__ epd_src, float *__restrict__ epd_w,
     int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows,
     int32_t *__restrict__ brim1) {
-    __shared__ unsigned long long wmask[kWavesPerChunk][kMaxBins];
-    __shared__ int wpre[kWavesPerChunk][kMaxBins];
+    // bit (tok mod 64) of bmask[tok / 64][b]: token tok is in bin b
+    __shared__ unsigned long long bmask[kBlocksPerChunk][kMaxBins];
+    __shared__ int bpre[kBlocksPerChunk][kMaxBins];
     __shared__ int s_base[kMaxBins];
-    __shared__ uint8_t s_grp[kMaxNe];
-    __shared__ int16_t s_pos[kMaxNe];
+    __shared__ int s_epd[kMaxNe + 1], s_first[kMaxNe], s_sfd[kMaxNd + 1];
+    __shared__ ChunkIds c;
     const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
-    for (int i = threadIdx.x; i < kWavesPerChunk * NB; i += blockDim.x)
-        wmask[i / NB][i % NB] = 0ull;
+    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
+    for (int i = threadIdx.x; i < kBlocksPerChunk * NB; i += blockDim.x)
+        bmask[i / NB][i % NB] = 0ull;
     for (int b = threadIdx.x; b < NB; b += blockDim.x)
         s_base[b] = chunk_base[static_cast<size_t>(blockIdx.x) * NB + b];
-    for (int e = threadIdx.x; e < Ne; e += blockDim.x) {
-        s_grp[e] = tab.grp[e];
-        s_pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
-    }
-    __syncthreads();
+    for (int e = threadIdx.x; e < Ne; e += blockDim.x) s_first[e] = first_cnt[e];
+    for (int e = threadIdx.x; e <= Ne; e += blockDim.x) s_epd[e] = epd_off[e];
+    for (int g = threadIdx.x; g <= Nd; g += blockDim.x) s_sfd[g] = sfd_off[g];
+    load_chunk(ids, t0, nt, k, tab, c);
 
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
-    const int t = blockIdx.x * kBrimChunk + threadIdx.x;
-    const bool valid = t < T;
-    const unsigned long long bit = 1ull << lane, lower = bit - 1ull;
-    uint64_t gmask = 0, em[4] = {0, 0, 0, 0};
-    if (valid) {
-        for (int j = 0; j < k; j++) {
-            const int e = ids[static_cast<size_t>(t) * k + j];
-            const int p = s_pos[e];
-            em[p >> 6] |= 1ull << (p & 63);
-            gmask |= 1ull << s_grp[e];
-            atomicOr(&wmask[wv][Nd + p], bit);
-        }
-        for (int j = 0; j < k; j++) {
-            const int p = s_pos[ids[static_cast<size_t>(t) * k + j]];
-            if (first_in_group(em, p, n)) atomicOr(&wmask[wv][Nd + Ne + p], bit);
-        }
-        for (uint64_t m = gmask; m; m &= m - 1)
-            atomicOr(&wmask[wv][__ffsll(static_cast<unsigned long long>(m)) - 1], bit);
+    // bin membership bits (LDS atomic OR, so the result does not depend on timing)
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int tok = i / k, q = c.pos[c.id[i]];
+        const unsigned long long bit = 1ull << (tok & 63);
+        atomicOr(&bmask[tok >> 6][Nd + q], bit);
+        if (first_contrib(c, tok, q, n)) atomicOr(&bmask[tok >> 6][Nd + Ne + q], bit);
+    }
+    for (int i = threadIdx.x; i < nt * Nd; i += blockDim.x) {
+        const int g = i / nt, tok = i - g * nt;
+        if ((c.gm[tok] >> g) & 1ull) atomicOr(&bmask[tok >> 6][g], 1ull << (tok & 63));
     }
     __syncthreads();
     for (int b = threadIdx.x; b < NB; b += blockDim.x) {
-        int run = 0;
-        for (int q = 0; q < kWavesPerChunk; q++) {
-            wpre[q][b] = run;
-            run += __popcll(wmask[q][b]);
+        int run = s_base[b];
+        for (int q = 0; q < kBlocksPerChunk; q++) {
+            bpre[q][b] = run;
+            run += __popcll(bmask[q][b]);
         }
     }
     __syncthreads();
-    if (!valid) return;
 
-    // rank of this token among the chunk-ordered tokens of bin b
-    auto slot_of = [&](int b) { return s_base[b] + wpre[wv][b] + __popcll(wmask[wv][b] & lower); };
+    // row of token tok in bin b: tokens of the chunk before it in the bin
+    auto slot_of = [&](int tok, int b) {
+        const unsigned long long below = (1ull << (tok & 63)) - 1ull;
+        return bpre[tok >> 6][b] + __popcll(bmask[tok >> 6][b] & below);
+    };
 
-    for (int g = 0; g < Nd; g++)
-        brim0[static_cast<size_t>(g) * T + t] = ((gmask >> g) & 1ull) ? slot_of(g) : -1;
-    for (int j = 0; j < k; j++) {
-        const size_t o = static_cast<size_t>(t) * k + j;
-        const int p = s_pos[ids[o]], g = p / n;
-        const int srow = slot_of(g);
-        const int erow = slot_of(Nd + p);
+    // BRIM_0: coalesced along tokens
+    for (int i = threadIdx.x; i < nt * Nd; i += blockDim.x) {
+        const int g = i / nt, tok = i - g * nt;
+        brim0[static_cast<size_t>(g) * T + t0 + tok] = ((c.gm[tok] >> g) & 1ull) ? slot_of(tok, g) : -1;
+    }
+    // one thread per routing entry: its EPD row, SFD row and merge order
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int tok = i / k;
+        const size_t o = static_cast<size_t>(t0) * k + i;
+        const int q = c.pos[c.id[i]], g = q / n;
+        const int srow = slot_of(tok, g);
+        const int erow = slot_of(tok, Nd + q);
         epd_src[erow] = srow;
         epd_w[erow] = w[o];
         tok_epd[o] = erow;
-        // merge order: first contributors of expert p, then its other rows
-        const int e0 = epd_off[p];
-        const int f_before = slot_of(Nd + Ne + p);  // e0 + first rows of p before t
-        if (first_in_group(em, p, n)) down_rows[f_before] = erow;
-        else down_rows[e0 + first_cnt[p] + (erow - e0) - (f_before - e0)] = erow;
+        // merge order: first contributors of expert q, then its other rows
+        const int e0 = s_epd[q];
+        const int f_before = slot_of(tok, Nd + Ne + q);  // e0 + first rows of q before tok
+        if (first_contrib(c, tok, q, n)) down_rows[f_before] = erow;
+        else down_rows[e0 + s_first[q] + (erow - e0) - (f_before - e0)] = erow;
         if (dense) {
-            const int g0 = sfd_off[g], Ng = sfd_off[g + 1] - g0;
-            brim1[static_cast<size_t>(n) * g0 + static_cast<size_t>(p - g * n) * Ng + (srow - g0)] =
-                erow - epd_off[g * n];
+            const int g0 = s_sfd[g], Ng = s_sfd[g + 1] - g0;
+            brim1[static_cast<size_t>(n) * g0 + static_cast<size_t>(q - g * n) * Ng + (srow - g0)] =
+                erow - s_epd[g * n];
         }
     }
     if (dense) {
-        for (uint64_t m = gmask; m; m &= m - 1) {
-            const int g = __ffsll(static_cast<unsigned long long>(m)) - 1;
-            const int g0 = sfd_off[g], Ng = sfd_off[g + 1] - g0;
-            const int srow = slot_of(g);
+        // the positions of a group that a token's SFD row does not use
+        for (int i = threadIdx.x; i < nt * Nd; i += blockDim.x) {
+            const int g = i / nt, tok = i - g * nt;
+            if (!((c.gm[tok] >> g) & 1ull)) continue;
+            const int g0 = s_sfd[g], Ng = s_sfd[g + 1] - g0;
+            const int srow = slot_of(tok, g);
             for (int j = 0; j < n; j++)
-                if (!has_pos(em, g * n + j))
+                if (!has_pos(c.em[tok], g * n + j))
                     brim1[static_cast<size_t>(n) * g0 + static_cast<size_t>(j) * Ng + (srow - g0)] = -1;
         }
     }
@@ -251,11 +306,11 @@ __global__ __launch_bounds__(kBrimChunk) void k_brim_fill(
 hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
                        int tile_rows, int dense_brim1, const BrimBufs &b, hipStream_t s) {
     const int nchunks = static_cast<int>(ceil_div(T, kBrimChunk));
-    k_brim_count<<<nchunks, kBrimChunk, 0, s>>>(ids, T, k, tab, b.chunk_cnt);
+    k_brim_count<<<nchunks, kBrimThreads, 0, s>>>(ids, T, k, tab, b.chunk_cnt);
     k_brim_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, tab.Nd, tab.Ne, tile_rows, b.chunk_base,
                                    b.sfd_off, b.epd_off, b.tile_off, b.first_cnt,
                                    b.tile_off_first, b.tile_off_rest);
-    k_brim_fill<<<nchunks, kBrimChunk, 0, s>>>(ids, w, T, k, tab, b.chunk_base, b.sfd_off,
+    k_brim_fill<<<nchunks, kBrimThreads, 0, s>>>(ids, w, T, k, tab, b.chunk_base, b.sfd_off,
                                                b.epd_off, b.first_cnt, dense_brim1, b.brim0,
                                                b.epd_src, b.epd_w, b.tok_epd, b.down_rows,
                                                b.brim1);

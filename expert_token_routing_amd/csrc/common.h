@@ -47,33 +47,58 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
+// Wave scans and reductions on the DPP lane network (gfx9 row shifts and row
+// broadcasts), with no LDS traffic: shifts by 1, 2, 4 and 8 inside each row
+// of 16 lanes give row-local inclusive scans, then lane 15 of each row is
+// added into the next row and lane 31 into the upper two rows.  A lane
+// whose DPP source does not exist receives the identity.  The combination
+// order is fixed, so results are deterministic.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int identity, int v) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xf, false);
 }
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float identity, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
+                                                      CTRL, ROW_MASK, 0xf, false));
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(v, o);
-        if (lane >= o) v += u;
-    }
+    v += dpp_i<kDppRowShr1, 0xf>(0, v);
+    v += dpp_i<kDppRowShr2, 0xf>(0, v);
+    v += dpp_i<kDppRowShr4, 0xf>(0, v);
+    v += dpp_i<kDppRowShr8, 0xf>(0, v);
+    v += dpp_i<kDppRowBcast15, 0xa>(0, v);
+    v += dpp_i<kDppRowBcast31, 0xc>(0, v);
     return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<kDppRowShr1, 0xf>(0.f, v);
+    v += dpp_f<kDppRowShr2, 0xf>(0.f, v);
+    v += dpp_f<kDppRowShr4, 0xf>(0.f, v);
+    v += dpp_f<kDppRowShr8, 0xf>(0.f, v);
+    v += dpp_f<kDppRowBcast15, 0xa>(0.f, v);
+    v += dpp_f<kDppRowBcast31, 0xc>(0.f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<kDppRowShr1, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppRowShr2, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppRowShr4, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppRowShr8, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppRowBcast15, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppRowBcast31, 0xc>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 // Wave-wide arg-max of (value, index): larger value wins, ties to the lower

@@ -3,11 +3,14 @@
 // expert-similarity-based.
 //
 // One 64-lane wave per token; lane l holds the logits of experts l, l+64, ...
-// Softmax max and denominator are wave reductions; the top k come from k
-// rounds of a wave arg-max on (logit, -index), so the order is (logit
-// descending, index ascending).  Softmax is monotone, so selecting on the
-// logits selects the top k probabilities.  A NaN logit ranks as -inf, so the
-// k results are always distinct experts.
+// Softmax max and denominator are wave reductions.  The top k are selected
+// without cross-lane shuffles: each logit maps to an unsigned key that keeps
+// its order, the k-th largest key is found bit by bit from wave ballots
+// (a radix select), ties at that key go to the lower expert index, and a
+// selected expert's place in the list is the number of selected experts
+// that precede it in (logit descending, index ascending) order.  Softmax is
+// monotone, so selecting on the logits selects the top k probabilities.  A
+// NaN logit ranks as -inf, so the k results are always distinct experts.
 #include "launch.h"
 
 namespace occ {
@@ -20,40 +23,73 @@ struct TokenLogits {
     float v[NI];
 };
 
-// k rounds of arg-max over the experts whose group bit is set in `allowed`.
-// Winners go to sel/sel_l (per-wave LDS, k entries).
+// Key of a logit for selection: a larger logit has a larger key, -0 and +0
+// share one key (they compare equal), and -inf maps to 0x007fffff, so every
+// logit's key is above 0, the key of experts that may not be chosen.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The k experts of largest logit among those whose group bit is set in
+// `allowed`, in (logit descending, index ascending) order, go to sel / sel_l
+// (per-wave LDS, k entries; sel_l holds the logit, NaN read as -inf).
 template <int NI>
 __device__ void select_topk(const TokenLogits<NI> &l, int Ne, int k, uint64_t allowed,
                             const uint8_t *s_grp, int *sel, float *sel_l) {
     const int lane = lane_id();
-    uint32_t taken = 0;
-    bool ok[NI];
+    float v[NI];
+    uint32_t key[NI];
 #pragma unroll
     for (int i = 0; i < NI; i++) {
         const int e = lane + kWave * i;
-        ok[i] = e < Ne && ((allowed >> s_grp[e]) & 1ull);
+        v[i] = l.v[i] == l.v[i] ? l.v[i] : -INFINITY;
+        const bool ok = e < Ne && ((allowed >> s_grp[e]) & 1ull);
+        key[i] = ok ? logit_key(v[i]) : 0u;
     }
-    float v[NI];
+    // k-th largest key: the largest t with at least k keys >= t
+    uint32_t thr = 0;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = thr | (1u << b);
+        int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NI; i++) v[i] = l.v[i] == l.v[i] ? l.v[i] : -INFINITY;
-    for (int j = 0; j < k; j++) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
+        for (int i = 0; i < NI; i++) cnt += __popcll(__ballot(key[i] >= cand));
+        if (cnt >= k) thr = cand;
+    }
+    // every key above thr, then keys equal to thr in expert order up to k
+    int need = k;
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
-            const int e = lane + kWave * i;
-            if (ok[i] && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-                bv = v[i];
-                bi = e;
-            }
-        }
-        wave_argmax(bv, bi);
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-        if (lane == 0) {
-            sel[j] = bi;
-            sel_l[j] = bv;
+    for (int i = 0; i < NI; i++) need -= __popcll(__ballot(key[i] > thr));
+    const uint64_t below = (1ull << lane) - 1ull;
+    bool take[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        const uint64_t eq = __ballot(key[i] == thr);
+        take[i] = key[i] > thr || (key[i] == thr && __popcll(eq & below) < need);
+        need -= min(need, __popcll(eq));
+    }
+    // place in the list: selected experts with a larger key, or an equal key
+    // and a lower index
+    int rank[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) rank[i] = 0;
+#pragma unroll
+    for (int i2 = 0; i2 < NI; i2++) {
+        for (uint64_t m = __ballot(take[i2]); m; m &= m - 1) {
+            const int j = __builtin_ctzll(m);
+            const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key[i2]), j));
+            const int ej = j + kWave * i2;
+#pragma unroll
+            for (int i = 0; i < NI; i++)
+                rank[i] += kj > key[i] || (kj == key[i] && ej < lane + kWave * i);
         }
     }
+#pragma unroll
+    for (int i = 0; i < NI; i++)
+        if (take[i]) {
+            sel[rank[i]] = lane + kWave * i;
+            sel_l[rank[i]] = v[i];
+        }
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -145,21 +181,22 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
     __shared__ uint8_t s_grp[kMaxNe];
     __shared__ int s_sel[kRouteWaves][kMaxK];
     __shared__ float s_sell[kRouteWaves][kMaxK];
-    for (int e = threadIdx.x; e < Ne; e += blockDim.x) s_grp[e] = tab.grp[e];
-    __syncthreads();
-
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int t = blockIdx.x * kRouteWaves + wv;
-    if (t >= T) return;
-
+    // the logits load is issued before the table fill and its barrier
     TokenLogits<NI> l;
-    float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NI; i++) {
         const int e = lane + kWave * i;
-        l.v[i] = e < Ne ? logits[static_cast<size_t>(t) * Ne + e] : -INFINITY;
-        m = fmaxf(m, l.v[i]);
+        l.v[i] = e < Ne && t < T ? logits[static_cast<size_t>(t) * Ne + e] : -INFINITY;
     }
+    for (int e = threadIdx.x; e < Ne; e += blockDim.x) s_grp[e] = tab.grp[e];
+    __syncthreads();
+    if (t >= T) return;
+
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; i++) m = fmaxf(m, l.v[i]);
     m = wave_max(m);
     float s = 0.f;
 #pragma unroll

@@ -59,6 +59,20 @@ def test_route_pruning(rule, G):
     np.testing.assert_allclose(w, w_o, rtol=W_RTOL)
 
 
+def test_route_signed_zeros_and_infinities():
+    # -0 and +0 compare equal (ties to the lower index); infinities order
+    # like any other value
+    vals = np.array([-np.inf, -1.0, -0.0, 0.0, 1.0, np.inf], dtype=np.float32)
+    for Ne, k, Nd in [(64, 8, 8), (200, 6, 8)]:
+        wl = W.Workload(f"zeros_{Ne}", 9, T=513, d=64, Ne=Ne, k=k, Nd=Nd, F=64)
+        pick = np.random.default_rng(Ne).integers(0, len(vals), (513, Ne))
+        logits = torch.from_numpy(vals[pick])
+        L = synth.contiguous_placement(wl)
+        ids, _ = gpu_route(wl, logits, L)
+        ids_o, _ = oracle.route(logits.numpy(), k, L)
+        assert np.array_equal(ids, ids_o), Ne
+
+
 def test_route_ties_and_wide_expert_counts():
     # integer-valued logits: many exact ties, broken toward the lower index
     for Ne, k, Nd in [(8, 2, 2), (64, 8, 8), (256, 8, 16), (130, 5, 10), (32, 32, 4)]:
