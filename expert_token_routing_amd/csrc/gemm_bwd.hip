@@ -297,8 +297,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
 
 // ---------------------------------------------------------------- wgrad ----
 
+constexpr int kRowsLds = 4096;  // gathered row indices of one expert kept in LDS
+
 __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    __shared__ int s_rows[kRowsLds];
     const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
     int tq, tn;
     if (!map_tile(a.n_groups * m_tiles, n_tiles, tq, tn)) return;
@@ -316,6 +319,15 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
     const uint16_t *Z = static_cast<const uint16_t *>(a.zero_row);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
     const int nk = (len + BK - 1) / BK;
+    // The K dimension is the expert's (gathered) rows: when one operand is
+    // gathered and its index list fits, it comes into LDS with one pass, so
+    // that no slice's loads wait for a global index load.
+    const int32_t *gidx = a.a_rows && !a.b_rows ? a.a_rows : (a.b_rows && !a.a_rows ? a.b_rows : nullptr);
+    const bool staged = gidx && len <= kRowsLds;
+    if (staged) {
+        for (int i = threadIdx.x; i < len; i += NT) s_rows[i] = gidx[seg + i];
+        __syncthreads();
+    }
     const int acol = a.a_col0 + grp * a.a_col_grp + mload;
     const int bcol = a.b_col0 + grp * a.b_col_grp + nload;
 
@@ -339,8 +351,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
                 const int kk = kt * BK + kmajor_row(i, w);
                 if (kk < len) {
                     const int pos = seg + kk;
-                    const int ra = a.a_rows ? a.a_rows[pos] : pos;
-                    const int rb = a.b_rows ? a.b_rows[pos] : pos;
+                    const int sr = staged ? s_rows[kk] : 0;
+                    const int ra = a.a_rows ? (staged ? sr : a.a_rows[pos]) : pos;
+                    const int rb = a.b_rows ? (staged ? sr : a.b_rows[pos]) : pos;
                     arow[i] = A + static_cast<size_t>(ra) * a.lda + acol;
                     brow[i] = B + static_cast<size_t>(rb) * a.ldb + bcol;
                 } else {
