@@ -141,6 +141,18 @@ def test_forward_edge_shapes(shape):
     check_forward(wl32, inp=synth.make_all(wl32))
 
 
+@pytest.mark.parametrize("shape", [
+    # the largest expert count, group count and top-k the library takes
+    dict(T=100, d=256, Ne=256, Nd=64, k=32, F=64),
+    # the widest bf16 hidden size (several 256-column tiles of d, 128 K slices)
+    dict(T=70, d=8192, Ne=8, Nd=4, k=2, F=128),
+], ids=["Ne256_Nd64_k32", "d8192"])
+def test_forward_maximum_sizes(shape):
+    wl = W.Workload("max_" + "_".join(f"{k}{v}" for k, v in shape.items()), 17, n_c=2,
+                    bonus=1.0, **shape)
+    check_forward(wl, inp=synth.make_all(wl))
+
+
 def test_forward_with_starved_expert_and_group():
     wl = W.Workload("starved_fwd", 16, T=600, d=128, Ne=16, k=2, Nd=4, F=128, n_c=2)
     inp = synth.make_all(wl)
