@@ -155,6 +155,13 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int m_tiles = a.tile_off[a.Ne], n_tiles = (a.N + BN - 1) / BN;
     if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
     const int p = find_pos(a.tile_off, a.Ne, tm);
+    if (a.phase != 2) {
+        // column tiles outermost inside each expert, as in the forward GEMMs
+        const int r = a.tile_off[p + 1] - a.tile_off[p];
+        const int local = (tm - a.tile_off[p]) * n_tiles + tn;
+        tn = local / r;
+        tm = a.tile_off[p] + local % r;
+    }
     const int seg0 = a.seg_off[p], len = a.seg_off[p + 1] - seg0;
     const int nf = a.phase ? a.first_cnt[p] : 0;
     const int seg = a.phase == 2 ? seg0 + nf : seg0;
