@@ -379,8 +379,13 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
     OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
     OCC_TRY(mark(2));
+    // Small batches (the same rule as the 64-row tiles) merge in one
+    // down-projection launch of atomic adds, whose SFD accumulator rows the
+    // dispatch zeroes as it writes the same rows of x_sfd.
+    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
     // Algorithm 4: ORI -> SFD
-    OCC_HIP(launch_dispatch(x, D.T, D.Nd, static_cast<size_t>(D.d) * es, bb.brim0, x_sfd, s));
+    OCC_HIP(launch_dispatch(x, D.T, D.Nd, static_cast<size_t>(D.d) * es, bb.brim0, x_sfd, s,
+                            one_launch ? sfd_out : nullptr, D.d));
     OCC_TRY(mark(3));
     // shared experts: dense SwiGLU over all T tokens, fp32 result
     if (D.n_shared > 0) {
@@ -429,11 +434,9 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     OCC_TRY(mark(5));
     // Algorithm 8: EPD -> SFD, summed inside each group in fp32.  The first
     // contributor to every SFD row stores (so no zero-fill is needed), then
-    // the other rows of the group add with atomics.  Small batches (the same
-    // rule as the 64-row tiles) are bound by reading the weights, which the
-    // two launches would read twice: there the SFD rows are zeroed and one
-    // launch adds every row.
-    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
+    // the other rows of the group add with atomics.  Small batches are bound
+    // by reading the weights, which the two launches would read twice: there
+    // the SFD rows were zeroed by the dispatch and one launch adds every row.
     DownArgs dn{};
     dn.A = epd;
     dn.W = w_down;
@@ -449,8 +452,6 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     dn.k_split = D.F;
     dn.tab = tab;
     if (one_launch) {
-        const size_t nsfd_max = static_cast<size_t>(D.T) * std::min(D.k, D.Nd);
-        OCC_HIP(launch_fill_i32(reinterpret_cast<int32_t *>(sfd_out), nsfd_max * D.d, 0, s));
         dn.phase = 0;
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
@@ -564,8 +565,10 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     OCC_HIP(launch_fill_i32(static_cast<int32_t *>(zero_row), zero_elems * es / 4, 0, s));
     OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdTile, bt_all, bt_first, bt_rest,
                               s));
-    // dy ORI -> SFD: the combine's transpose copies dy into each replica
-    OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s));
+    // dy ORI -> SFD: the combine's transpose copies dy into each replica (and
+    // zeroes the dx accumulator rows when the merge is one launch of adds)
+    OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s,
+                            one_launch ? dx_sfd : nullptr, D.d));
     OCC_TRY(mark(1));
     // dh = dy W_d for every EPD row (its SFD row's gradient, BRIM_1), then
     // the SwiGLU and modulation backward
@@ -612,8 +615,6 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     g2.epilogue = BWD_EPI_MERGE;
     g2.tab = tab;
     if (one_launch) {
-        const size_t nsfd_max = T * std::min(D.k, D.Nd);
-        OCC_HIP(launch_fill_i32(reinterpret_cast<int32_t *>(dx_sfd), nsfd_max * d, 0, s));
         g2.phase = 0;
         g2.tile_off = bt_all;
         g2.merge_store = 0;

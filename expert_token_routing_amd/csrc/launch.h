@@ -41,9 +41,11 @@ hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const P
                        int tile_rows, int dense_brim1, const BrimBufs &b, hipStream_t s);
 
 // --- row movers (rows.hip) ---
-// x_sfd[brim0[g, t]] = x[t] for every group the token uses.
+// x_sfd[brim0[g, t]] = x[t] for every group the token uses; with zero_out,
+// also zero_out[brim0[g, t]][0 .. zero_cols) = 0 (fp32, zero_cols % 4 == 0).
 hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
-                           void *x_sfd, hipStream_t s);
+                           void *x_sfd, hipStream_t s, float *zero_out = nullptr,
+                           int zero_cols = 0);
 // y[t] = dtype( sum over g of sfd_out[brim0[g, t]] (+ y_sh[t]) ), fp32 sums in
 // ascending group order.
 hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const float *y_sh, int T,

@@ -1,6 +1,8 @@
 // Memory-bound row movers of the Occult pipeline (paper, appendix A.2):
 //   dispatch  ORI -> SFD (Algorithm 4): each token row is read once and
-//             written once per group it uses, at BRIM_0[g, t];
+//             written once per group it uses, at BRIM_0[g, t]; optionally
+//             the same rows of an fp32 buffer are zeroed on the way (the
+//             accumulator of a merge done entirely with atomic adds);
 //   combine   SFD -> ORI (Algorithm 9): y[t] = sum over g of
 //             sfd_out[BRIM_0[g, t]], entries -1 skipped, summed in fp32 in
 //             ascending group order, plus the shared experts' fp32 output,
@@ -21,7 +23,9 @@ template <int VPL>
 __global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const u32x4 *__restrict__ x, int T,
                                                                int Nd, int row_vec,
                                                                const int32_t *__restrict__ brim0,
-                                                               u32x4 *__restrict__ x_sfd) {
+                                                               u32x4 *__restrict__ x_sfd,
+                                                               f32x4 *__restrict__ zero_out,
+                                                               int zero_vec) {
     const int lane = lane_id();
     const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
     if (t >= T) return;
@@ -40,6 +44,9 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_dispatch(const u32x4 *__re
             const int c = lane + kWave * i;
             if (c < row_vec) x_sfd[static_cast<size_t>(r) * row_vec + c] = v[i];
         }
+        if (zero_out)
+            for (int c = lane; c < zero_vec; c += kWave)
+                zero_out[static_cast<size_t>(r) * zero_vec + c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -131,17 +138,19 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
 }  // namespace
 
 hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
-                           void *x_sfd, hipStream_t s) {
+                           void *x_sfd, hipStream_t s, float *zero_out, int zero_cols) {
     const int row_vec = static_cast<int>(row_bytes / 16);
     const int vpl = (row_vec + kWave - 1) / kWave;
     const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
     const u32x4 *xs = static_cast<const u32x4 *>(x);
     u32x4 *xd = static_cast<u32x4 *>(x_sfd);
-    if (vpl <= 1) k_dispatch<1><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
-    else if (vpl <= 2) k_dispatch<2><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
-    else if (vpl <= 4) k_dispatch<4><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
-    else if (vpl <= 8) k_dispatch<8><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
-    else k_dispatch<16><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd);
+    f32x4 *zo = reinterpret_cast<f32x4 *>(zero_out);
+    const int zv = zero_cols / 4;
+    if (vpl <= 1) k_dispatch<1><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd, zo, zv);
+    else if (vpl <= 2) k_dispatch<2><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd, zo, zv);
+    else if (vpl <= 4) k_dispatch<4><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd, zo, zv);
+    else if (vpl <= 8) k_dispatch<8><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd, zo, zv);
+    else k_dispatch<16><<<grid, block, 0, s>>>(xs, T, Nd, row_vec, brim0, xd, zo, zv);
     return hipGetLastError();
 }
 
