@@ -81,19 +81,12 @@ constexpr int ROWS_PER_PASS = NT / CHUNKS;  // rows one pass of the workgroup mo
 constexpr int A_LD = BM / ROWS_PER_PASS;
 constexpr int B_LD = BN / ROWS_PER_PASS;
 constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per LDS buffer
-#ifndef OCC_GEMM_DMA
-#define OCC_GEMM_DMA 1
-#endif
-#if OCC_GEMM_DMA
 #ifndef OCC_GEMM_NSTAGE
 #define OCC_GEMM_NSTAGE 2
 #endif
 constexpr int NSTAGE = OCC_GEMM_NSTAGE;  // LDS ring filled by direct global->LDS loads
 static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth");
 static_assert(BK == 32 || BK == 64, "a wave load moves 1 KB: 16 rows of 64 bytes or 8 of 128");
-#else
-constexpr int NSTAGE = 2;
-#endif
 constexpr int OUT_PITCH = 128 + 8;       // up epilogue staging row (elements)
 static_assert(NSTAGE * STAGE * 2 * OCC_GEMM_WG_PER_CU <= 160 * 1024, "LDS");
 static_assert(BM * OUT_PITCH <= NSTAGE * STAGE, "epilogue staging fits in the K buffers");
@@ -108,13 +101,12 @@ __device__ __forceinline__ int swz_key(int row) { return row >> 1; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (swz_key(row) & (BK / 8 - 1))) << 3); }
 
 // The K chunk of tile row `row` that this thread fetches.  Thread t moves
-// rows (t / CHUNKS) + i * ROWS_PER_PASS, i.e. wave w owns 16-row groups; with
-// register staging it fetches logical chunk t % CHUNKS and stores it at its
-// swizzled slot; the direct loads write LDS slot t % CHUNKS, so they fetch
-// the logical chunk that belongs there.
+// rows (t / CHUNKS) + i * ROWS_PER_PASS, i.e. wave w owns 16-row groups; the
+// direct loads write LDS slot t % CHUNKS of the row, so the thread fetches
+// the logical chunk that the swizzle puts in that slot.
 __device__ __forceinline__ int fetch_chunk(int row) {
     const int c = threadIdx.x % CHUNKS;
-    return OCC_GEMM_DMA ? (c ^ (swz_key(row) & (CHUNKS - 1))) : c;
+    return c ^ (swz_key(row) & (CHUNKS - 1));
 }
 
 // Workgroup -> (row tile, column tile).  Returns false when there is no tile.
@@ -218,7 +210,6 @@ __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB
     }
 }
 
-#if OCC_GEMM_DMA
 // Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).  m0 must be
 // wave-uniform.  Issued as inline assembly because the compiler's builtin
@@ -281,58 +272,6 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
     }
     __syncthreads();
 }
-#else
-// K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
-// rows at k = 0 (chunk offset included).  B is laid out as blocks of
-// ksp-wide K ranges, blk elements apart (the shared experts' down weights);
-// a single block (ksp = K) is the plain case.  The staging registers are
-// plain arrays indexed with constants only, so they stay in VGPRs.
-__device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
-                                       const uint16_t *const (&b_src)[B_LD], int K, int ksp,
-                                       size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
-                                       f32x4_t (&acc)[MI][NI]) {
-    const int tid = threadIdx.x, chunk = tid % CHUNKS, r0 = tid / CHUNKS;
-    u32x4 ra[A_LD], rb[B_LD];
-    const int nk = K / BK;
-#pragma unroll
-    for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i]);
-#pragma unroll
-    for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i]);
-    {
-        uint16_t *sA = smem, *sB = smem + BM * BK;
-#pragma unroll
-        for (int i = 0; i < A_LD; i++)
-            *reinterpret_cast<u32x4 *>(sA + swz(r0 + i * ROWS_PER_PASS, chunk)) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_LD; i++)
-            *reinterpret_cast<u32x4 *>(sB + swz(r0 + i * ROWS_PER_PASS, chunk)) = rb[i];
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int k0 = (kt + 1) * BK;
-            const size_t bo = static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp);
-#pragma unroll
-            for (int i = 0; i < A_LD; i++) ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + k0);
-#pragma unroll
-            for (int i = 0; i < B_LD; i++) rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + bo);
-        }
-        mma_slice(smem + cur * STAGE, smem + cur * STAGE + BM * BK, wm, brow, acc);
-        if (more) {
-            uint16_t *sA = smem + (cur ^ 1) * STAGE, *sB = sA + BM * BK;
-#pragma unroll
-            for (int i = 0; i < A_LD; i++)
-                *reinterpret_cast<u32x4 *>(sA + swz(r0 + i * ROWS_PER_PASS, chunk)) = ra[i];
-#pragma unroll
-            for (int i = 0; i < B_LD; i++)
-                *reinterpret_cast<u32x4 *>(sB + swz(r0 + i * ROWS_PER_PASS, chunk)) = rb[i];
-        }
-        __syncthreads();
-    }
-}
-#endif
 
 // Second bound: waves per SIMD = workgroups per CU x NT / 256.
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k_gemm_up)(UpArgs a) {
