@@ -71,15 +71,46 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
-// MFMA fragment (8 consecutive k of column c0 + (lane & 15), k chunk lane >> 4
-// of the 32-deep step at kb) from a K-major tile, by two transpose reads.
-__device__ __forceinline__ bf16x8_t kmaj_frag(const uint16_t *tile, int kb, int c0) {
+// Addresses of K-major fragments with few live registers.  For a wave whose
+// columns start at cw (a multiple of 16 whose chunk bits do not meet those of
+// 16 f) and fragment f at cw + 16 f, kmaj(k, cw + 16 f + 4 b) equals
+// P(k) + (X(k) ^ 16 f) with P(k) = k BM + 8 (b >> 1) + (4 b mod 8) and
+// X(k) = 8 ((cw / 8) xor key(k)): the swizzle only touches chunk bits 1-3, the
+// fragment index only chunk bits 1-3 above the wave's base, and b >> 1 is
+// chunk bit 0.  A lane keeps P and X for its four rows (two per 32-deep step).
+struct KmajAddr {
+    int P[2][2], X[2][2];  // [step ks][row k1 or k1 + 4]
+};
+__device__ __forceinline__ void kmaj_addr(int cw, KmajAddr &o) {
     const int l = lane_id(), G = l >> 4, a = (l >> 2) & 3, b = l & 3;
-    const int k1 = kb + 8 * G + a, col = c0 + 4 * b;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tile + kmaj(k1, col)));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(tile + kmaj(k1 + 4, col)));
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int k = 32 * ks + 8 * G + a + 4 * h;
+            o.P[ks][h] = k * BM + 8 * (b >> 1) + ((4 * b) & 7);
+            o.X[ks][h] = 8 * ((cw >> 3) ^ kkey(k));
+        }
+}
+// MFMA fragment f (8 consecutive k of column cw + 16 f + (lane & 15), k chunk
+// lane >> 4 of 32-deep step ks) from a K-major tile, by two transpose reads.
+__device__ __forceinline__ bf16x8_t kmaj_frag(const uint16_t *tile, const KmajAddr &ad, int ks,
+                                              int f) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + ad.P[ks][0] + (ad.X[ks][0] ^ (16 * f))));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + ad.P[ks][1] + (ad.X[ks][1] ^ (16 * f))));
     const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, v);
+}
+// Marks X as changed each iteration, so that the compiler keeps four values
+// per operand instead of hoisting one precomputed address per fragment out
+// of the K loop (which spilled the weight-gradient kernel at 256 VGPRs).
+__device__ __forceinline__ void launder(KmajAddr &ad) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) asm volatile("" : "+v"(ad.X[ks][h]));
 }
 
 // MFMA fragment from a K-contiguous tile: row r, chunk (ks * 4 + lane >> 4).
@@ -195,6 +226,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int nk = a.K / BK;
 
     const int wm = w >> 1, wn = w & 1;
+    KmajAddr adB;
+    kmaj_addr(wn * WN, adB);
     f32x4 acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
@@ -206,6 +239,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             wait_all_loads();
             __syncthreads();
         }
+        launder(adB);
         if (kt < nk) {
             const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
             const int k0 = kt * BK;
@@ -229,7 +263,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
 #pragma unroll
             for (int mi = 0; mi < MI; mi++) fa[mi] = rows_frag(sA, wm * WM + mi * 16 + (l & 15), ks);
 #pragma unroll
-            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
+            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, adB, ks, ni);
             mfma_tile<EPI == BWD_EPI_SWIGLU>(fa, fb, acc);
         }
     }
@@ -339,6 +373,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
     const int bcol = a.b_col0 + grp * a.b_col_grp + nload;
 
     const int wm = w >> 1, wn = w & 1;
+    KmajAddr adA, adB;
+    kmaj_addr(wm * WM, adA);
+    kmaj_addr(wn * WN, adB);
     f32x4 acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
@@ -350,6 +387,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
             wait_all_loads();
             __syncthreads();
         }
+        launder(adA);
+        launder(adB);
         if (kt < nk) {
             const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
             const uint16_t *arow[4], *brow[4];
@@ -377,9 +416,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
         for (int ks = 0; ks < BK / 32; ks++) {
             bf16x8_t fa[MI], fb[NI];
 #pragma unroll
-            for (int mi = 0; mi < MI; mi++) fa[mi] = kmaj_frag(sA, 32 * ks, wm * WM + mi * 16);
+            for (int mi = 0; mi < MI; mi++) fa[mi] = kmaj_frag(sA, adA, ks, mi);
 #pragma unroll
-            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, 32 * ks, wn * WN + ni * 16);
+            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, adB, ks, ni);
             mfma_tile<true>(fa, fb, acc);
         }
     }
