@@ -8,8 +8,9 @@ the rescheduled one (Algorithm 1 on the batch's co-activation counts, built
 with the library's own calls, untimed); the contiguous placement is timed
 too and reported beside it.  `value` is the rate of the step replayed from a
 HIP graph (the launches captured once); the eager rate, with HIP events
-between the stages, is reported beside it.  A training step (forward that
-keeps the backward's state, then the backward pass) is timed as well.
+between the stages, is reported beside it.  The deterministic merge (no
+atomic adds) and a training step (forward that keeps the backward's state,
+then the backward pass) are timed as well.
 
 Prints one JSON line.  The roofline entry is for the dominant kernel (the
 SwiGLU up-projection GEMM): algorithmic FLOPs per launch over its average
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--no-det", action="store_true",
+                    help="skip the deterministic-merge forward")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training step (forward with saved state + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -75,6 +78,7 @@ def main():
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     desc = occ.desc_of(wl)
     ws = occ.alloc_workspace(desc, dev)
+    desc_main, ws_main = desc, ws
     dt = synth.torch_dtype(wl)
     y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
@@ -124,7 +128,8 @@ def main():
     r_ids = torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev)
     r_w = torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev)
 
-    def run(L, steps, events=None, route_events=None):
+    def run(L, steps, events=None, route_events=None, mode=None):
+        desc, ws = mode or (desc_main, ws_main)
         for i in range(steps):
             ev = events[i].handles if events is not None else None
             if wl.gated:
@@ -147,9 +152,9 @@ def main():
                                        g["w_down"], g["ws_gate"], g["ws_up"], g["ws_down"], y,
                                        ws, stage_events=ev)
 
-    def timed(L, label):
+    def timed(L, label, mode=None):
         log(f"[bench] {label}: warmup {args.warmup}")
-        run(L, args.warmup)
+        run(L, args.warmup, mode=mode)
         torch.cuda.synchronize()
         events = [occ.StageEvents() for _ in range(args.steps)]
         rev = None
@@ -160,7 +165,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record(stream)
-        run(L, args.steps, events, rev)
+        run(L, args.steps, events, rev, mode=mode)
         stop.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -176,17 +181,17 @@ def main():
         log(f"[bench] {label}: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
         return ms, st
 
-    def graph_timed(L, label):
+    def graph_timed(L, label, mode=None):
         """One step captured in a HIP graph (no stage events), replayed."""
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            run(L, 1)
+            run(L, 1, mode=mode)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            run(L, 1)
+            run(L, 1, mode=mode)
         for _ in range(args.warmup):
             g.replay()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -206,6 +211,17 @@ def main():
     # runs it; the eager rate is reported beside it
     ms = ms_graph if ms_graph is not None else ms_eager
     tokens_per_s = wl.T / (ms / 1e3)
+    res_det = None
+    if not args.no_det and not sim and not wl.gated:
+        # the deterministic merge (no atomic adds): same layer, same placement
+        desc_det = occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC)
+        mode_det = (desc_det, occ.alloc_workspace(desc_det, dev))
+        ms_d, stages_d = timed(L_alg1, "deterministic merge", mode=mode_det)
+        ms_dg = None if args.no_graph else graph_timed(L_alg1, "deterministic merge", mode=mode_det)
+        stages_d["gemm_down"] = stages_d.pop("gemm_down_first")
+        stages_d["merge"] = stages_d.pop("gemm_down_rest")
+        res_det = {"value": wl.T / ((ms_dg or ms_d) / 1e3), "ms_per_step": ms_dg or ms_d,
+                   "eager_ms_per_step": ms_d, "stages_ms": stages_d}
     res_contig = None
     if not args.no_contiguous:
         ms_c, stages_c = timed(L_contig, "contiguous placement")
@@ -269,6 +285,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "stages_ms": {s: round(v, 5) for s, v in stages.items()},
         "contiguous": res_contig,
+        "deterministic": res_det,
     }
     if train is not None:
         out["train"] = train

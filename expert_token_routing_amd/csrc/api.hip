@@ -39,7 +39,7 @@ int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
 struct Layout {
     size_t logits, ids, w, brim0, sfd_off, epd_off, tile_off, tile_off_first, tile_off_rest, first_cnt,
         chunk_cnt, chunk_base, epd_src, epd_w, tok_epd, down_rows, brim1, brim_end, x_sfd, epd,
-        sfd_out, h_sh, y_sh;
+        sfd_out, h_sh, y_sh, y_epd;
     // training only (flags & OCC_FLAG_TRAIN): saved pre-activations and the
     // backward pass's buffers
     size_t gu, gu_sh, dy_sfd, dgu, dx_sfd, dw_part, zero_row, bt_all, bt_first, bt_rest, dgu_sh,
@@ -82,6 +82,9 @@ Layout layout(const occ_layer_desc &D) {
     L.x_sfd = take(nsfd_max * d * es);
     L.epd = take(nepd * F * es);
     L.sfd_out = take(nsfd_max * d * 4);
+    // deterministic merge: every EPD row's fp32 result (the backward reuses
+    // it for dx)
+    if (D.flags & OCC_FLAG_DETERMINISTIC) L.y_epd = take(nepd * d * 4);
     const size_t Nsh = static_cast<size_t>(D.n_shared) * D.F_shared;
     if (D.n_shared > 0) {
         L.h_sh = take(T * Nsh * es);
@@ -123,7 +126,7 @@ occ_status check_desc(const occ_layer_desc *D) {
         (D->prune_groups < 1 ||
          static_cast<int64_t>(D->prune_groups) * (D->Ne / D->Nd) < D->k))
         return OCC_ERR_INVALID_ARG;
-    if (D->flags & ~OCC_FLAG_TRAIN) return OCC_ERR_INVALID_ARG;
+    if (D->flags & ~(OCC_FLAG_TRAIN | OCC_FLAG_DETERMINISTIC)) return OCC_ERR_INVALID_ARG;
     // training keeps bf16 pre-activations for the bf16 backward GEMMs, whose
     // 256-wide tiles need d, F (and F_shared) of at least 256
     if ((D->flags & OCC_FLAG_TRAIN) &&
@@ -382,7 +385,8 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     // Small batches (the same rule as the 64-row tiles) merge in one
     // down-projection launch of atomic adds, whose SFD accumulator rows the
     // dispatch zeroes as it writes the same rows of x_sfd.
-    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
+    const bool det = D.flags & OCC_FLAG_DETERMINISTIC;
+    const bool one_launch = !det && static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
     // Algorithm 4: ORI -> SFD
     OCC_HIP(launch_dispatch(x, D.T, D.Nd, static_cast<size_t>(D.d) * es, bb.brim0, x_sfd, s,
                             one_launch ? sfd_out : nullptr, D.d));
@@ -451,7 +455,20 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     dn.Ne = D.Ne;
     dn.k_split = D.F;
     dn.tab = tab;
-    if (one_launch) {
+    if (det) {
+        // every EPD row stores its own fp32 result; the merge then sums each
+        // SFD row's contributions in slot order
+        float *y_epd = at<float>(workspace, L.y_epd);
+        dn.rows = nullptr;
+        dn.dst_rows = nullptr;
+        dn.out = y_epd;
+        dn.phase = 0;
+        dn.tile_off = bb.tile_off;
+        OCC_HIP(ops.down(dn, routed_tiles, s));
+        OCC_TRY(mark(6));
+        OCC_HIP(launch_merge_slots(y_epd, ids, bb.tok_epd, bb.brim0, tab, D.T, D.k, D.d, sfd_out,
+                                   s));
+    } else if (one_launch) {
         dn.phase = 0;
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
@@ -557,7 +574,8 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     int32_t *bt_rest = at<int32_t>(workspace, L.bt_rest);
     float *dx_sh = D.n_shared > 0 ? at<float>(workspace, L.dx_sh) : nullptr;
     const size_t routed_tiles = (T * D.k + kBwdTile - 1) / kBwdTile + D.Ne;
-    const bool one_launch = static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
+    const bool det = D.flags & OCC_FLAG_DETERMINISTIC;
+    const bool one_launch = !det && static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
 
     OCC_TRY(mark(0));
     // schedules for 256-row tiles, a zero row for the tails of K-major operands
@@ -614,7 +632,19 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     g2.Ne = D.Ne;
     g2.epilogue = BWD_EPI_MERGE;
     g2.tab = tab;
-    if (one_launch) {
+    if (det) {
+        // each EPD row's fp32 dx stored at that row, then summed per SFD row
+        // in slot order
+        float *dx_epd = at<float>(workspace, L.y_epd);
+        g2.dst_rows = nullptr;
+        g2.merge_out = dx_epd;
+        g2.phase = 0;
+        g2.tile_off = bt_all;
+        g2.merge_store = 1;
+        OCC_HIP(launch_bwd_dgrad(g2, routed_tiles, s));
+        OCC_HIP(launch_merge_slots(dx_epd, at<int32_t>(workspace, L.ids), bb.tok_epd, bb.brim0,
+                                   tab, D.T, D.k, D.d, dx_sfd, s));
+    } else if (one_launch) {
         g2.phase = 0;
         g2.tile_off = bt_all;
         g2.merge_store = 0;

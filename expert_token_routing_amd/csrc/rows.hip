@@ -3,6 +3,9 @@
 //             written once per group it uses, at BRIM_0[g, t]; optionally
 //             the same rows of an fp32 buffer are zeroed on the way (the
 //             accumulator of a merge done entirely with atomic adds);
+//   merge     the deterministic stage one of Algorithm 8: sfd_out[BRIM_0[g,
+//             t]] = sum, in ascending placement position, of the fp32 results
+//             y_epd of the token's EPD rows in group g (no atomics);
 //   combine   SFD -> ORI (Algorithm 9): y[t] = sum over g of
 //             sfd_out[BRIM_0[g, t]], entries -1 skipped, summed in fp32 in
 //             ascending group order, plus the shared experts' fp32 output,
@@ -135,7 +138,77 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
     }
 }
 
+// One wave per token.  Lane j < k holds the token's j-th expert: placement
+// position p_j, group g_j, EPD row erow_j.  Its rank among the token's
+// positions orders the walk; a group's positions are contiguous, so the walk
+// visits each group's experts together, in slot order, and a change of group
+// flushes the running fp32 sum to that group's SFD row.
+template <int VPL>
+__global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
+    const f32x4 *__restrict__ y_epd, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ tok_epd, const int32_t *__restrict__ brim0, PlaceTab tab, int T,
+    int k, int row_vec4, f32x4 *__restrict__ sfd_out) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    if (t >= T) return;
+    int p = 0x7fffffff, erow = 0;
+    if (lane < k) {
+        const size_t o = static_cast<size_t>(t) * k + lane;
+        const int e = ids[o];
+        p = tab.grp[e] * tab.n + tab.slot[e];
+        erow = tok_epd[o];
+    }
+    int rank = 0;  // positions are distinct: the token's experts are
+    for (int j = 0; j < k; j++) rank += __shfl(p, j) < p;
+    f32x4 acc[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int cur_g = -1;
+    auto flush = [&](int g) {
+        const int r = brim0[static_cast<size_t>(g) * T + t];
+        f32x4 *dst = sfd_out + static_cast<size_t>(r) * row_vec4;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane + kWave * i;
+            if (c < row_vec4) dst[c] = acc[i];
+            acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    for (int r = 0; r < k; r++) {
+        const int src = __builtin_ctzll(__ballot(lane < k && rank == r));
+        const int pr = __shfl(p, src), er = __shfl(erow, src);
+        const int g = pr / tab.n;
+        if (g != cur_g) {
+            if (cur_g >= 0) flush(cur_g);
+            cur_g = g;
+        }
+        const f32x4 *row = y_epd + static_cast<size_t>(er) * row_vec4;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) acc[i] += row[min(lane + kWave * i, row_vec4 - 1)];
+    }
+    if (cur_g >= 0) flush(cur_g);
+}
+
 }  // namespace
+
+hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int32_t *tok_epd,
+                              const int32_t *brim0, const PlaceTab &tab, int T, int k, int d,
+                              float *sfd_out, hipStream_t s) {
+    const int row_vec4 = d / 4;
+    const int vpl = (row_vec4 + kWave - 1) / kWave;
+    const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
+    const f32x4 *ye = reinterpret_cast<const f32x4 *>(y_epd);
+    f32x4 *so = reinterpret_cast<f32x4 *>(sfd_out);
+#define OCC_MERGE(V) k_merge_slots<V><<<grid, block, 0, s>>>(ye, ids, tok_epd, brim0, tab, T, k, row_vec4, so)
+    if (vpl <= 1) OCC_MERGE(1);
+    else if (vpl <= 2) OCC_MERGE(2);
+    else if (vpl <= 4) OCC_MERGE(4);
+    else if (vpl <= 8) OCC_MERGE(8);
+    else if (vpl <= 16) OCC_MERGE(16);
+    else OCC_MERGE(32);
+#undef OCC_MERGE
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
                            void *x_sfd, hipStream_t s, float *zero_out, int zero_cols) {

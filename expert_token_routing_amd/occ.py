@@ -24,6 +24,7 @@ OCC_OK, OCC_ERR_INVALID_ARG, OCC_ERR_UNSUPPORTED, OCC_ERR_WORKSPACE, OCC_ERR_HIP
 OCC_F32, OCC_BF16 = 0, 1
 OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM, OCC_PRUNE_SIMILARITY = 0, 1, 2, 3
 OCC_FLAG_TRAIN = 1
+OCC_FLAG_DETERMINISTIC = 2
 BSTAGES = ["dispatch", "dgrad_down", "dgrad_up", "shared", "combine", "wgrad_down", "wgrad_up",
            "route"]
 OCC_BSTAGE_COUNT = len(BSTAGES)

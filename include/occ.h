@@ -75,6 +75,15 @@ typedef enum occ_prune_rule {
  * 256 when there are shared experts): OCC_ERR_UNSUPPORTED otherwise. */
 #define OCC_FLAG_TRAIN 1
 
+/* Deterministic merge (paper appendix A.2, Algorithm 8, and its remark that
+ * the stage-one results may equally be summed serially over the local
+ * experts): the down-projection stores every EPD row's fp32 result, then each
+ * SFD row is the sum of its contributions in ascending placement position
+ * (slot order inside the group), with no atomic adds.  Every output (y, and
+ * with OCC_FLAG_TRAIN every gradient) is then bitwise identical from run to
+ * run.  The workspace grows by T*k*d fp32. */
+#define OCC_FLAG_DETERMINISTIC 2
+
 /* Shape of one MoE layer.  Limits of this build:
  *   1 <= T, T*k < 2^31;  1 <= Ne <= 256;  1 <= k <= min(Ne, 32);
  *   1 <= Nd <= 64 and Nd divides Ne (n = Ne/Nd experts per group);
@@ -93,7 +102,7 @@ typedef struct occ_layer_desc {
     int32_t prune_rule;   /* occ_prune_rule */
     int32_t prune_groups; /* groups a token may use when pruning */
     int32_t dtype;        /* occ_dtype of x, weights and y */
-    int32_t flags;        /* 0, or OCC_FLAG_TRAIN */
+    int32_t flags;        /* 0, or OCC_FLAG_TRAIN | OCC_FLAG_DETERMINISTIC */
 } occ_layer_desc;
 
 /* Index structures of the paper's appendix A.2, as left in the workspace by

@@ -68,7 +68,8 @@ def _ws(desc):
     (dict(prune_rule=3, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=1, prune_groups=0), occ.OCC_ERR_INVALID_ARG),
     (dict(prune_rule=2, prune_groups=1, k=9), occ.OCC_ERR_INVALID_ARG),  # 1 group of 8 < k
-    (dict(flags=2), occ.OCC_ERR_INVALID_ARG),
+    (dict(flags=4), occ.OCC_ERR_INVALID_ARG),
+    (dict(flags=6), occ.OCC_ERR_INVALID_ARG),
     (dict(flags=1, dtype=0), occ.OCC_ERR_UNSUPPORTED),  # training is bf16 only
     (dict(flags=1, F=192), occ.OCC_ERR_UNSUPPORTED),    # backward tiles need F >= 256
     (dict(n_shared=1, F_shared=0), occ.OCC_ERR_INVALID_ARG),
@@ -93,6 +94,20 @@ def test_workspace_size_covers_the_worst_case(L):
         floor = nsfd_max * wl.d * (es + 4) + wl.T * wl.k * wl.F * es
         assert n >= floor
         assert n < 300 * 2**30
+
+
+def test_deterministic_flag_adds_the_epd_result_buffer(L):
+    """OCC_FLAG_DETERMINISTIC is valid alone and with training, and grows the
+    workspace by the fp32 per-EPD-row results (T*k*d*4 bytes, plus at most
+    one alignment pad)."""
+    for wl in (W.OLMOE, W.DEEPSEEK, W.TINY_F32):
+        rc0, n0 = _ws(occ.desc_of(wl))
+        rc1, n1 = _ws(occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC))
+        assert rc0 == rc1 == occ.OCC_OK
+        extra = wl.T * wl.k * wl.d * 4
+        assert extra <= n1 - n0 <= extra + 4096
+    rc, _ = _ws(occ.desc_of(W.OLMOE, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC))
+    assert rc == occ.OCC_OK
 
 
 def _null():
