@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec at 1 GPU + % of bf16 MFMA / HBM roofline; CT"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3  # fp32 vector / MFMA
 
 
 def parse():
@@ -259,6 +260,39 @@ def main():
     roofline.update({"traffic": traffic, "kernel": up_kernel, "avg_ms": round(up_ms, 5),
                      "flops_per_launch": flops_up, "bytes_per_launch": bytes_up})
 
+    # --- every stage against its own bound, t_roof = max(flops / peak, bytes /
+    # HBM peak), with the algorithmic work of each step (x, weights and
+    # outputs moved once; the fp32 stage-one rows written once)
+    peak_f = (PEAK_BF16_TFLOPS if es == 2 else PEAK_F32_TFLOPS) * 1e12
+    T, d, k, F = wl.T, wl.d, wl.k, wl.F
+
+    def bound(ms_stage, flops, nbytes):
+        t_f, t_b = flops / peak_f, nbytes / (PEAK_HBM_GBS * 1e9)
+        t = max(t_f, t_b)
+        return {"ms": round(ms_stage, 5), "bound": "mfma" if t_f >= t_b else "hbm",
+                "roof_ms": round(t * 1e3, 5), "frac": round(t * 1e3 / ms_stage, 4)}
+
+    down_ms = stages.get("gemm_down_first", 0.0) + stages.get("gemm_down_rest", 0.0)
+    stage_roof = {
+        "route": bound(stages.get("route", stages.get("route_copy", 0.0)) or 1e-9, 0.0,
+                       T * (4 * wl.Ne + 8 * k)),
+        "dispatch": bound(stages["dispatch"], 0.0, (T + nsfd_alg1) * d * es),
+        "gemm_up": bound(up_ms, flops_up, bytes_up),
+        "gemm_down": bound(down_ms, 2.0 * T * k * F * d,
+                           active * d * F * es + T * k * F * es + nsfd_alg1 * d * 4),
+        "combine": bound(stages["combine"], 0.0,
+                         nsfd_alg1 * d * 4 + T * d * es + (T * d * 4 if wl.n_shared else 0)),
+    }
+    if wl.n_shared:
+        fs = wl.n_shared * wl.F_shared
+        stage_roof["shared"] = bound(stages["shared"], 2.0 * T * d * 3 * fs,
+                                     3 * fs * d * es + T * d * (es + 4))
+    roof_sum = sum(v["roof_ms"] for v in stage_roof.values())
+    stage_roof["layer"] = {"ms": round(ms, 5), "roof_ms": round(roof_sum, 5),
+                           "frac": round(roof_sum / ms, 4),
+                           "note": "sum of the stages' roofline times over the step time; "
+                                   "BRIM is latency-bound and counted at zero"}
+
     # --- training step: forward keeping the backward's state, then backward
     train = None
     if (not args.no_train and wl.dtype == W.DTYPE_BF16 and not sim and not wl.gated
@@ -282,7 +316,7 @@ def main():
                    "Nd": wl.Nd, "F": wl.F, "placement": "alg1"},
         "ct": ct_alg1, "n_sfd": nsfd_alg1, "intra": intra_alg1,
         "ct_bounds": [-(-wl.k * wl.Nd // wl.Ne), min(wl.k, wl.Nd)],
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "stage_roofline": stage_roof,
         "stages_ms": {s: round(v, 5) for s, v in stages.items()},
         "contiguous": res_contig,
         "deterministic": res_det,
