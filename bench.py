@@ -49,6 +49,8 @@ def parse():
                     help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--no-det", action="store_true",
                     help="skip the deterministic-merge forward")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="time the deterministic merge as the main step")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training step (forward with saved state + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -80,6 +82,9 @@ def main():
     desc = occ.desc_of(wl)
     ws = occ.alloc_workspace(desc, dev)
     desc_main, ws_main = desc, ws
+    if args.deterministic:
+        desc_main = occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC)
+        ws_main = occ.alloc_workspace(desc_main, dev)
     dt = synth.torch_dtype(wl)
     y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
@@ -213,7 +218,7 @@ def main():
     ms = ms_graph if ms_graph is not None else ms_eager
     tokens_per_s = wl.T / (ms / 1e3)
     res_det = None
-    if not args.no_det and not sim and not wl.gated:
+    if not args.no_det and not args.deterministic and not sim and not wl.gated:
         # the deterministic merge (no atomic adds): same layer, same placement
         desc_det = occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC)
         mode_det = (desc_det, occ.alloc_workspace(desc_det, dev))
@@ -313,7 +318,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == W.DTYPE_BF16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "Ne": wl.Ne, "k": wl.k,
-                   "Nd": wl.Nd, "F": wl.F, "placement": "alg1"},
+                   "Nd": wl.Nd, "F": wl.F, "placement": "alg1",
+                   "merge": "deterministic" if args.deterministic else "atomic"},
         "ct": ct_alg1, "n_sfd": nsfd_alg1, "intra": intra_alg1,
         "ct_bounds": [-(-wl.k * wl.Nd // wl.Ne), min(wl.k, wl.Nd)],
         "roofline": roofline, "cpu_baseline": cpu, "stage_roofline": stage_roof,
