@@ -6,11 +6,15 @@ the OLMoE-shaped workload (T = 8192 tokens, d = 2048, 64 experts, top-8,
 8 groups, F = 1024, bf16), inputs resident in HBM.  The expert placement is
 the rescheduled one (Algorithm 1 on the batch's co-activation counts, built
 with the library's own calls, untimed); the contiguous placement is timed
-too and reported beside it.  `value` is the rate of the step replayed from a
-HIP graph (the launches captured once); the eager rate, with HIP events
-between the stages, is reported beside it.  The deterministic merge (no
-atomic adds) and a training step (forward that keeps the backward's state,
-then the backward pass) are timed as well.
+too and reported beside it.  The step uses the deterministic merge of
+Algorithm 8 (every EPD row's fp32 result stored, each SFD row summed in slot
+order, the combine done in the same pass), which on this GPU is both faster
+than the atomic-add merge and bitwise reproducible; the atomic merge is timed
+beside it (`--atomic` swaps the two).  `value` is the rate of the step
+replayed from a HIP graph (the launches captured once); the eager rate, with
+HIP events between the stages, is reported beside it.  A training step
+(forward that keeps the backward's state, then the backward pass) is timed
+as well.
 
 Prints one JSON line.  The roofline entry is for the dominant kernel (the
 SwiGLU up-projection GEMM): algorithmic FLOPs per launch over its average
@@ -47,15 +51,33 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replay)")
-    ap.add_argument("--no-det", action="store_true",
-                    help="skip the deterministic-merge forward")
-    ap.add_argument("--deterministic", action="store_true",
-                    help="time the deterministic merge as the main step")
+    ap.add_argument("--atomic", action="store_true",
+                    help="time the atomic-add merge as the main step (default: the "
+                         "deterministic merge)")
+    ap.add_argument("--one-merge", action="store_true",
+                    help="skip timing the other merge beside the main one")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training step (forward with saved state + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     return ap.parse_args()
+
+
+def merge_name(flags):
+    from expert_token_routing_amd import occ
+    return "deterministic" if flags & occ.OCC_FLAG_DETERMINISTIC else "atomic"
+
+
+def name_stages(st, flags):
+    """The forward's stage times under names that fit the merge in use: the
+    deterministic merge's seventh stage is the merge together with the combine."""
+    from expert_token_routing_amd import occ
+    st = dict(st)
+    if flags & occ.OCC_FLAG_DETERMINISTIC:
+        st["gemm_down"] = st.pop("gemm_down_first")
+        st["merge_and_combine"] = st.pop("gemm_down_rest")
+        st.pop("combine")
+    return st
 
 
 def log(msg):
@@ -81,10 +103,9 @@ def main():
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     desc = occ.desc_of(wl)
     ws = occ.alloc_workspace(desc, dev)
-    desc_main, ws_main = desc, ws
-    if args.deterministic:
-        desc_main = occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC)
-        ws_main = occ.alloc_workspace(desc_main, dev)
+    main_flags = 0 if args.atomic else occ.OCC_FLAG_DETERMINISTIC
+    desc_main = occ.desc_of(wl, flags=main_flags)
+    ws_main = occ.alloc_workspace(desc_main, dev)
     dt = synth.torch_dtype(wl)
     y = torch.empty(wl.T, wl.d, dtype=dt, device=dev)
     stream = torch.cuda.current_stream()
@@ -217,22 +238,23 @@ def main():
     # runs it; the eager rate is reported beside it
     ms = ms_graph if ms_graph is not None else ms_eager
     tokens_per_s = wl.T / (ms / 1e3)
-    res_det = None
-    if not args.no_det and not args.deterministic and not sim and not wl.gated:
-        # the deterministic merge (no atomic adds): same layer, same placement
-        desc_det = occ.desc_of(wl, flags=occ.OCC_FLAG_DETERMINISTIC)
-        mode_det = (desc_det, occ.alloc_workspace(desc_det, dev))
-        ms_d, stages_d = timed(L_alg1, "deterministic merge", mode=mode_det)
-        ms_dg = None if args.no_graph else graph_timed(L_alg1, "deterministic merge", mode=mode_det)
-        stages_d["gemm_down"] = stages_d.pop("gemm_down_first")
-        stages_d["merge"] = stages_d.pop("gemm_down_rest")
-        res_det = {"value": wl.T / ((ms_dg or ms_d) / 1e3), "ms_per_step": ms_dg or ms_d,
-                   "eager_ms_per_step": ms_d, "stages_ms": stages_d}
+    res_other = None
+    if not args.one_merge:
+        # the other merge strategy: same layer, same placement
+        other_flags = occ.OCC_FLAG_DETERMINISTIC if args.atomic else 0
+        desc_o = occ.desc_of(wl, flags=other_flags)
+        mode_o = (desc_o, occ.alloc_workspace(desc_o, dev))
+        label = merge_name(other_flags) + " merge"
+        ms_o, stages_o = timed(L_alg1, label, mode=mode_o)
+        ms_og = None if args.no_graph else graph_timed(L_alg1, label, mode=mode_o)
+        res_other = {"merge": merge_name(other_flags), "value": wl.T / ((ms_og or ms_o) / 1e3),
+                     "ms_per_step": ms_og or ms_o, "eager_ms_per_step": ms_o,
+                     "stages_ms": name_stages(stages_o, other_flags)}
     res_contig = None
     if not args.no_contiguous:
         ms_c, stages_c = timed(L_contig, "contiguous placement")
         res_contig = {"value": wl.T / (ms_c / 1e3), "ms_per_step": ms_c, "ct": ct_contig,
-                      "intra": intra_contig, "stages_ms": stages_c}
+                      "intra": intra_contig, "stages_ms": name_stages(stages_c, main_flags)}
 
     if args.copy_calibration:
         n = 1 << 30
@@ -277,17 +299,26 @@ def main():
         return {"ms": round(ms_stage, 5), "bound": "mfma" if t_f >= t_b else "hbm",
                 "roof_ms": round(t * 1e3, 5), "frac": round(t * 1e3 / ms_stage, 4)}
 
-    down_ms = stages.get("gemm_down_first", 0.0) + stages.get("gemm_down_rest", 0.0)
+    flops_down = 2.0 * T * k * F * d
+    y_bytes = T * d * es + (T * d * 4 if wl.n_shared else 0)
     stage_roof = {
         "route": bound(stages.get("route", stages.get("route_copy", 0.0)) or 1e-9, 0.0,
                        T * (4 * wl.Ne + 8 * k)),
         "dispatch": bound(stages["dispatch"], 0.0, (T + nsfd_alg1) * d * es),
         "gemm_up": bound(up_ms, flops_up, bytes_up),
-        "gemm_down": bound(down_ms, 2.0 * T * k * F * d,
-                           active * d * F * es + T * k * F * es + nsfd_alg1 * d * 4),
-        "combine": bound(stages["combine"], 0.0,
-                         nsfd_alg1 * d * 4 + T * d * es + (T * d * 4 if wl.n_shared else 0)),
     }
+    if main_flags & occ.OCC_FLAG_DETERMINISTIC:
+        # one down-projection launch storing every EPD row's fp32 result, then
+        # the merge (reads them, writes the SFD rows) with the combine (y)
+        stage_roof["gemm_down"] = bound(stages["gemm_down_first"], flops_down,
+                                        active * d * F * es + T * k * F * es + T * k * d * 4)
+        stage_roof["merge_and_combine"] = bound(stages["gemm_down_rest"], 0.0,
+                                                T * k * d * 4 + nsfd_alg1 * d * 4 + y_bytes)
+    else:
+        down_ms = stages["gemm_down_first"] + stages["gemm_down_rest"]
+        stage_roof["gemm_down"] = bound(down_ms, flops_down,
+                                        active * d * F * es + T * k * F * es + nsfd_alg1 * d * 4)
+        stage_roof["combine"] = bound(stages["combine"], 0.0, nsfd_alg1 * d * 4 + y_bytes)
     if wl.n_shared:
         fs = wl.n_shared * wl.F_shared
         stage_roof["shared"] = bound(stages["shared"], 2.0 * T * d * 3 * fs,
@@ -319,13 +350,13 @@ def main():
         "dtype": "bf16" if wl.dtype == W.DTYPE_BF16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "Ne": wl.Ne, "k": wl.k,
                    "Nd": wl.Nd, "F": wl.F, "placement": "alg1",
-                   "merge": "deterministic" if args.deterministic else "atomic"},
+                   "merge": merge_name(main_flags)},
         "ct": ct_alg1, "n_sfd": nsfd_alg1, "intra": intra_alg1,
         "ct_bounds": [-(-wl.k * wl.Nd // wl.Ne), min(wl.k, wl.Nd)],
         "roofline": roofline, "cpu_baseline": cpu, "stage_roofline": stage_roof,
-        "stages_ms": {s: round(v, 5) for s, v in stages.items()},
+        "stages_ms": {s: round(v, 5) for s, v in name_stages(stages, main_flags).items()},
         "contiguous": res_contig,
-        "deterministic": res_det,
+        "other_merge": res_other,
     }
     if train is not None:
         out["train"] = train
@@ -344,7 +375,8 @@ def train_leg(args, wl, g, L, stream):
     from expert_token_routing_amd import occ
 
     dev = torch.device("cuda:0")
-    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN |
+                       (0 if args.atomic else occ.OCC_FLAG_DETERMINISTIC))
     ws = occ.alloc_workspace(desc, dev)
     dt = torch.bfloat16
     f32 = dict(dtype=torch.float32, device=dev)
