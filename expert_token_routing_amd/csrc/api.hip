@@ -466,8 +466,10 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
         OCC_TRY(mark(6));
+        // stage one (SFD rows) and, in the same pass over each token, stage
+        // two (Algorithm 9) with the combine's order of additions
         OCC_HIP(launch_merge_slots(y_epd, ids, bb.tok_epd, bb.brim0, tab, D.T, D.k, D.d, sfd_out,
-                                   s));
+                                   y_sh, y, bf16, s));
     } else if (one_launch) {
         dn.phase = 0;
         dn.tile_off = bb.tile_off;
@@ -484,7 +486,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     }
     OCC_TRY(mark(7));
     // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once
-    OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
+    if (!det) OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
     OCC_TRY(mark(8));
     return OCC_OK;
 }
@@ -633,17 +635,14 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     g2.epilogue = BWD_EPI_MERGE;
     g2.tab = tab;
     if (det) {
-        // each EPD row's fp32 dx stored at that row, then summed per SFD row
-        // in slot order
-        float *dx_epd = at<float>(workspace, L.y_epd);
+        // each EPD row's fp32 dx stored at that row; summed per SFD row in
+        // slot order after the shared experts, with the combine
         g2.dst_rows = nullptr;
-        g2.merge_out = dx_epd;
+        g2.merge_out = at<float>(workspace, L.y_epd);
         g2.phase = 0;
         g2.tile_off = bt_all;
         g2.merge_store = 1;
         OCC_HIP(launch_bwd_dgrad(g2, routed_tiles, s));
-        OCC_HIP(launch_merge_slots(dx_epd, at<int32_t>(workspace, L.ids), bb.tok_epd, bb.brim0,
-                                   tab, D.T, D.k, D.d, dx_sfd, s));
     } else if (one_launch) {
         g2.phase = 0;
         g2.tile_off = bt_all;
@@ -748,7 +747,13 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     OCC_TRY(mark(4));
     // dx: SFD -> ORI, summed across groups (the dispatch's transpose), plus
     // the shared experts' part, cast once
-    OCC_HIP(launch_combine(dx_sfd, bb.brim0, dx_sh, D.T, D.Nd, D.d, D.dtype == OCC_BF16, dx, s));
+    if (det)
+        OCC_HIP(launch_merge_slots(at<float>(workspace, L.y_epd), at<int32_t>(workspace, L.ids),
+                                   bb.tok_epd, bb.brim0, tab, D.T, D.k, D.d, dx_sfd, dx_sh, dx,
+                                   D.dtype == OCC_BF16, s));
+    else
+        OCC_HIP(launch_combine(dx_sfd, bb.brim0, dx_sh, D.T, D.Nd, D.d, D.dtype == OCC_BF16, dx,
+                               s));
     OCC_TRY(mark(5));
     // dW_d[e] = sum over e's rows of dy_sfd[row's SFD row] (x) h[row]
     BwdWgradArgs w1{};

@@ -48,9 +48,11 @@ hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const
                            int zero_cols = 0);
 // Deterministic stage one: sfd_out[brim0[g, t]] = sum over the token's experts
 // in group g, in ascending placement position, of y_epd[tok_epd[t, j]] (fp32).
+// With y, also stage two, as launch_combine would compute it (same order).
 hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int32_t *tok_epd,
                               const int32_t *brim0, const PlaceTab &tab, int T, int k, int d,
-                              float *sfd_out, hipStream_t s);
+                              float *sfd_out, const float *y_sh, void *y, int y_bf16,
+                              hipStream_t s);
 // y[t] = dtype( sum over g of sfd_out[brim0[g, t]] (+ y_sh[t]) ), fp32 sums in
 // ascending group order.
 hipError_t launch_combine(const float *sfd_out, const int32_t *brim0, const float *y_sh, int T,

@@ -139,15 +139,21 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
 }
 
 // One wave per token.  Lane j < k holds the token's j-th expert: placement
-// position p_j, group g_j, EPD row erow_j.  Its rank among the token's
-// positions orders the walk; a group's positions are contiguous, so the walk
-// visits each group's experts together, in slot order, and a change of group
-// flushes the running fp32 sum to that group's SFD row.
-template <int VPL>
+// position p_j and EPD row erow_j; after a sort by position (the positions
+// are distinct), lane r holds the r-th.  The walk visits each group's
+// experts together, in slot order (a group's positions are contiguous), and
+// a change of group stores the running fp32 sum as that group's SFD row.
+// With Y, the kernel also finishes the layer as the combine would: the
+// group sums are added in ascending group order (the order in which the walk
+// meets them), then the shared experts' row, and the result is cast once --
+// the same additions in the same order, so y is the combine's bit for bit.
+// The next row's loads are issued before the current row is added.
+template <int VPL, int Y>  // Y: 0 none, 1 bf16, 2 fp32
 __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     const f32x4 *__restrict__ y_epd, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ tok_epd, const int32_t *__restrict__ brim0, PlaceTab tab, int T,
-    int k, int row_vec4, f32x4 *__restrict__ sfd_out) {
+    int k, int row_vec4, f32x4 *__restrict__ sfd_out, const f32x4 *__restrict__ y_sh,
+    void *__restrict__ y) {
     const int lane = lane_id();
     const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
     if (t >= T) return;
@@ -158,12 +164,27 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
         p = tab.grp[e] * tab.n + tab.slot[e];
         erow = tok_epd[o];
     }
-    int rank = 0;  // positions are distinct: the token's experts are
+    int rank = 0;
     for (int j = 0; j < k; j++) rank += __shfl(p, j) < p;
-    f32x4 acc[VPL];
+    int sp = 0, se = 0;  // lane r: position and EPD row of the r-th expert
+    for (int j = 0; j < k; j++) {
+        const int rj = __shfl(rank, j), pj = __shfl(p, j), ej = __shfl(erow, j);
+        if (rj == lane) {
+            sp = pj;
+            se = ej;
+        }
+    }
+    f32x4 acc[VPL], ya[VPL], cur[VPL], nxt[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int cur_g = -1;
+    for (int i = 0; i < VPL; i++) {
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ya[i] = acc[i];
+    }
+    auto load = [&](int er, f32x4 (&v)[VPL]) {
+        const f32x4 *row = y_epd + static_cast<size_t>(er) * row_vec4;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) v[i] = row[min(lane + kWave * i, row_vec4 - 1)];
+    };
     auto flush = [&](int g) {
         const int r = brim0[static_cast<size_t>(g) * T + t];
         f32x4 *dst = sfd_out + static_cast<size_t>(r) * row_vec4;
@@ -171,35 +192,72 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
         for (int i = 0; i < VPL; i++) {
             const int c = lane + kWave * i;
             if (c < row_vec4) dst[c] = acc[i];
+            if (Y) ya[i] += acc[i];
             acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
+    int cur_g = -1;
+    load(__shfl(se, 0), cur);
     for (int r = 0; r < k; r++) {
-        const int src = __builtin_ctzll(__ballot(lane < k && rank == r));
-        const int pr = __shfl(p, src), er = __shfl(erow, src);
-        const int g = pr / tab.n;
+        if (r + 1 < k) load(__shfl(se, r + 1), nxt);
+        const int g = __shfl(sp, r) / tab.n;
         if (g != cur_g) {
             if (cur_g >= 0) flush(cur_g);
             cur_g = g;
         }
-        const f32x4 *row = y_epd + static_cast<size_t>(er) * row_vec4;
 #pragma unroll
-        for (int i = 0; i < VPL; i++) acc[i] += row[min(lane + kWave * i, row_vec4 - 1)];
+        for (int i = 0; i < VPL; i++) {
+            acc[i] += cur[i];
+            cur[i] = nxt[i];
+        }
     }
-    if (cur_g >= 0) flush(cur_g);
+    flush(cur_g);
+    if constexpr (Y != 0) {
+        if (y_sh) {
+            const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) ya[i] += src[min(lane + kWave * i, row_vec4 - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane + kWave * i;
+            if (c >= row_vec4) continue;
+            const size_t o = static_cast<size_t>(t) * row_vec4 + c;
+            if constexpr (Y == 1) {
+                uint2 packed;
+                packed.x = static_cast<uint32_t>(f32_to_bf16_bits(ya[i].x)) |
+                           (static_cast<uint32_t>(f32_to_bf16_bits(ya[i].y)) << 16);
+                packed.y = static_cast<uint32_t>(f32_to_bf16_bits(ya[i].z)) |
+                           (static_cast<uint32_t>(f32_to_bf16_bits(ya[i].w)) << 16);
+                reinterpret_cast<uint2 *>(y)[o] = packed;
+            } else {
+                reinterpret_cast<f32x4 *>(y)[o] = ya[i];
+            }
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int32_t *tok_epd,
                               const int32_t *brim0, const PlaceTab &tab, int T, int k, int d,
-                              float *sfd_out, hipStream_t s) {
+                              float *sfd_out, const float *y_sh, void *y, int y_bf16,
+                              hipStream_t s) {
     const int row_vec4 = d / 4;
     const int vpl = (row_vec4 + kWave - 1) / kWave;
     const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
     const f32x4 *ye = reinterpret_cast<const f32x4 *>(y_epd);
     f32x4 *so = reinterpret_cast<f32x4 *>(sfd_out);
-#define OCC_MERGE(V) k_merge_slots<V><<<grid, block, 0, s>>>(ye, ids, tok_epd, brim0, tab, T, k, row_vec4, so)
+    const f32x4 *ys = reinterpret_cast<const f32x4 *>(y_sh);
+    const int ymode = y ? (y_bf16 ? 1 : 2) : 0;
+#define OCC_MERGE_Y(V, YM) \
+    k_merge_slots<V, YM><<<grid, block, 0, s>>>(ye, ids, tok_epd, brim0, tab, T, k, row_vec4, so, ys, y)
+#define OCC_MERGE(V)                          \
+    do {                                      \
+        if (ymode == 1) OCC_MERGE_Y(V, 1);    \
+        else if (ymode == 2) OCC_MERGE_Y(V, 2); \
+        else OCC_MERGE_Y(V, 0);               \
+    } while (0)
     if (vpl <= 1) OCC_MERGE(1);
     else if (vpl <= 2) OCC_MERGE(2);
     else if (vpl <= 4) OCC_MERGE(4);
@@ -207,6 +265,7 @@ hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int3
     else if (vpl <= 16) OCC_MERGE(16);
     else OCC_MERGE(32);
 #undef OCC_MERGE
+#undef OCC_MERGE_Y
     return hipGetLastError();
 }
 

@@ -79,9 +79,10 @@ typedef enum occ_prune_rule {
  * the stage-one results may equally be summed serially over the local
  * experts): the down-projection stores every EPD row's fp32 result, then each
  * SFD row is the sum of its contributions in ascending placement position
- * (slot order inside the group), with no atomic adds.  Every output (y, and
- * with OCC_FLAG_TRAIN every gradient) is then bitwise identical from run to
- * run.  The workspace grows by T*k*d fp32. */
+ * (slot order inside the group), with no atomic adds; the same pass over
+ * each token also adds its SFD rows into y (Algorithm 9, in the combine's
+ * order).  Every output (y, and with OCC_FLAG_TRAIN every gradient) is then
+ * bitwise identical from run to run.  The workspace grows by T*k*d fp32. */
 #define OCC_FLAG_DETERMINISTIC 2
 
 /* Shape of one MoE layer.  Limits of this build:
@@ -175,10 +176,13 @@ enum {
     OCC_STAGE_SHARED = 3,
     OCC_STAGE_GEMM_UP = 4,
     OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores (one-launch
-                                      merge: the zero-fill and every row) */
+                                      merge: every row's atomic add;
+                                      OCC_FLAG_DETERMINISTIC: every row's
+                                      result stored) */
     OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds (one-launch
-                                      merge: empty) */
-    OCC_STAGE_COMBINE = 7,
+                                      merge: empty; OCC_FLAG_DETERMINISTIC:
+                                      the merge and the combine) */
+    OCC_STAGE_COMBINE = 7,         /* OCC_FLAG_DETERMINISTIC: empty */
     OCC_STAGE_COUNT = 8
 };
 
@@ -320,9 +324,13 @@ occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, con
 enum {
     OCC_BSTAGE_DISPATCH = 0,    /* dy ORI -> SFD (BRIM_0) */
     OCC_BSTAGE_DGRAD_DOWN = 1,  /* dh = dy W_d per EPD row, SwiGLU backward */
-    OCC_BSTAGE_DGRAD_UP = 2,    /* dg W_g + du W_u, merged EPD -> SFD in fp32 */
+    OCC_BSTAGE_DGRAD_UP = 2,    /* dg W_g + du W_u, merged EPD -> SFD in fp32
+                                   (OCC_FLAG_DETERMINISTIC: stored per EPD
+                                   row, merged in the combine stage) */
     OCC_BSTAGE_SHARED = 3,      /* the shared experts' four products */
-    OCC_BSTAGE_COMBINE = 4,     /* dx SFD -> ORI across groups (+ shared) */
+    OCC_BSTAGE_COMBINE = 4,     /* dx SFD -> ORI across groups (+ shared);
+                                   OCC_FLAG_DETERMINISTIC: the slot-order
+                                   merge too */
     OCC_BSTAGE_WGRAD_DOWN = 5,  /* dW_d = sum dy h^T per expert */
     OCC_BSTAGE_WGRAD_UP = 6,    /* dW_g, dW_u = sum [dg; du] x^T per expert */
     OCC_BSTAGE_ROUTE = 7,       /* routing-weight and logit gradients */

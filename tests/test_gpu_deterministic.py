@@ -54,6 +54,20 @@ def test_deterministic_forward_matches_oracle_and_repeats_bitwise(wl):
     ref = oracle_rows(wl, inp, np.arange(wl.T), ids, w)
     err = row_err(y0.float().cpu().numpy(), ref)
     assert err.max() <= TOL[wl.dtype], err.max()
+    # stage one is materialised: the SFD rows, added in ascending group order
+    # in fp32 (plus the shared experts) and cast once, give y bit for bit
+    v = occ.occ_forward_views(desc, ws0)
+    sfd_off = occ.ws_view(ws0, v.brim.sfd_off, (wl.Nd + 1,), torch.int32).cpu().numpy()
+    n_sfd = int(sfd_off[-1])
+    sfd = occ.ws_view(ws0, v.sfd_out, (n_sfd, wl.d), torch.float32).cpu()
+    b0 = occ.ws_view(ws0, v.brim.brim0, (wl.Nd, wl.T), torch.int32).cpu().numpy()
+    acc = torch.zeros(wl.T, wl.d, dtype=torch.float32)
+    for gi in range(wl.Nd):
+        sel = np.nonzero(b0[gi] >= 0)[0]
+        acc[sel] = acc[sel] + sfd[b0[gi][sel]]
+    if wl.n_shared:
+        acc = acc + occ.ws_view(ws0, v.y_shared, (wl.T, wl.d), torch.float32).cpu()
+    assert torch.equal(acc.to(y0.dtype), y0.cpu())
     # the merged SFD rows agree with the atomic path's up to summation order
     ya, _, _ = run_forward(wl, inp, dev, flags=0)
     assert row_err(ya.float().cpu().numpy(), y0.float().cpu().numpy().astype(np.float64)).max() \
