@@ -18,10 +18,11 @@ constexpr int kMaxNd = 64;
 constexpr int kMaxK = 32;
 constexpr int kMaxBins = kMaxNd + 2 * kMaxNe;  // BRIM bins: groups, experts, first contributors
 
-// Row tile of the grouped GEMMs (tokens per workgroup tile); the BRIM scan
-// lays out the per-expert tile schedule with it.
+// Row-tile capacity of the bf16 grouped GEMMs (at most this many tokens per
+// workgroup tile); the BRIM scan gives each expert ceil(rows / capacity)
+// tiles, whose rows the GEMMs share out evenly.
 #ifndef OCC_GEMM_BM
-#define OCC_GEMM_BM 256
+#define OCC_GEMM_BM 320
 #endif
 constexpr int kGemmBmBf16 = OCC_GEMM_BM;
 constexpr int kGemmBmF32 = 64;

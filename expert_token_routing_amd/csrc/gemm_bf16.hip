@@ -14,11 +14,12 @@
 //         share that row -- the intra-group pre-aggregation of section 3.1).
 //
 // Tiling: a 512-thread workgroup (8 waves, one workgroup per CU, two waves
-// per SIMD) computes a 256 x 256 tile of MFMA outputs; each wave owns a
-// 64 x 128 sub-tile of 16 x 16 MFMA blocks.  In the up GEMM the 256 columns
+// per SIMD) computes a tile of up to 320 rows x 256 MFMA output columns.  The
+// rows come in 16-row blocks dealt to the four wave rows in turn, and each
+// wave holds 128 columns of its blocks.  In the up GEMM the 256 columns
 // are 128 gate and 128 up rows of the same output features, so the SwiGLU
 // epilogue has both operands in registers.  K is consumed in 64-deep slices
-// (each row's slice is one 128-byte line) through two 64 KB LDS buffers
+// (each row's slice is one 128-byte line) through two 72 KB LDS buffers
 // filled by direct global->LDS loads: slice kt+1 is issued right after the
 // barrier that opens slice kt and lands during its MFMA work.  Measured on
 // the OLMoE-shaped layer, this beats 32-deep slices in a 3- to 5-deep ring
@@ -29,14 +30,23 @@
 // and written as whole 16-byte row chunks.
 //
 // Scheduling: the BRIM scan gives each expert ceil(rows / BM) row tiles
-// (tile_off), so every tile reads one expert's weights.  Workgroup b runs on
+// (tile_off), so every tile reads one expert's weights, and the expert's
+// row blocks are shared out evenly among them.  With 320-row capacity an
+// expert of 1025-1067 rows is four tiles of 256-272 rows instead of four
+// full 256-row tiles and a fifth of at most 43 rows that costs as much as a
+// full one (the tile's time is set by its weight loads).  Measured on the
+// OLMoE-shaped layer (287 -> 255 row tiles): -3% in both projections; the
+// balance is imperfect because a 17-block tile gives one SIMD pair 9 blocks.
+// A wave skips the MFMAs and the direct loads of blocks that hold no rows.
+// Workgroup b runs on
 // XCD b % 8; tiles are renumbered so that each XCD takes a contiguous range
 // of an expert-major tile order (column tiles outer, row tiles inner inside
 // an expert, except in the atomic merge phase): the workgroups sharing an
 // expert's weights and a row tile's activations share one L2.
 // 256-row tiles halve the weight bytes fetched per flop against 128-row
 // tiles (measured: 1.6 vs 2.5 GB beyond L2 per up-projection launch on the
-// OLMoE-shaped layer).
+// OLMoE-shaped layer).  The 64-row build (the decode regime) shares all of
+// this with four single-block wave rows.
 #include "launch.h"
 
 namespace occ {
@@ -141,9 +151,20 @@ struct Tile {
     int e;     // expert
     int seg;   // first row of the expert's segment
     int m0;    // first row of the tile inside the segment
-    int rows;  // valid rows in the tile
+    int rows;  // valid rows in the tile (at most BM)
     int n0;    // first column (output feature) of the tile
 };
+
+// A segment of len rows in n = ceil(len / BM) row tiles: its ceil(len / 16)
+// MFMA row blocks are dealt out as evenly as possible (the first B mod n
+// tiles take one more), so an expert of 1030 rows is four tiles of 272, 256,
+// 256 and 246 rows rather than four full tiles and one of 6 rows.  Tile j's
+// first row and row count.
+__device__ __forceinline__ void split_rows(int len, int n, int j, int &m0, int &rows) {
+    const int B = (len + 15) >> 4, base = B / n, rem = B - base * n;
+    m0 = 16 * (j * base + min(j, rem));
+    rows = min(16 * (base + (j < rem ? 1 : 0)), len - m0);
+}
 
 // Routed tiles walk expert segments [seg_off[p], seg_off[p+1]) -- all rows
 // (phase 0), the first first_cnt[p] rows (phase 1) or the rest (phase 2) --
@@ -173,40 +194,47 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
         const int nf = phase ? first_cnt[p] : 0;
         t.e = tab.expert[p];
         t.seg = phase == 2 ? seg0 + nf : seg0;
-        t.m0 = (tm - tile_off[p]) * BM;
-        t.rows = min(BM, (phase == 1 ? nf : len - nf) - t.m0);
+        split_rows(phase == 1 ? nf : len - nf, tile_off[p + 1] - tile_off[p], tm - tile_off[p],
+                   t.m0, t.rows);
     } else {
         const int m_tiles = (M + BM - 1) / BM;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
         t.e = 0;
         t.seg = 0;
-        t.m0 = tm * BM;
-        t.rows = min(BM, M - t.m0);
+        split_rows(M, m_tiles, tm, t.m0, t.rows);
     }
     t.n0 = tn * n_step;
     return true;
 }
 
+// The tile's 16-row blocks are dealt to the wave rows in turn: wave row wm
+// owns blocks wm, wm + WAVES_M, ...; its mi-th block starts at this row.
+// The two wave rows that share a SIMD (wm and wm + 2) then hold
+// ceil(blocks / 2) blocks between them whatever the tile's height.
+__device__ __forceinline__ int block_row(int wm, int mi) { return (wm + WAVES_M * mi) * 16; }
+
+// NV: the wave's blocks that hold rows (the others are not multiplied).
+template <int NV>
 __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB, int wm,
                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI]) {
-    const int l = lane_id();
+    if constexpr (NV > 0) {
+        const int l = lane_id();
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ks++) {
-        const int chunk = ks * 4 + (l >> 4);
-        bf16x8_t a[MI], b[NI];
+        for (int ks = 0; ks < BK / 32; ks++) {
+            const int chunk = ks * 4 + (l >> 4);
+            bf16x8_t a[NV], b[NI];
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++) {
-            const int r = wm * WM + mi * 16 + (l & 15);
-            a[mi] = *reinterpret_cast<const bf16x8_t *>(sA + swz(r, chunk));
-        }
-#pragma unroll
-        for (int ni = 0; ni < NI; ni++)
-            b[ni] = *reinterpret_cast<const bf16x8_t *>(sB + swz(brow[ni], chunk));
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+            for (int mi = 0; mi < NV; mi++)
+                a[mi] = *reinterpret_cast<const bf16x8_t *>(sA + swz(block_row(wm, mi) + (l & 15), chunk));
 #pragma unroll
             for (int ni = 0; ni < NI; ni++)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+                b[ni] = *reinterpret_cast<const bf16x8_t *>(sB + swz(brow[ni], chunk));
+#pragma unroll
+            for (int mi = 0; mi < NV; mi++)
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        }
     }
 }
 
@@ -228,6 +256,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Wait until at most n (wave-uniform, 0 <= n <= N) loads are in flight; the
+// count is an immediate of the instruction, hence the chain.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= N) wait_vmcnt<N>();
+        else wait_vmcnt_le<N - 1>(n);
+    }
+}
+
 // K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
 // fetch chunk of its rows at k = 0.  A ring of NSTAGE LDS buffers is filled
 // by direct loads: slice kt+NSTAGE-1 is issued right after the barrier that
@@ -236,11 +276,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // buffer it overwrites (slice kt-1's).  B is laid out as blocks of ksp-wide
 // K ranges, blk elements apart (the shared experts' down weights); one block
 // (ksp = K) is the plain case.
+// The wave issues only its first na A loads per slice (the 8-row groups
+// that hold rows; the LDS rows it skips keep stale values, which reach only
+// output rows that are never stored) and multiplies its first NV blocks.
+template <int NV>
 __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
                                        const uint16_t *const (&b_src)[B_LD], int K, int ksp,
                                        size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
-                                       f32x4_t (&acc)[MI][NI]) {
+                                       f32x4_t (&acc)[MI][NI], int na) {
     constexpr int LOADS = A_LD + B_LD;
+    const int per_slice = na + B_LD;  // loads the wave issues per slice
     const int nk = K / BK;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
@@ -251,7 +296,8 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
         const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
 #pragma unroll
         for (int i = 0; i < A_LD; i++)
-            dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (i * (NT / kWave) + w) * kWave * 16));
+            if (i < na)
+                dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (i * (NT / kWave) + w) * kWave * 16));
 #pragma unroll
         for (int i = 0; i < B_LD; i++)
             dma16(b_src[i] + bo, __builtin_amdgcn_readfirstlane(st + BM * BK * 2 + (i * (NT / kWave) + w) * kWave * 16));
@@ -261,16 +307,38 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
     for (int kt = 0; kt < nk; kt++) {
         // Slices kt+1 .. min(kt+D, nk)-1 may stay in flight.
         const int ahead = min(kt + D, nk) - 1 - kt;
-        if (D >= 4 && ahead >= 3) wait_vmcnt<(D >= 4 ? 3 : 0) * LOADS>();
-        else if (D >= 3 && ahead >= 2) wait_vmcnt<(D >= 3 ? 2 : 0) * LOADS>();
-        else if (ahead >= 1) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
+        wait_vmcnt_le<(D - 1) * LOADS>(ahead * per_slice);
         __syncthreads();
         if (kt + D < nk) issue(kt + D);
         uint16_t *buf = smem + (kt % NSTAGE) * STAGE;
-        mma_slice(buf, buf + BM * BK, wm, brow, acc);
+        mma_slice<NV>(buf, buf + BM * BK, wm, brow, acc);
     }
     __syncthreads();
+}
+
+// Runs the K loop with the wave's block count as a constant.
+template <int NV = MI>
+__device__ __forceinline__ void run_k_loop(int nv, const uint16_t *const (&a_src)[A_LD],
+                                           const uint16_t *const (&b_src)[B_LD], int K, int ksp,
+                                           size_t blk, uint16_t *smem, int wm,
+                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na) {
+    if constexpr (NV == 0) {
+        k_loop<0>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+    } else {
+        if (nv >= NV) k_loop<NV>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        else run_k_loop<NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+    }
+}
+
+// The wave's share of a tile of `rows` rows: its blocks that hold rows, and
+// its A loads (wave w's load i moves rows i * ROWS_PER_PASS + w * 8 .. + 7)
+// that do.
+__device__ __forceinline__ void wave_share(int rows, int wm, int &nv, int &na) {
+    const int blocks = (rows + 15) >> 4;
+    nv = __builtin_amdgcn_readfirstlane(min(MI, max(0, (blocks - wm + WAVES_M - 1) / WAVES_M)));
+    const int first = static_cast<int>(threadIdx.x) / kWave * (kWave / CHUNKS);
+    na = __builtin_amdgcn_readfirstlane(
+        min(A_LD, max(0, (rows - first + ROWS_PER_PASS - 1) / ROWS_PER_PASS)));
 }
 
 // Second bound: waves per SIMD = workgroups per CU x NT / 256.
@@ -311,7 +379,9 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    k_loop(a_src, b_src, K, K, 0, smem, wm, brow, acc);
+    int nv, na;
+    wave_share(t.rows, wm, nv, na);
+    run_k_loop(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na);
 
     // SwiGLU + modulation in registers, bf16 tile staged in LDS (the K
     // buffers are free after the loop's last barrier).
@@ -319,7 +389,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+            const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
             const int rr = min(r, t.rows - 1);
             const float wr = a.row_w ? a.row_w[t.seg + t.m0 + rr] : 1.f;
 #pragma unroll
@@ -389,14 +459,16 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    k_loop(a_src, b_src, K, ksp, blk, smem, wm, brow, acc);
+    int nv, na;
+    wave_share(t.rows, wm, nv, na);
+    run_k_loop(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
 
     float *out = a.out;
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+            const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
             if (r >= t.rows) continue;
             const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
             if (a.dst_rows) {

@@ -115,7 +115,7 @@ def test_forward_on_both_sides_of_the_tile_switch(T):
     w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
     tile_off = occ.ws_view(ws, v.brim.tile_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
     epd_off = occ.ws_view(ws, v.brim.epd_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
-    bm = 64 if T * wl.k < 128 * wl.Ne else 256
+    bm = 64 if T * wl.k < 128 * wl.Ne else 320  # tile capacity in rows
     assert np.array_equal(np.diff(tile_off), (np.diff(epd_off) + bm - 1) // bm)
     rows = synth.sample_rows(wl.T, 128, seed=T)
     ref = oracle_rows(wl, inp, rows, ids, w)
