@@ -423,12 +423,22 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k_gemm_down)(DownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    __shared__ int s_dst[BM];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t, a.first_cnt,
                  a.phase))
         return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
+    // The SFD row of each of the tile's rows, looked up once by one thread
+    // per row (two dependent loads) and published by the K loop's barriers:
+    // looked up by every lane in the epilogue, the lookups ran in series,
+    // one L2 round trip pair per row (measured on the OLMoE-shaped layer:
+    // -10% in the first merge phase, -5% in the atomic phase).
+    if (a.dst_rows && tid < t.rows) {
+        const size_t row = static_cast<size_t>(t.seg) + t.m0 + tid;
+        s_dst[tid] = a.dst_rows[a.rows ? a.rows[row] : static_cast<int>(row)];
+    }
     const int K = a.K, N = a.N, ksp = a.k_split;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
@@ -472,8 +482,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
             if (r >= t.rows) continue;
             const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
             if (a.dst_rows) {
-                const int erow = a.rows ? a.rows[row] : static_cast<int>(row);
-                const size_t dst = static_cast<size_t>(a.dst_rows[erow]) * N;
+                const size_t dst = static_cast<size_t>(s_dst[r]) * N;
                 if (a.phase == 1) {
 #pragma unroll
                     for (int ni = 0; ni < NI; ni++) {

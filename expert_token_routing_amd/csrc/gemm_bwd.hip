@@ -182,6 +182,7 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 template <int EPI>
 __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    __shared__ int s_dst[EPI == BWD_EPI_MERGE ? BM : 1];
     int tm, tn;
     const int m_tiles = a.tile_off[a.Ne], n_tiles = (a.N + BN - 1) / BN;
     if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
@@ -202,6 +203,15 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int n0 = tn * BN;
 
     const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+    if constexpr (EPI == BWD_EPI_MERGE) {
+        // each row's destination, looked up once per row (not in series by
+        // every lane in the epilogue); the K loop's barriers publish it
+        if (tid < rows) {
+            const int pos = seg + m0 + tid;
+            const int erow = a.a_rows ? a.a_rows[pos] : pos;
+            s_dst[tid] = a.dst_rows ? a.dst_rows[erow] : erow;
+        }
+    }
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     // A: K-contiguous gathered rows, thread rows r0 + 64 i, chunk slot tid & 7
     const uint16_t *a_src[4];
@@ -322,9 +332,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             for (int v = 0; v < 4; v++) {
                 const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
                 if (r >= rows) continue;
-                const int pos = seg + m0 + r;
-                const int erow = a.a_rows ? a.a_rows[pos] : pos;
-                float *drow = out + static_cast<size_t>(a.dst_rows ? a.dst_rows[erow] : erow) * a.N;
+                float *drow = out + static_cast<size_t>(s_dst[r]) * a.N;
 #pragma unroll
                 for (int ni = 0; ni < NI; ni++) {
                     const int c = ncol + wn * WN + ni * 16 + (l & 15);
