@@ -344,10 +344,15 @@ __device__ __forceinline__ void wave_share(int rows, int wm, int &nv, int &na) {
 // Second bound: waves per SIMD = workgroups per CU x NT / 256.
 __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k_gemm_up)(UpArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+    __shared__ float s_w[BM];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
+    // The rows' routing weights, loaded once by one thread per row and
+    // published by the K loop's barriers (loaded by every lane in the
+    // epilogue, they were waited for one by one).
+    if (tid < t.rows) s_w[tid] = a.row_w ? a.row_w[t.seg + t.m0 + tid] : 1.f;
     const int K = a.K, N = a.N;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
@@ -390,8 +395,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
-            const int rr = min(r, t.rows - 1);
-            const float wr = a.row_w ? a.row_w[t.seg + t.m0 + rr] : 1.f;
+            const float wr = s_w[min(r, t.rows - 1)];
 #pragma unroll
             for (int ni = 0; ni < NI / 2; ni++) {
                 const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];

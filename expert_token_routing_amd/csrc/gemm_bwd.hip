@@ -294,13 +294,22 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             const float wr = a.row_w ? a.row_w[pos] : 1.f;
             const uint16_t *gr = gu + static_cast<size_t>(pos) * a.gu_ld + a.gu_col;
             uint16_t *orow = out + static_cast<size_t>(pos) * a.out_ld + a.out_col;
+            // the row's pre-activations, all loaded before any result is
+            // stored: interleaved with the stores (which the compiler cannot
+            // tell apart from them) each pair was waited for in turn
+            u16x4 g4s[NI], u4s[NI];
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++) {
+                const int f = ncol + cloc + ni * 16;
+                g4s[ni] = *reinterpret_cast<const u16x4 *>(gr + f);
+                u4s[ni] = *reinterpret_cast<const u16x4 *>(gr + a.gu_uoff + f);
+            }
             float part = 0.f;
 #pragma unroll
             for (int ni = 0; ni < NI; ni++) {
                 const int f = ncol + cloc + ni * 16;  // 4 consecutive features f..f+3
                 if (f < n0) continue;  // overlapped columns belong to the previous tile
-                const u16x4 g4 = *reinterpret_cast<const u16x4 *>(gr + f);
-                const u16x4 u4 = *reinterpret_cast<const u16x4 *>(gr + a.gu_uoff + f);
+                const u16x4 g4 = g4s[ni], u4 = u4s[ni];
                 u16x4 dg4, du4;
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
