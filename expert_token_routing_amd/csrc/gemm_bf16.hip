@@ -421,7 +421,13 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
         const int r = i / CH, c = (i % CH) * 8;
         if (r >= t.rows || t.n0 + c >= N) continue;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * OUT_PITCH + c);
-        *reinterpret_cast<u32x4 *>(out + (static_cast<size_t>(t.seg) + t.m0 + r) * N + t.n0 + c) = v;
+        // Non-temporal: the hidden states are read back only by the next
+        // launch, and kept out of the L2 they leave the weight and
+        // activation slices that the running tiles share (measured on the
+        // OLMoE-shaped layer: -1.5% here, -4% in the decode step; the same
+        // hint on the down-projection's fp32 stores cost 6-10%).
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(
+                                           out + (static_cast<size_t>(t.seg) + t.m0 + r) * N + t.n0 + c));
     }
 }
 

@@ -59,11 +59,14 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t *__restrict__ p, size_
         p[i] = v;
 }
 
+// A row that is read once (the combine's SFD rows and shared-expert rows):
+// non-temporal loads keep it out of the caches the GEMMs rely on.
 template <int VPL>
 __device__ __forceinline__ void load_row(const f32x4 *__restrict__ src, int lane, int row_vec4,
                                          f32x4 (&v)[VPL]) {
 #pragma unroll
-    for (int i = 0; i < VPL; i++) v[i] = src[min(lane + kWave * i, row_vec4 - 1)];
+    for (int i = 0; i < VPL; i++)
+        v[i] = __builtin_nontemporal_load(src + min(lane + kWave * i, row_vec4 - 1));
 }
 
 // The groups holding a replica of the token are the set bits of `mask`;
@@ -147,7 +150,12 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
 // group sums are added in ascending group order (the order in which the walk
 // meets them), then the shared experts' row, and the result is cast once --
 // the same additions in the same order, so y is the combine's bit for bit.
-// The next row's loads are issued before the current row is added.
+// The next row's loads are issued before the current row is added.  Every
+// byte it moves is touched once, so its loads and stores are non-temporal:
+// kept out of the L2 and the last-level cache, they no longer evict the
+// weights and activations the next step's GEMMs read (measured on the
+// OLMoE-shaped step: -8% here and -2.5% in the following up-projection;
+// -13% in the decode step's up-projection).
 template <int VPL, int Y>  // Y: 0 none, 1 bf16, 2 fp32
 __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     const f32x4 *__restrict__ y_epd, const int32_t *__restrict__ ids,
@@ -183,7 +191,8 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     auto load = [&](int er, f32x4 (&v)[VPL]) {
         const f32x4 *row = y_epd + static_cast<size_t>(er) * row_vec4;
 #pragma unroll
-        for (int i = 0; i < VPL; i++) v[i] = row[min(lane + kWave * i, row_vec4 - 1)];
+        for (int i = 0; i < VPL; i++)
+            v[i] = __builtin_nontemporal_load(row + min(lane + kWave * i, row_vec4 - 1));
     };
     auto flush = [&](int g) {
         const int r = brim0[static_cast<size_t>(g) * T + t];
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
             const int c = lane + kWave * i;
-            if (c < row_vec4) dst[c] = acc[i];
+            if (c < row_vec4) __builtin_nontemporal_store(acc[i], dst + c);
             if (Y) ya[i] += acc[i];
             acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -229,7 +238,9 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
                            (static_cast<uint32_t>(f32_to_bf16_bits(ya[i].y)) << 16);
                 packed.y = static_cast<uint32_t>(f32_to_bf16_bits(ya[i].z)) |
                            (static_cast<uint32_t>(f32_to_bf16_bits(ya[i].w)) << 16);
-                reinterpret_cast<uint2 *>(y)[o] = packed;
+                typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+                __builtin_nontemporal_store(u32x2_t{packed.x, packed.y},
+                                            reinterpret_cast<u32x2_t *>(y) + o);
             } else {
                 reinterpret_cast<f32x4 *>(y)[o] = ya[i];
             }
