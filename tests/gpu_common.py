@@ -70,3 +70,22 @@ def oracle_rows(wl: W.Workload, inp: dict, rows, ids, w, nthreads: int = 0):
 def oracle_route(wl: W.Workload, inp: dict, placement=None):
     L = inp["placement"] if placement is None else placement
     return oracle.route(inp["logits"].numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
+
+
+def routed_to_counts(counts, k, seed):
+    """Logits under which token t picks a chosen set of k experts, the sets
+    laid out so that expert e receives exactly counts[e] rows (the neediest
+    experts first, token by token)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    T = int(counts.sum()) // k
+    assert T * k == counts.sum() and counts.max() <= T
+    need = counts.copy()
+    rng = np.random.default_rng(seed)
+    logits = rng.uniform(-1.0, 0.0, size=(T, len(counts))).astype(np.float32)
+    for t in range(T):
+        # the k neediest experts, ties to the lower index
+        pick = np.lexsort((np.arange(len(need)), -need))[:k]
+        need[pick] -= 1
+        logits[t, pick] = 4.0 - 0.1 * np.arange(k)
+    assert not need.any()
+    return torch.from_numpy(logits)

@@ -19,7 +19,7 @@ import torch
 import oracle
 from expert_token_routing_amd import occ, synth, workloads as W
 
-from gpu_common import bits, row_err, to_dev
+from gpu_common import bits, routed_to_counts, row_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -39,11 +39,11 @@ def shape(name, T, d, F, Ne=8, k=2, Nd=4, n_shared=0, F_shared=0, index=11):
                       F_shared=F_shared, n_c=2, bonus=1.0)
 
 
-def run(wl, placement=None, with_logits=True):
-    inp = synth.make_all(wl)
+def run(wl, placement=None, with_logits=True, inp=None, flags=occ.OCC_FLAG_TRAIN):
+    inp = inp or synth.make_all(wl)
     dev = to_dev(inp)
     L = inp["placement"] if placement is None else placement
-    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    desc = occ.desc_of(wl, flags=flags)
     ws = occ.alloc_workspace(desc)
     dt = torch.bfloat16
     y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
@@ -111,6 +111,21 @@ SHARED = ["dWs_gate", "dWs_up", "dWs_down"]
 ], ids=lambda w: w.name)
 def test_backward_matches_oracle(wl):
     got, ref = run(wl)
+    check(got, ref, ROUTED)
+
+
+@pytest.mark.parametrize("flags", [occ.OCC_FLAG_TRAIN,
+                                   occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC],
+                         ids=["atomic", "deterministic"])
+def test_backward_row_tile_split_edges(flags):
+    """Experts whose row counts straddle the backward GEMMs' 256-row tiles
+    (and the K range of the weight gradients): no rows, 1, 15-17, 255-257,
+    511-513."""
+    counts = [0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 3]
+    wl = shape("bwd_split_edges", T=sum(counts) // 2, d=256, F=256, Ne=12, k=2, Nd=4, index=16)
+    inp = synth.make_all(wl)
+    inp["logits"] = routed_to_counts(counts, wl.k, seed=16)
+    got, ref = run(wl, inp=inp, flags=flags)
     check(got, ref, ROUTED)
 
 

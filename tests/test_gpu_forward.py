@@ -11,7 +11,8 @@ import torch
 import oracle
 from expert_token_routing_amd import occ, synth, workloads as W
 
-from gpu_common import TOL, bits, forward, inputs, oracle_route, oracle_rows, row_err, to_dev
+from gpu_common import (TOL, bits, forward, inputs, oracle_route, oracle_rows, routed_to_counts,
+                        row_err, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,6 +152,32 @@ def test_forward_maximum_sizes(shape):
     wl = W.Workload("max_" + "_".join(f"{k}{v}" for k, v in shape.items()), 17, n_c=2,
                     bonus=1.0, **shape)
     check_forward(wl, inp=synth.make_all(wl))
+
+
+def test_forward_row_tile_split_edges():
+    """Experts whose row counts straddle the GEMMs' row-tile boundaries: no
+    rows, 1, 15-17 rows (one MFMA block and a ragged second), 255-257,
+    319-321 (a full 320-row tile and one row past it), 336, 640-641 (two
+    full tiles and one row more) -- every one of them compared row by row
+    with the oracle under both merges."""
+    counts = [0, 1, 15, 16, 17, 255, 256, 257, 319, 320, 321, 336, 640, 641, 2, 34]
+    wl = W.Workload("split_edges", 21, T=sum(counts) // 2, d=256, Ne=16, k=2, Nd=4, F=256,
+                    n_c=4, bonus=1.5)
+    inp = synth.make_all(wl)
+    inp["logits"] = routed_to_counts(counts, wl.k, seed=21)
+    ids, w = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"])
+    assert np.array_equal(np.bincount(ids.reshape(-1), minlength=wl.Ne), counts)
+    ref = oracle_rows(wl, inp, np.arange(wl.T), ids, w)
+    dev = to_dev(inp)
+    for flags in (0, occ.OCC_FLAG_DETERMINISTIC):
+        desc = occ.desc_of(wl, flags=flags)
+        ws = occ.alloc_workspace(desc)
+        y = torch.empty(wl.T, wl.d, dtype=synth.torch_dtype(wl), device="cuda")
+        occ.occ_moe_forward(desc, dev["x"], dev["logits"], inp["placement"], dev["w_gate"],
+                            dev["w_up"], dev["w_down"], None, None, None, y, ws)
+        torch.cuda.synchronize()
+        err = row_err(y.float().cpu().numpy().astype(np.float64), ref)
+        assert err.max() <= TOL[wl.dtype], f"flags {flags}: max per-row rel err {err.max():.3e}"
 
 
 def test_forward_with_starved_expert_and_group():
