@@ -54,6 +54,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef f32x4 f32x4_t;
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 #ifndef OCC_GEMM_BK
 #define OCC_GEMM_BK 64
@@ -214,7 +215,11 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
 __device__ __forceinline__ int block_row(int wm, int mi) { return (wm + WAVES_M * mi) * 16; }
 
 // NV: the wave's blocks that hold rows (the others are not multiplied).
-template <int NV>
+// SWAP issues the MFMA with the operands' roles exchanged, which yields the
+// transposed 16 x 16 block: lane l then holds row (l & 15) and the four
+// consecutive columns 4 (l >> 4) .. + 3 (the plain layout gives a lane four
+// rows of one column).
+template <int NV, bool SWAP>
 __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB, int wm,
                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI]) {
     if constexpr (NV > 0) {
@@ -233,7 +238,8 @@ __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB
             for (int mi = 0; mi < NV; mi++)
 #pragma unroll
                 for (int ni = 0; ni < NI; ni++)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0)
+                                       : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
         }
     }
 }
@@ -279,7 +285,7 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 // The wave issues only its first na A loads per slice (the 8-row groups
 // that hold rows; the LDS rows it skips keep stale values, which reach only
 // output rows that are never stored) and multiplies its first NV blocks.
-template <int NV>
+template <int NV, bool SWAP>
 __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
                                        const uint16_t *const (&b_src)[B_LD], int K, int ksp,
                                        size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
@@ -311,22 +317,22 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
         __syncthreads();
         if (kt + D < nk) issue(kt + D);
         uint16_t *buf = smem + (kt % NSTAGE) * STAGE;
-        mma_slice<NV>(buf, buf + BM * BK, wm, brow, acc);
+        mma_slice<NV, SWAP>(buf, buf + BM * BK, wm, brow, acc);
     }
     __syncthreads();
 }
 
 // Runs the K loop with the wave's block count as a constant.
-template <int NV = MI>
+template <bool SWAP = false, int NV = MI>
 __device__ __forceinline__ void run_k_loop(int nv, const uint16_t *const (&a_src)[A_LD],
                                            const uint16_t *const (&b_src)[B_LD], int K, int ksp,
                                            size_t blk, uint16_t *smem, int wm,
                                            const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na) {
     if constexpr (NV == 0) {
-        k_loop<0>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        k_loop<0, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
     } else {
-        if (nv >= NV) k_loop<NV>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
-        else run_k_loop<NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        if (nv >= NV) k_loop<NV, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        else run_k_loop<SWAP, NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
     }
 }
 
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 
     int nv, na;
     wave_share(t.rows, wm, nv, na);
-    run_k_loop(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na);
+    run_k_loop<true>(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na);
 
     // SwiGLU + modulation in registers; bf16 tiles staged in LDS (the K
     // buffers are free after the loop's last barrier) and written as whole
@@ -401,19 +407,25 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     // stores cost 6-10%).
     constexpr int CH = 128 / 8;  // 16-byte chunks per staged row
     auto stage = [&](int which) {  // 0: h, 1: g, 2: u
+        // lane l holds row (l & 15) of each block and features 4 (l >> 4) .. + 3
+        // of each 16-feature group (the MFMAs ran with their operands
+        // exchanged): one 8-byte LDS write per group
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+        for (int mi = 0; mi < MI; mi++) {
+            const int r = block_row(wm, mi) + (l & 15);
+            const float wr = s_w[min(r, t.rows - 1)];
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
-                const float wr = s_w[min(r, t.rows - 1)];
+            for (int ni = 0; ni < NI / 2; ni++) {
+                u16x4 o;
 #pragma unroll
-                for (int ni = 0; ni < NI / 2; ni++) {
+                for (int v = 0; v < 4; v++) {
                     const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];
                     const float x = which == 0 ? g / (1.f + __expf(-g)) * u * wr : (which == 1 ? g : u);
-                    smem[r * OUT_PITCH + wn * 64 + ni * 16 + (l & 15)] = f32_to_bf16_bits(x);
+                    o[v] = f32_to_bf16_bits(x);
                 }
+                *reinterpret_cast<u16x4 *>(smem + r * OUT_PITCH + wn * 64 + ni * 16 + 4 * (l >> 4)) = o;
             }
+        }
         __syncthreads();
     };
     auto flush = [&](uint16_t *base, size_t ld) {  // staged rows -> base[row * ld + n0 ..]
