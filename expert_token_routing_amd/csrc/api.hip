@@ -575,16 +575,17 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     int32_t *bt_first = at<int32_t>(workspace, L.bt_first);
     int32_t *bt_rest = at<int32_t>(workspace, L.bt_rest);
     float *dx_sh = D.n_shared > 0 ? at<float>(workspace, L.dx_sh) : nullptr;
-    const size_t routed_tiles = (T * D.k + kBwdTile - 1) / kBwdTile + D.Ne;
+    const size_t routed_tiles = (T * D.k + kBwdRowTile - 1) / kBwdRowTile + D.Ne;
     const bool det = D.flags & OCC_FLAG_DETERMINISTIC;
     const bool one_launch = !det && static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
 
     OCC_TRY(mark(0));
-    // schedules for 256-row tiles, a zero row for the tails of K-major operands
+    // row schedules of the input-gradient tiles, a zero row for the tails of
+    // K-major operands
     const size_t zero_elems = std::max<size_t>({d, 2 * F, 2 * Nsh, kBwdTile});
     OCC_HIP(launch_fill_i32(static_cast<int32_t *>(zero_row), zero_elems * es / 4, 0, s));
-    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdTile, bt_all, bt_first, bt_rest,
-                              s));
+    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdRowTile, bt_all, bt_first,
+                              bt_rest, s));
     // dy ORI -> SFD: the combine's transpose copies dy into each replica (and
     // zeroes the dx accumulator rows when the merge is one launch of adds)
     OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s,
@@ -664,8 +665,8 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     if (D.n_shared > 0) {
         int32_t *dseg = at<int32_t>(workspace, L.dense_seg);
         int32_t *dtile = at<int32_t>(workspace, L.dense_tile);
-        OCC_HIP(launch_dense_sched(D.T, kBwdTile, dseg, dtile, s));
-        const size_t dense_tiles = (T + kBwdTile - 1) / kBwdTile;
+        OCC_HIP(launch_dense_sched(D.T, kBwdRowTile, dseg, dtile, s));
+        const size_t dense_tiles = (T + kBwdRowTile - 1) / kBwdRowTile;
         PlaceTab one{};
         one.Ne = 1;
         one.Nd = 1;

@@ -17,9 +17,11 @@
 // rows x 32 bytes on distinct bank windows (two 256-byte cycles, the
 // minimum); "K-contiguous" operands use the forward kernels' layout.
 //
-// Tiles are 256 x 256 outputs per 512-thread workgroup (8 waves of 64 x 128),
-// K in 64-deep slices through two LDS buffers filled by direct global->LDS
-// loads, as in the forward GEMMs.
+// Tiles are up to 320 rows (dgrad; its experts' row blocks shared out evenly
+// over ceil(rows / 320) tiles, as in the forward GEMMs) or 256 rows (wgrad)
+// x 256 outputs per 512-thread workgroup (8 waves, each 128 columns of its
+// wave row's 16-row blocks), K in 64-deep slices through two LDS buffers
+// filled by direct global->LDS loads, as in the forward GEMMs.
 //   k_bwd_dgrad  A = gathered K-contiguous rows, B = an expert's weights read
 //                K-major; routed row tiles over expert segments.  Epilogues:
 //                SwiGLU backward (dh -> dg, du and the routing-weight
@@ -29,6 +31,8 @@
 //   k_bwd_wgrad  A and B both K-major token rows of one expert; K = that
 //                expert's rows (tail rows read a zero row); the fp32 tile is
 //                stored into the expert's weight gradient.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace occ {
@@ -50,6 +54,26 @@ constexpr int STAGE = 2 * OP;
 constexpr int NSTAGE = 2;
 static_assert(BM == BN, "both operand tiles share one size");
 static_assert(NSTAGE * STAGE * 2 <= 160 * 1024, "LDS");
+// dgrad: up to kBwdRowTile gathered rows (K-contiguous) against a K-major
+// weight tile of BN columns
+constexpr int BMD = kBwdRowTile;
+constexpr int MID = BMD / 16 / WAVES_M;            // 16-row blocks per wave row
+constexpr int A_LDD = BMD / 64;                    // A loads per thread per slice
+constexpr int OPA = BMD * BK;                      // bf16 elements of the A tile
+constexpr int STAGED = OPA + OP;
+static_assert(NSTAGE * STAGED * 2 + BMD * 4 <= 160 * 1024, "LDS");
+
+// Block mi of wave row wm starts at this row: blocks are dealt to the wave
+// rows in turn, so the two wave rows sharing a SIMD hold ceil(blocks / 2).
+__device__ __forceinline__ int block_row(int wm, int mi) { return (wm + WAVES_M * mi) * 16; }
+
+// A segment of len rows in n row tiles: ceil(len / 16) blocks dealt out as
+// evenly as possible; tile j's first row and row count.
+__device__ __forceinline__ void split_rows(int len, int n, int j, int &m0, int &rows) {
+    const int B = (len + 15) >> 4, base = B / n, rem = B - base * n;
+    m0 = 16 * (j * base + min(j, rem));
+    rows = min(16 * (base + (j < rem ? 1 : 0)), len - m0);
+}
 
 // ---- K-contiguous operand tiles: rows of 64 k, chunk c at c ^ ((r >> 1) & 7)
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -164,11 +188,11 @@ __device__ __forceinline__ void issue_kmajor(uint32_t lds, const uint16_t *const
 // SWAP = false keeps the plain layout: lane l holds rows 4 (l >> 4) .. +3 of
 // column (l & 15), so 16 lanes cover 64 contiguous bytes of a row -- the
 // better shape for the fp32 atomic adds of the merge.
-template <bool SWAP>
-__device__ __forceinline__ void mfma_tile(const bf16x8_t (&a)[MI], const bf16x8_t (&b)[NI],
-                                          f32x4 (&acc)[MI][NI]) {
+template <bool SWAP, int NV = MI, int M = MI>
+__device__ __forceinline__ void mfma_tile(const bf16x8_t (&a)[M], const bf16x8_t (&b)[NI],
+                                          f32x4 (&acc)[M][NI]) {
 #pragma unroll
-    for (int mi = 0; mi < MI; mi++)
+    for (int mi = 0; mi < NV; mi++)
 #pragma unroll
         for (int ni = 0; ni < NI; ni++)
             acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0)
@@ -181,8 +205,8 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 template <int EPI>
 __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
-    __shared__ int s_dst[EPI == BWD_EPI_MERGE ? BM : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGED];
+    __shared__ int s_dst[EPI == BWD_EPI_MERGE ? BMD : 1];
     int tm, tn;
     const int m_tiles = a.tile_off[a.Ne], n_tiles = (a.N + BN - 1) / BN;
     if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
@@ -197,8 +221,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int seg0 = a.seg_off[p], len = a.seg_off[p + 1] - seg0;
     const int nf = a.phase ? a.first_cnt[p] : 0;
     const int seg = a.phase == 2 ? seg0 + nf : seg0;
-    const int m0 = (tm - a.tile_off[p]) * BM;
-    const int rows = min(BM, (a.phase == 1 ? nf : len - nf) - m0);
+    int m0, rows;
+    split_rows(a.phase == 1 ? nf : len - nf, a.tile_off[p + 1] - a.tile_off[p], tm - a.tile_off[p],
+               m0, rows);
     const int e = a.tab.expert[p];
     const int n0 = tn * BN;
 
@@ -214,11 +239,11 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     }
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     // A: K-contiguous gathered rows, thread rows r0 + 64 i, chunk slot tid & 7
-    const uint16_t *a_src[4];
+    const uint16_t *a_src[A_LDD];
     {
         const int r0 = tid / CHUNKS;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < A_LDD; i++) {
             const int r = min(r0 + 64 * i, rows - 1);
             const int pos = seg + m0 + r;
             const int src = a.a_rows ? a.a_rows[pos] : pos;
@@ -238,57 +263,76 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int wm = w >> 1, wn = w & 1;
     KmajAddr adB;
     kmaj_addr(wn * WN, adB);
-    f32x4 acc[MI][NI];
+    f32x4 acc[MID][NI];
 #pragma unroll
-    for (int mi = 0; mi < MI; mi++)
+    for (int mi = 0; mi < MID; mi++)
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt <= nk; kt++) {
-        // slice kt is issued in iteration kt, consumed in iteration kt + 1
-        if (kt > 0) {
-            wait_all_loads();
-            __syncthreads();
-        }
-        launder(adB);
-        if (kt < nk) {
-            const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGE * 2);
-            const int k0 = kt * BK;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (8 * i + w) * 1024));
-            const uint16_t *brow[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int kk = k0 + kmajor_row(i, w);
-                brow[i] = (kk < a.ksplit ? B1 + static_cast<size_t>(kk) * a.N
-                                         : B2 + static_cast<size_t>(kk - a.ksplit) * a.N) + ncol;
+    // the wave's blocks that hold rows, and its A loads (8-row groups 64 i +
+    // 8 w) that do: the others are neither loaded nor multiplied (their LDS
+    // rows keep stale values, which reach only rows that are never stored)
+    const int nv = __builtin_amdgcn_readfirstlane(
+        min(MID, max(0, (((rows + 15) >> 4) - wm + WAVES_M - 1) / WAVES_M)));
+    const int na = __builtin_amdgcn_readfirstlane(min(A_LDD, max(0, (rows - 8 * w + 63) / 64)));
+    auto k_loop = [&](auto nv_const) {
+        constexpr int NV = decltype(nv_const)::value;
+        for (int kt = 0; kt <= nk; kt++) {
+            // slice kt is issued in iteration kt, consumed in iteration kt + 1
+            if (kt > 0) {
+                wait_all_loads();
+                __syncthreads();
             }
-            issue_kmajor(st + OP * 2, brow, w);
+            launder(adB);
+            if (kt < nk) {
+                const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGED * 2);
+                const int k0 = kt * BK;
+#pragma unroll
+                for (int i = 0; i < A_LDD; i++)
+                    if (i < na)
+                        dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (8 * i + w) * 1024));
+                const uint16_t *brow[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int kk = k0 + kmajor_row(i, w);
+                    brow[i] = (kk < a.ksplit ? B1 + static_cast<size_t>(kk) * a.N
+                                             : B2 + static_cast<size_t>(kk - a.ksplit) * a.N) + ncol;
+                }
+                issue_kmajor(st + OPA * 2, brow, w);
+            }
+            if (kt == 0 || NV == 0) continue;
+            const uint16_t *sA = smem + ((kt - 1) % NSTAGE) * STAGED, *sB = sA + OPA;
+#pragma unroll
+            for (int ks = 0; ks < BK / 32; ks++) {
+                bf16x8_t fa[MID], fb[NI];
+#pragma unroll
+                for (int mi = 0; mi < NV; mi++) fa[mi] = rows_frag(sA, block_row(wm, mi) + (l & 15), ks);
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, adB, ks, ni);
+                mfma_tile<EPI == BWD_EPI_SWIGLU, NV, MID>(fa, fb, acc);
+            }
         }
-        if (kt == 0) continue;
-        const uint16_t *sA = smem + ((kt - 1) % NSTAGE) * STAGE, *sB = sA + OP;
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ks++) {
-            bf16x8_t fa[MI], fb[NI];
-#pragma unroll
-            for (int mi = 0; mi < MI; mi++) fa[mi] = rows_frag(sA, wm * WM + mi * 16 + (l & 15), ks);
-#pragma unroll
-            for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, adB, ks, ni);
-            mfma_tile<EPI == BWD_EPI_SWIGLU>(fa, fb, acc);
-        }
+    };
+    switch (nv) {
+        case MID: k_loop(std::integral_constant<int, MID>{}); break;
+        case MID - 1: k_loop(std::integral_constant<int, MID - 1>{}); break;
+        case MID - 2: k_loop(std::integral_constant<int, MID - 2>{}); break;
+        case MID - 3: k_loop(std::integral_constant<int, MID - 3>{}); break;
+        case MID - 4: k_loop(std::integral_constant<int, MID - 4>{}); break;
+        default: k_loop(std::integral_constant<int, 0>{}); break;
     }
+    static_assert(MID == 5, "the switch above covers 0 .. MID blocks");
 
-    // SWIGLU: acc[mi][ni][v] is row wm*WM + mi*16 + (l & 15), column
+    // SWIGLU: acc[mi][ni][v] is row block_row(wm, mi) + (l & 15), column
     // (relative to the loaded columns) wn*WN + ni*16 + 4*(l >> 4) + v.
-    // MERGE: row wm*WM + mi*16 + 4*(l >> 4) + v, column wn*WN + ni*16 + (l & 15).
-    const int rloc = wm * WM + (l & 15), cloc = wn * WN + 4 * (l >> 4);
+    // MERGE: row block_row(wm, mi) + 4*(l >> 4) + v, column wn*WN + ni*16 + (l & 15).
+    const int cloc = wn * WN + 4 * (l >> 4);
     if constexpr (EPI == BWD_EPI_SWIGLU) {
         // dh -> dg, du (bf16) and this tile half's share of dw = <dh, a>
         const uint16_t *gu = static_cast<const uint16_t *>(a.gu);
         uint16_t *out = static_cast<uint16_t *>(a.out);
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++) {
-            const int r = rloc + mi * 16;
+        for (int mi = 0; mi < MID; mi++) {
+            const int r = block_row(wm, mi) + (l & 15);
             const bool ok = r < rows;
             const int pos = seg + m0 + min(r, rows - 1);
             const float wr = a.row_w ? a.row_w[pos] : 1.f;
@@ -336,10 +380,10 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
         // merge into SFD rows (or dense rows): store, or add
         float *out = a.merge_out;
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+        for (int mi = 0; mi < MID; mi++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const int r = wm * WM + mi * 16 + 4 * (l >> 4) + v;
+                const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
                 if (r >= rows) continue;
                 float *drow = out + static_cast<size_t>(s_dst[r]) * a.N;
 #pragma unroll

@@ -109,7 +109,7 @@ hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s
 hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 
 // --- backward grouped GEMMs, bf16 MFMA (gemm_bwd.hip) ---
-// Input-gradient GEMM over row tiles of 256 (tile_off over the segments
+// Input-gradient GEMM over row tiles of up to kBwdRowTile rows (tile_off over the segments
 // seg_off of placement positions; first_cnt and phase select rows as in
 // DownArgs):  C[pos, :] = A_row . B_e, K contracted, with A_row the K values
 // at column a_col of row a_rows[pos] (or pos) of A (rows lda apart), and row
@@ -122,6 +122,10 @@ hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream
 // Epilogue MERGE: C goes to merge_out[dst_rows[a_rows[pos]]] (identity
 // without dst_rows / a_rows), N wide fp32: stored (merge_store) or added.
 enum { BWD_EPI_SWIGLU = 0, BWD_EPI_MERGE = 1 };
+// Row capacity of the input-gradient tiles: the row schedules tile_off are
+// built with it (ceil(rows / kBwdRowTile) tiles per segment, rows shared out
+// evenly in 16-row blocks).
+constexpr int kBwdRowTile = 320;
 struct BwdDgradArgs {
     const void *A;
     const int32_t *a_rows;
