@@ -20,7 +20,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 size_t elem_bytes(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? 2 : 4; }
 // The grouped GEMM kernels for a shape.  bf16 batches whose experts average
 // fewer than 128 rows (T*k < 128*Ne, e.g. decode steps) take the 64-row
-// tiles: 256-row tiles would spend most of their MFMA work on padding.
+// tiles, whose smaller LDS slices leave room for a third ring slot: such
+// launches stream the weights from HBM.
 struct GemmOps {
     hipError_t (*up)(const UpArgs &, size_t, hipStream_t);
     hipError_t (*down)(const DownArgs &, size_t, hipStream_t);

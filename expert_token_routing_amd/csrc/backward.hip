@@ -1,5 +1,5 @@
-// Small kernels of the backward pass: the 256-row tile schedules of the
-// backward GEMMs, and the router's backward (routing-weight and logit
+// Small kernels of the backward pass: the row-tile schedules of the
+// input-gradient GEMMs, and the router's backward (routing-weight and logit
 // gradients through Eq. 2's full softmax).
 #include "launch.h"
 

@@ -46,7 +46,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr int NT = 512;
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WAVES_M = NT / kWave / 2;            // 4
-constexpr int WM = BM / WAVES_M, WN = BN / 2;      // 64 x 128 per wave
+constexpr int WM = BM / WAVES_M, WN = BN / 2;      // wgrad: 64 x 128 per wave
 constexpr int MI = WM / 16, NI = WN / 16;          // 4 x 8 MFMA blocks
 constexpr int CHUNKS = BK / 8;                     // 16-byte chunks per K-contiguous row
 constexpr int OP = BM * BK;                        // bf16 elements per operand tile
