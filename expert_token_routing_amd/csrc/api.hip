@@ -457,13 +457,11 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     dn.k_split = D.F;
     dn.tab = tab;
     if (det) {
-        // every EPD row stores its own fp32 result; the merge then sums each
-        // SFD row's contributions in slot order
+        // first contributors store into their SFD rows, the others at their
+        // own EPD rows; the merge then adds those to the SFD rows in slot order
         float *y_epd = at<float>(workspace, L.y_epd);
-        dn.rows = nullptr;
-        dn.dst_rows = nullptr;
-        dn.out = y_epd;
-        dn.phase = 0;
+        dn.epd_out = y_epd;
+        dn.phase = 3;
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
         OCC_TRY(mark(6));
@@ -637,10 +635,11 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     g2.epilogue = BWD_EPI_MERGE;
     g2.tab = tab;
     if (det) {
-        // each EPD row's fp32 dx stored at that row; summed per SFD row in
-        // slot order after the shared experts, with the combine
-        g2.dst_rows = nullptr;
-        g2.merge_out = at<float>(workspace, L.y_epd);
+        // first contributors store into their SFD rows of dx, the others at
+        // their own EPD rows; summed per SFD row in slot order after the
+        // shared experts, with the combine
+        g2.epd_out = at<float>(workspace, L.y_epd);
+        g2.split = 1;
         g2.phase = 0;
         g2.tile_off = bt_all;
         g2.merge_store = 1;

@@ -154,6 +154,7 @@ struct Tile {
     int m0;    // first row of the tile inside the segment
     int rows;  // valid rows in the tile (at most BM)
     int n0;    // first column (output feature) of the tile
+    int first; // phase 3: the tile's first `first` rows are first contributors
 };
 
 // A segment of len rows in n = ceil(len / BM) row tiles: its ceil(len / 16)
@@ -168,7 +169,7 @@ __device__ __forceinline__ void split_rows(int len, int n, int j, int &m0, int &
 }
 
 // Routed tiles walk expert segments [seg_off[p], seg_off[p+1]) -- all rows
-// (phase 0), the first first_cnt[p] rows (phase 1) or the rest (phase 2) --
+// (phases 0 and 3), the first first_cnt[p] rows (phase 1) or the rest (phase 2) --
 // with the phase's row-tile schedule tile_off; shared tiles (seg_off NULL)
 // walk M rows.
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
@@ -192,17 +193,19 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
             tm = tile_off[p] + local % r;
         }
         const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
-        const int nf = phase ? first_cnt[p] : 0;
+        const int nf = phase == 1 || phase == 2 ? first_cnt[p] : 0;
         t.e = tab.expert[p];
         t.seg = phase == 2 ? seg0 + nf : seg0;
         split_rows(phase == 1 ? nf : len - nf, tile_off[p + 1] - tile_off[p], tm - tile_off[p],
                    t.m0, t.rows);
+        t.first = phase == 3 ? first_cnt[p] - t.m0 : 0;
     } else {
         const int m_tiles = (M + BM - 1) / BM;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
         t.e = 0;
         t.seg = 0;
         split_rows(M, m_tiles, tm, t.m0, t.rows);
+        t.first = 0;
     }
     t.n0 = tn * n_step;
     return true;
@@ -285,11 +288,14 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 // The wave issues only its first na A loads per slice (the 8-row groups
 // that hold rows; the LDS rows it skips keep stale values, which reach only
 // output rows that are never stored) and multiplies its first NV blocks.
-template <int NV, bool SWAP>
+// pre() runs once the first slices are issued: per-row tables the epilogue
+// needs are loaded there, their latency hidden under those slices' (the
+// loop's first barrier publishes what it writes to LDS).
+template <int NV, bool SWAP, class Pre>
 __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
                                        const uint16_t *const (&b_src)[B_LD], int K, int ksp,
                                        size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
-                                       f32x4_t (&acc)[MI][NI], int na) {
+                                       f32x4_t (&acc)[MI][NI], int na, Pre &pre) {
     constexpr int LOADS = A_LD + B_LD;
     const int per_slice = na + B_LD;  // loads the wave issues per slice
     const int nk = K / BK;
@@ -310,6 +316,7 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
     };
     constexpr int D = NSTAGE - 1;  // slices in flight ahead of the one consumed
     for (int kt = 0; kt < D && kt < nk; kt++) issue(kt);
+    pre();
     for (int kt = 0; kt < nk; kt++) {
         // Slices kt+1 .. min(kt+D, nk)-1 may stay in flight.
         const int ahead = min(kt + D, nk) - 1 - kt;
@@ -323,16 +330,17 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
 }
 
 // Runs the K loop with the wave's block count as a constant.
-template <bool SWAP = false, int NV = MI>
+template <bool SWAP, int NV = MI, class Pre>
 __device__ __forceinline__ void run_k_loop(int nv, const uint16_t *const (&a_src)[A_LD],
                                            const uint16_t *const (&b_src)[B_LD], int K, int ksp,
                                            size_t blk, uint16_t *smem, int wm,
-                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na) {
+                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na,
+                                           Pre &pre) {
     if constexpr (NV == 0) {
-        k_loop<0, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        k_loop<0, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
     } else {
-        if (nv >= NV) k_loop<NV, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
-        else run_k_loop<SWAP, NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+        if (nv >= NV) k_loop<NV, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+        else run_k_loop<SWAP, NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
     }
 }
 
@@ -355,10 +363,6 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
-    // The rows' routing weights, loaded once by one thread per row and
-    // published by the K loop's barriers (loaded by every lane in the
-    // epilogue, they were waited for one by one).
-    if (tid < t.rows) s_w[tid] = a.row_w ? a.row_w[t.seg + t.m0 + tid] : 1.f;
     const int K = a.K, N = a.N;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
@@ -392,7 +396,12 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 
     int nv, na;
     wave_share(t.rows, wm, nv, na);
-    run_k_loop<true>(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na);
+    // The rows' routing weights, loaded once by one thread per row (loaded by
+    // every lane in the epilogue, they were waited for one by one).
+    auto pre = [&] {
+        if (tid < t.rows) s_w[tid] = a.row_w ? a.row_w[t.seg + t.m0 + tid] : 1.f;
+    };
+    run_k_loop<true>(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na, pre);
 
     // SwiGLU + modulation in registers; bf16 tiles staged in LDS (the K
     // buffers are free after the loop's last barrier) and written as whole
@@ -462,15 +471,6 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
         return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
-    // The SFD row of each of the tile's rows, looked up once by one thread
-    // per row (two dependent loads) and published by the K loop's barriers:
-    // looked up by every lane in the epilogue, the lookups ran in series,
-    // one L2 round trip pair per row (measured on the OLMoE-shaped layer:
-    // -10% in the first merge phase, -5% in the atomic phase).
-    if (a.dst_rows && tid < t.rows) {
-        const size_t row = static_cast<size_t>(t.seg) + t.m0 + tid;
-        s_dst[tid] = a.dst_rows[a.rows ? a.rows[row] : static_cast<int>(row)];
-    }
     const int K = a.K, N = a.N, ksp = a.k_split;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
     const uint16_t *a_src[A_LD];
@@ -503,7 +503,21 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 
     int nv, na;
     wave_share(t.rows, wm, nv, na);
-    run_k_loop(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na);
+    // The SFD row of each of the tile's rows, looked up once by one thread
+    // per row (two dependent loads): looked up by every lane in the
+    // epilogue, the lookups ran in series, one L2 round trip pair per row
+    // (measured on the OLMoE-shaped layer: -10% in the first merge phase,
+    // -5% in the atomic phase).  Phase 3 sends the rows after the first
+    // contributors to their own EPD rows instead, marked by a negative entry
+    // ~erow.
+    auto pre = [&] {
+        if (a.dst_rows && tid < t.rows) {
+            const size_t row = static_cast<size_t>(t.seg) + t.m0 + tid;
+            const int erow = a.rows ? a.rows[row] : static_cast<int>(row);
+            s_dst[tid] = a.phase == 3 && tid >= t.first ? ~erow : a.dst_rows[erow];
+        }
+    };
+    run_k_loop<false>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
 
     float *out = a.out;
 #pragma unroll
@@ -514,18 +528,20 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
             if (r >= t.rows) continue;
             const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
             if (a.dst_rows) {
-                const size_t dst = static_cast<size_t>(s_dst[r]) * N;
-                if (a.phase == 1) {
+                const int d = s_dst[r];
+                float *dst = d < 0 ? a.epd_out + static_cast<size_t>(~d) * N
+                                   : out + static_cast<size_t>(d) * N;
+                if (a.phase == 1 || a.phase == 3) {
 #pragma unroll
                     for (int ni = 0; ni < NI; ni++) {
                         const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
-                        if (c < N) out[dst + c] = acc[mi][ni][v];
+                        if (c < N) dst[c] = acc[mi][ni][v];
                     }
                 } else {
 #pragma unroll
                     for (int ni = 0; ni < NI; ni++) {
                         const int c = t.n0 + wn * WN + ni * 16 + (l & 15);
-                        if (c < N) unsafeAtomicAdd(out + dst + c, acc[mi][ni][v]);
+                        if (c < N) unsafeAtomicAdd(dst + c, acc[mi][ni][v]);
                     }
                 }
             } else {

@@ -230,11 +230,14 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
     if constexpr (EPI == BWD_EPI_MERGE) {
         // each row's destination, looked up once per row (not in series by
-        // every lane in the epilogue); the K loop's barriers publish it
+        // every lane in the epilogue); the K loop's barriers publish it.
+        // With split, rows after the segment's first contributors go to
+        // their own EPD rows of epd_out, marked by a negative entry ~erow.
         if (tid < rows) {
             const int pos = seg + m0 + tid;
             const int erow = a.a_rows ? a.a_rows[pos] : pos;
-            s_dst[tid] = a.dst_rows ? a.dst_rows[erow] : erow;
+            s_dst[tid] = a.split && m0 + tid >= a.first_cnt[p] ? ~erow
+                                                               : (a.dst_rows ? a.dst_rows[erow] : erow);
         }
     }
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
@@ -385,7 +388,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             for (int v = 0; v < 4; v++) {
                 const int r = block_row(wm, mi) + 4 * (l >> 4) + v;
                 if (r >= rows) continue;
-                float *drow = out + static_cast<size_t>(s_dst[r]) * a.N;
+                const int d = s_dst[r];
+                float *drow = d < 0 ? a.epd_out + static_cast<size_t>(~d) * a.N
+                                    : out + static_cast<size_t>(d) * a.N;
 #pragma unroll
                 for (int ni = 0; ni < NI; ni++) {
                     const int c = ncol + wn * WN + ni * 16 + (l & 15);

@@ -31,10 +31,12 @@ __device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm)
 
 struct Tile {
     int e, seg, m0, rows, n0;
+    int first;  // phase 3: the tile's first `first` rows are first contributors
 };
 
 // Routed tiles walk expert segments [seg_off[p], seg_off[p+1]) -- all rows
-// (phase 0), the first first_cnt[p] rows (phase 1) or the rest (phase 2).
+// (phases 0 and 3), the first first_cnt[p] rows (phase 1) or the rest
+// (phase 2).
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
                                         int Ne, const PlaceTab &tab, int n_tiles, Tile &t,
                                         const int32_t *first_cnt = nullptr, int phase = 0) {
@@ -43,17 +45,19 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
         if (tm >= tile_off[Ne]) return false;
         const int p = find_pos(tile_off, Ne, tm);
         const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
-        const int nf = phase ? first_cnt[p] : 0;
+        const int nf = phase == 1 || phase == 2 ? first_cnt[p] : 0;
         t.e = tab.expert[p];
         t.seg = phase == 2 ? seg0 + nf : seg0;
         t.m0 = (tm - tile_off[p]) * BM;
         t.rows = min(BM, (phase == 1 ? nf : len - nf) - t.m0);
+        t.first = phase == 3 ? first_cnt[p] - t.m0 : 0;
     } else {
         if (tm * BM >= M) return false;
         t.e = 0;
         t.seg = 0;
         t.m0 = tm * BM;
         t.rows = min(BM, M - t.m0);
+        t.first = 0;
     }
     t.n0 = tn * BN;
     return true;
@@ -175,7 +179,8 @@ __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
             const int c = t.n0 + tx + 16 * j;
             if (c >= N) continue;
             if (!a.dst_rows) a.out[row * N + c] = acc[i][j];
-            else if (a.phase == 1) a.out[static_cast<size_t>(a.dst_rows[erow]) * N + c] = acc[i][j];
+            else if (a.phase == 3 && r >= t.first) a.epd_out[static_cast<size_t>(erow) * N + c] = acc[i][j];
+            else if (a.phase == 1 || a.phase == 3) a.out[static_cast<size_t>(a.dst_rows[erow]) * N + c] = acc[i][j];
             else unsafeAtomicAdd(a.out + static_cast<size_t>(a.dst_rows[erow]) * N + c, acc[i][j]);
         }
     }

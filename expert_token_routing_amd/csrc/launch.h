@@ -46,9 +46,12 @@ hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const P
 hipError_t launch_dispatch(const void *x, int T, int Nd, size_t row_bytes, const int32_t *brim0,
                            void *x_sfd, hipStream_t s, float *zero_out = nullptr,
                            int zero_cols = 0);
-// Deterministic stage one: sfd_out[brim0[g, t]] = sum over the token's experts
-// in group g, in ascending placement position, of y_epd[tok_epd[t, j]] (fp32).
-// With y, also stage two, as launch_combine would compute it (same order).
+// Deterministic stage one: each SFD row holds its first contributor's result
+// (the token's lowest-position expert in the group) and y_epd[tok_epd[t, j]]
+// holds the others'; sfd_out[brim0[g, t]] becomes the sum over the token's
+// experts in group g in ascending placement position (fp32), written back
+// only for groups with several experts.  With y, also stage two, as
+// launch_combine would compute it (same order).
 hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int32_t *tok_epd,
                               const int32_t *brim0, const PlaceTab &tab, int T, int k, int d,
                               float *sfd_out, const float *y_sh, void *y, int y_bf16,
@@ -86,6 +89,9 @@ hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t 
 // out[dst_rows[r], :] = A[r] . W[e]^T, which writes every SFD row once;
 // phase 2 multiplies the others and adds with fp32 atomics (several experts
 // of one group share an SFD row).  tile_off is the phase's row-tile schedule.
+// Phase 3 (the deterministic merge's first half) multiplies every row, with
+// the all-rows schedule: first contributors store into their SFD rows, the
+// others into epd_out at their own EPD rows.
 // Shared (seg_off NULL): out[r, :] = A[r] . W^T with W = n_sh blocks of
 // (N x k_split) laid end to end along K.
 struct DownArgs {
@@ -95,6 +101,7 @@ struct DownArgs {
     const int32_t *rows, *first_cnt;
     const int32_t *dst_rows;
     float *out;
+    float *epd_out;  // phase 3
     int M, K, N, Ne, k_split, phase;
     PlaceTab tab;
 };
@@ -120,7 +127,9 @@ hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream
 // out[pos*out_ld + out_col + f] and + out_uoff, and (dw_part non-NULL)
 // dw_part[pos * dw_stride + q] = this tile half's sum of dh * silu(g) u.
 // Epilogue MERGE: C goes to merge_out[dst_rows[a_rows[pos]]] (identity
-// without dst_rows / a_rows), N wide fp32: stored (merge_store) or added.
+// without dst_rows / a_rows), N wide fp32: stored (merge_store) or added;
+// with split (phase 0), the rows of a segment after its first_cnt first
+// contributors are stored to epd_out[a_rows[pos]] instead.
 enum { BWD_EPI_SWIGLU = 0, BWD_EPI_MERGE = 1 };
 // Row capacity of the input-gradient tiles: the row schedules tile_off are
 // built with it (ceil(rows / kBwdRowTile) tiles per segment, rows shared out
@@ -136,7 +145,8 @@ struct BwdDgradArgs {
     void *out;
     float *dw_part;
     float *merge_out;
-    int N, K, ksplit, Ne, phase, epilogue, dw_stride, merge_store;
+    float *epd_out;
+    int N, K, ksplit, Ne, phase, epilogue, dw_stride, merge_store, split;
     int lda, a_col, gu_ld, gu_col, gu_uoff, out_ld, out_col, out_uoff;
     PlaceTab tab;
 };

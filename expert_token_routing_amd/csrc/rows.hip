@@ -144,8 +144,11 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
 // One wave per token.  Lane j < k holds the token's j-th expert: placement
 // position p_j and EPD row erow_j; after a sort by position (the positions
 // are distinct), lane r holds the r-th.  The walk visits each group's
-// experts together, in slot order (a group's positions are contiguous), and
-// a change of group stores the running fp32 sum as that group's SFD row.
+// experts together, in slot order (a group's positions are contiguous).  A
+// group's first expert (its first contributor) left its result in the
+// group's SFD row, the others at their EPD rows: the walk starts each group
+// from the SFD row, adds the others in turn and writes the row back when
+// there were any (a single-expert group's row is final as it is).
 // With Y, the kernel also finishes the layer as the combine would: the
 // group sums are added in ascending group order (the order in which the walk
 // meets them), then the shared experts' row, and the result is cast once --
@@ -182,45 +185,46 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
             se = ej;
         }
     }
+    // lane r: does it open its group, and the row its result is read from
+    const int sg = sp / tab.n;
+    const int prev_g = __shfl(sg, lane > 0 ? lane - 1 : 0);
+    const int opens = lane == 0 || prev_g != sg;
+    const int src_row = lane < k && opens ? brim0[static_cast<size_t>(sg) * T + t] : se;
     f32x4 acc[VPL], ya[VPL], cur[VPL], nxt[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         ya[i] = acc[i];
     }
-    auto load = [&](int er, f32x4 (&v)[VPL]) {
-        const f32x4 *row = y_epd + static_cast<size_t>(er) * row_vec4;
+    auto load = [&](int r, f32x4 (&v)[VPL]) {
+        const f32x4 *row = (__shfl(opens, r) ? sfd_out : y_epd) +
+                           static_cast<size_t>(__shfl(src_row, r)) * row_vec4;
 #pragma unroll
         for (int i = 0; i < VPL; i++)
             v[i] = __builtin_nontemporal_load(row + min(lane + kWave * i, row_vec4 - 1));
     };
-    auto flush = [&](int g) {
-        const int r = brim0[static_cast<size_t>(g) * T + t];
-        f32x4 *dst = sfd_out + static_cast<size_t>(r) * row_vec4;
-#pragma unroll
-        for (int i = 0; i < VPL; i++) {
-            const int c = lane + kWave * i;
-            if (c < row_vec4) __builtin_nontemporal_store(acc[i], dst + c);
-            if (Y) ya[i] += acc[i];
-            acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-    int cur_g = -1;
-    load(__shfl(se, 0), cur);
+    int cur_srow = 0;
+    load(0, cur);
     for (int r = 0; r < k; r++) {
-        if (r + 1 < k) load(__shfl(se, r + 1), nxt);
-        const int g = __shfl(sp, r) / tab.n;
-        if (g != cur_g) {
-            if (cur_g >= 0) flush(cur_g);
-            cur_g = g;
-        }
+        if (r + 1 < k) load(r + 1, nxt);
+        const bool op = __shfl(opens, r) != 0;
+        const bool closes = r + 1 == k || __shfl(opens, r + 1) != 0;
+        if (op) cur_srow = __shfl(src_row, r);
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
-            acc[i] += cur[i];
+            acc[i] = op ? cur[i] : acc[i] + cur[i];
             cur[i] = nxt[i];
         }
+        if (closes) {
+            f32x4 *dst = sfd_out + static_cast<size_t>(cur_srow) * row_vec4;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) {
+                const int c = lane + kWave * i;
+                if (!op && c < row_vec4) __builtin_nontemporal_store(acc[i], dst + c);
+                if (Y) ya[i] += acc[i];
+            }
+        }
     }
-    flush(cur_g);
     if constexpr (Y != 0) {
         if (y_sh) {
             const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;

@@ -77,11 +77,12 @@ typedef enum occ_prune_rule {
 
 /* Deterministic merge (paper appendix A.2, Algorithm 8, and its remark that
  * the stage-one results may equally be summed serially over the local
- * experts): the down-projection stores every EPD row's fp32 result, then each
- * SFD row is the sum of its contributions in ascending placement position
- * (slot order inside the group), with no atomic adds; the same pass over
- * each token also adds its SFD rows into y (Algorithm 9, in the combine's
- * order).  Every output (y, and with OCC_FLAG_TRAIN every gradient) is then
+ * experts): the down-projection stores each SFD row's first contributor's
+ * fp32 result (the token's lowest-position expert in the group) into that
+ * row and the other EPD rows' results at their own rows; a pass over each
+ * token then adds those to the SFD rows in ascending placement position
+ * (slot order inside the group), with no atomic adds, and adds the SFD rows
+ * into y (Algorithm 9, in the combine's order).  Every output (y, and with OCC_FLAG_TRAIN every gradient) is then
  * bitwise identical from run to run.  The workspace grows by T*k*d fp32. */
 #define OCC_FLAG_DETERMINISTIC 2
 
@@ -178,7 +179,8 @@ enum {
     OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores (one-launch
                                       merge: every row's atomic add;
                                       OCC_FLAG_DETERMINISTIC: every row's
-                                      result stored) */
+                                      result stored, first contributors'
+                                      into their SFD rows) */
     OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds (one-launch
                                       merge: empty; OCC_FLAG_DETERMINISTIC:
                                       the merge and the combine) */
