@@ -403,7 +403,10 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     };
     run_k_loop<true>(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na, pre);
 
-    // SwiGLU + modulation in registers; bf16 tiles staged in LDS (the K
+    // SwiGLU + modulation in registers (the sigmoid's division by the
+    // hardware reciprocal: the result is rounded to bf16, and the IEEE
+    // division sequence made the epilogue -- during which the matrix cores
+    // idle -- several times longer); bf16 tiles staged in LDS (the K
     // buffers are free after the loop's last barrier) and written as whole
     // 16-byte row chunks: the hidden state, then in training the gate and up
     // pre-activations the backward pass reads (two more passes through the
@@ -429,7 +432,8 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
                     const float g = acc[mi][ni][v], u = acc[mi][ni + NI / 2][v];
-                    const float x = which == 0 ? g / (1.f + __expf(-g)) * u * wr : (which == 1 ? g : u);
+                    const float x = which == 0 ? g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u * wr
+                                               : (which == 1 ? g : u);
                     o[v] = f32_to_bf16_bits(x);
                 }
                 *reinterpret_cast<u16x4 *>(smem + r * OUT_PITCH + wn * 64 + ni * 16 + 4 * (l >> 4)) = o;

@@ -361,7 +361,8 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
                     const float g = bf16_bits_to_f32(g4[v]), u = bf16_bits_to_f32(u4[v]);
-                    const float sg = 1.f / (1.f + __expf(-g));
+                    // hardware reciprocal: dg and du are rounded to bf16
+                    const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
                     const float dh = acc[mi][ni][v];
                     part += dh * (g * sg * u);
                     const float da = wr * dh;
