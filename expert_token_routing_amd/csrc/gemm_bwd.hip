@@ -333,24 +333,33 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
         // dh -> dg, du (bf16) and this tile half's share of dw = <dh, a>
         const uint16_t *gu = static_cast<const uint16_t *>(a.gu);
         uint16_t *out = static_cast<uint16_t *>(a.out);
+        // The pre-activations of block mi + 1 are loaded before block mi's
+        // results are stored: a load placed after those stores would wait
+        // for them (the compiler cannot tell the buffers apart), leaving one
+        // load latency per block in series.  The routing weight comes with them.
+        auto row_pos = [&](int mi) { return seg + m0 + min(block_row(wm, mi) + (l & 15), rows - 1); };
+        auto load_gu = [&](int mi, u16x4(&g4)[NI], u16x4(&u4)[NI], float &wr) {
+            wr = a.row_w ? a.row_w[row_pos(mi)] : 1.f;
+            const uint16_t *gr = gu + static_cast<size_t>(row_pos(mi)) * a.gu_ld + a.gu_col;
+#pragma unroll
+            for (int ni = 0; ni < NI; ni++) {
+                const int f = ncol + cloc + ni * 16;
+                g4[ni] = *reinterpret_cast<const u16x4 *>(gr + f);
+                u4[ni] = *reinterpret_cast<const u16x4 *>(gr + a.gu_uoff + f);
+            }
+        };
+        u16x4 g4s[NI], u4s[NI];
+        float wr;
+        load_gu(0, g4s, u4s, wr);
 #pragma unroll
         for (int mi = 0; mi < MID; mi++) {
             const int r = block_row(wm, mi) + (l & 15);
             const bool ok = r < rows;
-            const int pos = seg + m0 + min(r, rows - 1);
-            const float wr = a.row_w ? a.row_w[pos] : 1.f;
-            const uint16_t *gr = gu + static_cast<size_t>(pos) * a.gu_ld + a.gu_col;
+            const int pos = row_pos(mi);
             uint16_t *orow = out + static_cast<size_t>(pos) * a.out_ld + a.out_col;
-            // the row's pre-activations, all loaded before any result is
-            // stored: interleaved with the stores (which the compiler cannot
-            // tell apart from them) each pair was waited for in turn
-            u16x4 g4s[NI], u4s[NI];
-#pragma unroll
-            for (int ni = 0; ni < NI; ni++) {
-                const int f = ncol + cloc + ni * 16;
-                g4s[ni] = *reinterpret_cast<const u16x4 *>(gr + f);
-                u4s[ni] = *reinterpret_cast<const u16x4 *>(gr + a.gu_uoff + f);
-            }
+            u16x4 g4n[NI], u4n[NI];
+            float wrn = 1.f;
+            if (mi + 1 < MID) load_gu(mi + 1, g4n, u4n, wrn);
             float part = 0.f;
 #pragma unroll
             for (int ni = 0; ni < NI; ni++) {
@@ -379,6 +388,14 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
             part += __shfl_xor(part, 32);
             if (a.dw_part && ok && l < 16)
                 a.dw_part[static_cast<size_t>(pos) * a.dw_stride + 2 * tn + wn] = part;
+            if (mi + 1 < MID) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ni++) {
+                    g4s[ni] = g4n[ni];
+                    u4s[ni] = u4n[ni];
+                }
+                wr = wrn;
+            }
         }
     } else {
         // merge into SFD rows (or dense rows): store, or add
