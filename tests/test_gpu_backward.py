@@ -118,11 +118,11 @@ def test_backward_matches_oracle(wl):
                                    occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC],
                          ids=["atomic", "deterministic"])
 def test_backward_row_tile_split_edges(flags):
-    """Experts whose row counts straddle the backward GEMMs' 256-row tiles
-    (and the K range of the weight gradients): no rows, 1, 15-17, 255-257,
-    511-513."""
-    counts = [0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 3]
-    wl = shape("bwd_split_edges", T=sum(counts) // 2, d=256, F=256, Ne=12, k=2, Nd=4, index=16)
+    """Experts whose row counts straddle the input-gradient GEMMs' 320-row
+    tiles (319-321, 639-641) and the weight-gradient GEMMs' 64-deep K slices
+    and 256-row steps (255-257, 511-513), besides no rows, 1 and 15-17."""
+    counts = [0, 1, 15, 16, 17, 255, 256, 257, 319, 320, 321, 511, 512, 513, 639, 640, 641, 3]
+    wl = shape("bwd_split_edges", T=sum(counts) // 2, d=256, F=256, Ne=18, k=2, Nd=6, index=16)
     inp = synth.make_all(wl)
     inp["logits"] = routed_to_counts(counts, wl.k, seed=16)
     got, ref = run(wl, inp=inp, flags=flags)
@@ -150,17 +150,20 @@ def test_backward_rescheduled_placement_and_no_logits():
     check(got, ref, ROUTED)
 
 
-def test_backward_full_size_sampled():
+@pytest.mark.parametrize("flags", [occ.OCC_FLAG_TRAIN,
+                                   occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC],
+                         ids=["atomic", "deterministic"])
+def test_backward_full_size_sampled(flags):
     """The OLMoE-shaped layer at the size bench.py runs (T = 8192), training
-    forward + backward in the benchmark's launch configuration; sampled dx,
-    dw and dlogits rows and sampled rows of two experts' weight gradients
-    against the oracle computed one by one."""
+    forward + backward in the benchmark's launch configuration (either
+    merge); sampled dx, dw and dlogits rows and sampled rows of two experts'
+    weight gradients against the oracle computed one by one."""
     from gpu_common import inputs
     wl = W.OLMOE
     inp = inputs(wl)
     dev = to_dev(inp)
     L = inp["placement"]
-    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN)
+    desc = occ.desc_of(wl, flags=flags)
     ws = occ.alloc_workspace(desc)
     dt = torch.bfloat16
     y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
