@@ -48,9 +48,9 @@ def row_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.abs(got.astype(np.float64) - ref).max(1) / den
 
 
-def forward(wl: W.Workload, inp: dict, placement=None, dev: dict | None = None):
+def forward(wl: W.Workload, inp: dict, placement=None, dev: dict | None = None, flags: int = 0):
     """Run occ_moe_forward; returns (y on host as float64, workspace, views, desc)."""
-    desc = occ.desc_of(wl)
+    desc = occ.desc_of(wl, flags=flags)
     dev = dev or to_dev(inp)
     L = inp["placement"] if placement is None else placement
     ws = occ.alloc_workspace(desc)

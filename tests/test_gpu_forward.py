@@ -58,9 +58,22 @@ FULL = [W.TINY_F32, W.OLMOE, W.DEEPSEEK, W.OLMOE_PRUNED, W.QWEN]
 
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
 def test_forward_full_size_sampled_rows(wl):
+    """Both merges of Algorithm 8 (atomic adds; first contributors stored and
+    the rest summed in slot order) on the same sampled rows."""
     rows = synth.sample_rows(wl.T, 96, seed=wl.index)
-    y, *_ = check_forward(wl, rows)
-    assert np.isfinite(y).all()
+    inp = inputs(wl)
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"], wl.prune_rule,
+                              wl.prune_groups)
+    ref = oracle_rows(wl, inp, rows, ids_o, w_o)
+    dev = to_dev(inp)
+    for flags in (0, occ.OCC_FLAG_DETERMINISTIC):
+        y, ws, v, _ = forward(wl, inp, dev=dev, flags=flags)
+        ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+        assert np.array_equal(ids, ids_o), flags
+        err = row_err(y[rows], ref)
+        assert err.max() <= TOL[wl.dtype], f"{wl.name} flags {flags}: max per-row rel err {err.max():.3e}"
+        assert np.isfinite(y).all()
+        del ws
 
 
 def test_forward_intermediates():
