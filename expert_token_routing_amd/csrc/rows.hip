@@ -141,7 +141,10 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
     }
 }
 
-// One wave per token.  Lane j < k holds the token's j-th expert: placement
+// SPLIT waves per token, each owning VPL * 64 consecutive float4 columns of
+// the row (rows of more than 1024 fp32 values are split, which keeps a
+// wave's registers, and so the waves in flight per CU, within bounds).
+// Lane j < k holds the token's j-th expert: placement
 // position p_j and EPD row erow_j; after a sort by position (the positions
 // are distinct), lane r holds the r-th.  The walk visits each group's
 // experts together, in slot order (a group's positions are contiguous).  A
@@ -159,15 +162,17 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_combine(const f32x4 *__res
 // weights and activations the next step's GEMMs read (measured on the
 // OLMoE-shaped step: -8% here and -2.5% in the following up-projection;
 // -13% in the decode step's up-projection).
-template <int VPL, int Y>  // Y: 0 none, 1 bf16, 2 fp32
+template <int VPL, int Y, int SPLIT>  // Y: 0 none, 1 bf16, 2 fp32
 __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     const f32x4 *__restrict__ y_epd, const int32_t *__restrict__ ids,
     const int32_t *__restrict__ tok_epd, const int32_t *__restrict__ brim0, PlaceTab tab, int T,
     int k, int row_vec4, f32x4 *__restrict__ sfd_out, const f32x4 *__restrict__ y_sh,
     void *__restrict__ y) {
     const int lane = lane_id();
-    const int t = blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    const int gw = blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    const int t = gw / SPLIT;
     if (t >= T) return;
+    const int c0 = (gw - t * SPLIT) * (VPL * kWave) + lane;  // this lane's first float4 column
     int p = 0x7fffffff, erow = 0;
     if (lane < k) {
         const size_t o = static_cast<size_t>(t) * k + lane;
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
                            static_cast<size_t>(__shfl(src_row, r)) * row_vec4;
 #pragma unroll
         for (int i = 0; i < VPL; i++)
-            v[i] = __builtin_nontemporal_load(row + min(lane + kWave * i, row_vec4 - 1));
+            v[i] = __builtin_nontemporal_load(row + min(c0 + kWave * i, row_vec4 - 1));
     };
     int cur_srow = 0;
     load(0, cur);
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
             f32x4 *dst = sfd_out + static_cast<size_t>(cur_srow) * row_vec4;
 #pragma unroll
             for (int i = 0; i < VPL; i++) {
-                const int c = lane + kWave * i;
+                const int c = c0 + kWave * i;
                 if (!op && c < row_vec4) __builtin_nontemporal_store(acc[i], dst + c);
                 if (Y) ya[i] += acc[i];
             }
@@ -229,11 +234,11 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
         if (y_sh) {
             const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
 #pragma unroll
-            for (int i = 0; i < VPL; i++) ya[i] += src[min(lane + kWave * i, row_vec4 - 1)];
+            for (int i = 0; i < VPL; i++) ya[i] += src[min(c0 + kWave * i, row_vec4 - 1)];
         }
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
-            const int c = lane + kWave * i;
+            const int c = c0 + kWave * i;
             if (c >= row_vec4) continue;
             const size_t o = static_cast<size_t>(t) * row_vec4 + c;
             if constexpr (Y == 1) {
@@ -260,25 +265,26 @@ hipError_t launch_merge_slots(const float *y_epd, const int32_t *ids, const int3
                               hipStream_t s) {
     const int row_vec4 = d / 4;
     const int vpl = (row_vec4 + kWave - 1) / kWave;
-    const dim3 grid(ceil_div(T, kRowWaves)), block(kRowWaves * kWave);
+    const dim3 block(kRowWaves * kWave);
     const f32x4 *ye = reinterpret_cast<const f32x4 *>(y_epd);
     f32x4 *so = reinterpret_cast<f32x4 *>(sfd_out);
     const f32x4 *ys = reinterpret_cast<const f32x4 *>(y_sh);
     const int ymode = y ? (y_bf16 ? 1 : 2) : 0;
-#define OCC_MERGE_Y(V, YM) \
-    k_merge_slots<V, YM><<<grid, block, 0, s>>>(ye, ids, tok_epd, brim0, tab, T, k, row_vec4, so, ys, y)
-#define OCC_MERGE(V)                          \
-    do {                                      \
-        if (ymode == 1) OCC_MERGE_Y(V, 1);    \
-        else if (ymode == 2) OCC_MERGE_Y(V, 2); \
-        else OCC_MERGE_Y(V, 0);               \
+#define OCC_MERGE_Y(V, YM, S)                                                             \
+    k_merge_slots<V, YM, S><<<dim3(ceil_div(static_cast<size_t>(T) * S, kRowWaves)), block, 0, \
+                              s>>>(ye, ids, tok_epd, brim0, tab, T, k, row_vec4, so, ys, y)
+#define OCC_MERGE(V, S)                            \
+    do {                                           \
+        if (ymode == 1) OCC_MERGE_Y(V, 1, S);      \
+        else if (ymode == 2) OCC_MERGE_Y(V, 2, S); \
+        else OCC_MERGE_Y(V, 0, S);                 \
     } while (0)
-    if (vpl <= 1) OCC_MERGE(1);
-    else if (vpl <= 2) OCC_MERGE(2);
-    else if (vpl <= 4) OCC_MERGE(4);
-    else if (vpl <= 8) OCC_MERGE(8);
-    else if (vpl <= 16) OCC_MERGE(16);
-    else OCC_MERGE(32);
+    if (vpl <= 1) OCC_MERGE(1, 1);
+    else if (vpl <= 2) OCC_MERGE(2, 1);
+    else if (vpl <= 4) OCC_MERGE(4, 1);
+    else if (vpl <= 8) OCC_MERGE(4, 2);
+    else if (vpl <= 16) OCC_MERGE(4, 4);
+    else OCC_MERGE(4, 8);
 #undef OCC_MERGE
 #undef OCC_MERGE_Y
     return hipGetLastError();
