@@ -19,7 +19,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 size_t elem_bytes(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? 2 : 4; }
 // The grouped GEMM kernels for a shape.  bf16 batches whose experts average
-// fewer than 128 rows (T*k < 128*Ne, e.g. decode steps) take the 64-row
+// fewer than 128 rows (T*k < 128*Ne, e.g. decode steps) take the 128-row
 // tiles, whose smaller LDS slices leave room for a third ring slot: such
 // launches stream the weights from HBM.
 struct GemmOps {
@@ -30,7 +30,7 @@ struct GemmOps {
 GemmOps gemm_ops(const occ_layer_desc &D) {
     if (D.dtype != OCC_BF16) return {launch_gemm_up_f32, launch_gemm_down_f32, kGemmBmF32};
     if (static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne)
-        return {launch_gemm_up_bf16_m64, launch_gemm_down_bf16_m64, kGemmBmBf16Small};
+        return {launch_gemm_up_bf16_m128, launch_gemm_down_bf16_m128, kGemmBmBf16Small};
     return {launch_gemm_up_bf16, launch_gemm_down_bf16, kGemmBmBf16};
 }
 int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
@@ -383,7 +383,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
     OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
     OCC_TRY(mark(2));
-    // Small batches (the same rule as the 64-row tiles) merge in one
+    // Small batches (the same rule as the 128-row tiles) merge in one
     // down-projection launch of atomic adds, whose SFD accumulator rows the
     // dispatch zeroes as it writes the same rows of x_sfd.
     const bool det = D.flags & OCC_FLAG_DETERMINISTIC;

@@ -45,8 +45,8 @@
 // expert's weights and a row tile's activations share one L2.
 // 256-row tiles halve the weight bytes fetched per flop against 128-row
 // tiles (measured: 1.6 vs 2.5 GB beyond L2 per up-projection launch on the
-// OLMoE-shaped layer).  The 64-row build (the decode regime) shares all of
-// this with four single-block wave rows.
+// OLMoE-shaped layer).  The 128-row build (the decode regime) shares all of
+// this with four two-block wave rows.
 #include "launch.h"
 
 namespace occ {
@@ -66,7 +66,7 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 #define OCC_XCD_MAP 1
 #endif
 // One source, two row-tile sizes: this file builds the kGemmBmBf16-row
-// kernels; gemm_bf16_m64.hip includes it with 64-row tiles and suffixed
+// kernels; gemm_bf16_m128.hip includes it with 128-row tiles and suffixed
 // kernel and launcher names.
 #ifndef OCC_GEMM_TILE_M
 #define OCC_GEMM_TILE_M kGemmBmBf16

@@ -8,7 +8,7 @@
 // (ty, tx) owns rows ty + 16*i and columns tx + 16*j (i, j < 4), so the LDS
 // reads of a 16-thread row are consecutive.  K slices of 16 are staged
 // K-major in LDS.  Tile scheduling follows the same per-expert row-tile
-// schedule (64-row tiles) as the bf16 kernels.
+// schedule as the bf16 kernels, with 64-row tiles.
 #include "launch.h"
 
 namespace occ {

@@ -106,10 +106,10 @@ struct DownArgs {
     PlaceTab tab;
 };
 hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
-// The same with 64-row tiles (gemm_bf16_m64.hip).
-constexpr int kGemmBmBf16Small = 64;
-hipError_t launch_gemm_up_bf16_m64(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
-hipError_t launch_gemm_down_bf16_m64(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+// The same with 128-row tiles (gemm_bf16_m128.hip).
+constexpr int kGemmBmBf16Small = 128;
+hipError_t launch_gemm_up_bf16_m128(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
+hipError_t launch_gemm_down_bf16_m128(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 
 // --- the same two GEMMs in fp32 on the vector ALUs (gemm_f32.hip) ---
 hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s);

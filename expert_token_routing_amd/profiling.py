@@ -184,7 +184,7 @@ def _main(argv=None):
         text = summarize_stats(a.dir, a.command, a.title)
     else:
         sources = {"k_gemm_up": "gemm_bf16.hip", "k_gemm_down": "gemm_bf16.hip",
-                   "k_gemm_up_m64": "gemm_bf16.hip", "k_gemm_down_m64": "gemm_bf16.hip",
+                   "k_gemm_up_m128": "gemm_bf16.hip", "k_gemm_down_m128": "gemm_bf16.hip",
                    "k_gate_bf16": "gate.hip", "k_sim_gram": "similarity.hip",
                    "k_dispatch": "rows.hip", "k_combine": "rows.hip",
                    "k_route": "route.hip", "k_brim_fill": "brim.hip"}

@@ -2,7 +2,7 @@
 2.1) against the fp64 oracle within fp32 accumulation's error bound, routing
 on the device's own logits bit for bit, the gated layer to the layer
 tolerance, and both GEMM tile sizes around the point where the library
-switches between them (64-row tiles when T*k < 128*Ne)."""
+switches between them (128-row tiles when T*k < 128*Ne)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +10,8 @@ import torch
 import oracle
 from expert_token_routing_amd import occ, synth, workloads as W
 
-from gpu_common import TOL, W_RTOL, bits, inputs, oracle_rows, row_err, to_dev
+from gpu_common import (TOL, W_RTOL, bits, forward, inputs, oracle_rows, routed_to_counts,
+                        row_err, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -97,10 +98,10 @@ def test_gated_forward_matches_oracle(wl):
     assert row_err(y2.float().cpu().numpy(), y.float().cpu().numpy()).max() <= 1e-2
 
 
-@pytest.mark.parametrize("T", [1023, 1024], ids=["m64_tiles", "m256_tiles"])
+@pytest.mark.parametrize("T", [1023, 1024], ids=["m128_tiles", "m320_tiles"])
 def test_forward_on_both_sides_of_the_tile_switch(T):
-    """OLMoE shape: T*k < 128*Ne below 1024 tokens (64-row tiles), not at 1024
-    (256-row tiles); both against the oracle on sampled rows."""
+    """OLMoE shape: T*k < 128*Ne below 1024 tokens (128-row tiles), not at 1024
+    (tiles of up to 320 rows); both against the oracle on sampled rows."""
     wl = W.scaled(W.OLMOE, T)
     inp = inputs(wl)
     dev = to_dev(inp)
@@ -115,8 +116,33 @@ def test_forward_on_both_sides_of_the_tile_switch(T):
     w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
     tile_off = occ.ws_view(ws, v.brim.tile_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
     epd_off = occ.ws_view(ws, v.brim.epd_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
-    bm = 64 if T * wl.k < 128 * wl.Ne else 320  # tile capacity in rows
+    bm = 128 if T * wl.k < 128 * wl.Ne else 320  # tile capacity in rows
     assert np.array_equal(np.diff(tile_off), (np.diff(epd_off) + bm - 1) // bm)
     rows = synth.sample_rows(wl.T, 128, seed=T)
     ref = oracle_rows(wl, inp, rows, ids, w)
     assert row_err(y.float().cpu().numpy()[rows], ref).max() <= TOL[wl.dtype]
+
+
+def test_small_tile_split_edges():
+    """Small batches (T*k < 128*Ne: 128-row tiles, and with the atomic merge
+    one down-projection launch into rows the dispatch zeroed): experts whose
+    row counts straddle one MFMA block (15-17), half a tile (63-65), one tile
+    (127-129) and two (255-257, shared out over three tiles), besides no rows
+    and 1 -- row by row against the oracle under both merges."""
+    counts = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 2, 35]
+    wl = W.Workload("small_tile_edges", 22, T=sum(counts) // 2, d=256, Ne=16, k=2, Nd=4, F=256,
+                    n_c=4, bonus=1.5)
+    assert wl.T * wl.k < 128 * wl.Ne
+    inp = synth.make_all(wl)
+    inp["logits"] = routed_to_counts(counts, wl.k, seed=22)
+    ids, w = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"])
+    assert np.array_equal(np.bincount(ids.reshape(-1), minlength=wl.Ne), counts)
+    ref = oracle_rows(wl, inp, np.arange(wl.T), ids, w)
+    dev = to_dev(inp)
+    for flags in (0, occ.OCC_FLAG_DETERMINISTIC):
+        y, ws, v, _ = forward(wl, inp, dev=dev, flags=flags)
+        tile_off = occ.ws_view(ws, v.brim.tile_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
+        epd_off = occ.ws_view(ws, v.brim.epd_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
+        assert np.array_equal(np.diff(tile_off), (np.diff(epd_off) + 127) // 128)
+        err = row_err(y, ref)
+        assert err.max() <= TOL[wl.dtype], f"flags {flags}: max per-row rel err {err.max():.3e}"
