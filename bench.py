@@ -274,7 +274,7 @@ def main():
     flops_up = 2.0 * wl.T * wl.k * wl.d * 2 * wl.F
     active = int((torch.diagonal(C) > 0).sum().item())
     bytes_up = (active * 2 * wl.F * wl.d + nsfd_alg1 * wl.d + wl.T * wl.k * wl.F) * es
-    up_kernel = "k_gemm_up_m128" if wl.T * wl.k < 128 * wl.Ne and es == 2 else "k_gemm_up"
+    up_kernel = "k_gemm_up_m128" if wl.T * wl.k < 96 * wl.Ne and es == 2 else "k_gemm_up"
     traffic = profiling.traffic_bytes(up_kernel, wl.name, "gemm_bf16.hip")
     if flops_up / bytes_up >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = flops_up / (up_ms / 1e3) / 1e12

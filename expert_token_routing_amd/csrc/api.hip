@@ -19,9 +19,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 size_t elem_bytes(const occ_layer_desc &D) { return D.dtype == OCC_BF16 ? 2 : 4; }
 // The grouped GEMM kernels for a shape.  bf16 batches whose experts average
-// fewer than 128 rows (T*k < 128*Ne, e.g. decode steps) take the 128-row
-// tiles, whose smaller LDS slices leave room for a third ring slot: such
-// launches stream the weights from HBM.
+// fewer than kSmallTileRows rows (T*k < 96*Ne, e.g. decode steps) take the
+// 128-row tiles, whose smaller LDS slices leave room for a third ring slot:
+// such launches stream the weights from HBM.  The choice is made from the
+// shape alone (nothing is read back): an average of 96 keeps the largest
+// expert within one 128-row tile at the spread of expert loads seen in
+// routed batches (the largest about 1.25x the average), and above it an
+// expert's second 128-row tile costs a round of the CUs that one 320-row
+// tile avoids (OLMoE shape: 128-row tiles 7% faster at 700 tokens, 5%
+// slower at 1000).
 struct GemmOps {
     hipError_t (*up)(const UpArgs &, size_t, hipStream_t);
     hipError_t (*down)(const DownArgs &, size_t, hipStream_t);
@@ -29,7 +35,7 @@ struct GemmOps {
 };
 GemmOps gemm_ops(const occ_layer_desc &D) {
     if (D.dtype != OCC_BF16) return {launch_gemm_up_f32, launch_gemm_down_f32, kGemmBmF32};
-    if (static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne)
+    if (static_cast<int64_t>(D.T) * D.k < static_cast<int64_t>(kSmallTileRows) * D.Ne)
         return {launch_gemm_up_bf16_m128, launch_gemm_down_bf16_m128, kGemmBmBf16Small};
     return {launch_gemm_up_bf16, launch_gemm_down_bf16, kGemmBmBf16};
 }
@@ -383,7 +389,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
     OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
     OCC_TRY(mark(2));
-    // Small batches (the same rule as the 128-row tiles) merge in one
+    // Small batches (experts averaging fewer than 128 rows) merge in one
     // down-projection launch of atomic adds, whose SFD accumulator rows the
     // dispatch zeroes as it writes the same rows of x_sfd.
     const bool det = D.flags & OCC_FLAG_DETERMINISTIC;

@@ -106,8 +106,10 @@ struct DownArgs {
     PlaceTab tab;
 };
 hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
-// The same with 128-row tiles (gemm_bf16_m128.hip).
+// The same with 128-row tiles (gemm_bf16_m128.hip), taken by bf16 batches
+// whose experts average fewer than kSmallTileRows rows.
 constexpr int kGemmBmBf16Small = 128;
+constexpr int kSmallTileRows = 96;
 hipError_t launch_gemm_up_bf16_m128(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 hipError_t launch_gemm_down_bf16_m128(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 
