@@ -86,7 +86,7 @@ typedef enum occ_prune_rule {
  * bitwise identical from run to run.  The workspace grows by T*k*d fp32. */
 #define OCC_FLAG_DETERMINISTIC 2
 
-/* Shape of one MoE layer.  Limits of this build:
+/* Shape of one MoE layer.  Limits of the library:
  *   1 <= T, T*k < 2^31;  1 <= Ne <= 256;  1 <= k <= min(Ne, 32);
  *   1 <= Nd <= 64 and Nd divides Ne (n = Ne/Nd experts per group);
  *   bf16: d, F and F_shared multiples of 64;  fp32: multiples of 16;
