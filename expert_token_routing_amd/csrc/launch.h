@@ -30,7 +30,7 @@ hipError_t launch_sim_gram(const float *H, int T, int Ne, double *gram, hipStrea
 hipError_t launch_sim_rank(const double *gram, int Ne, double *t2, int32_t *rank, hipStream_t s);
 
 // --- BRIM (brim.hip) ---
-constexpr int kBrimChunk = 256;  // tokens per BRIM workgroup
+constexpr int kBrimChunk = 128;  // tokens per BRIM workgroup
 struct BrimBufs {
     int32_t *brim0, *sfd_off, *epd_off, *tile_off, *epd_src, *tok_epd, *brim1;
     float *epd_w;
