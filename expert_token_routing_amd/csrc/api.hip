@@ -422,9 +422,12 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         sd.k_split = D.F_shared;
         sd.tab = tab;
         OCC_HIP(ops.up(su, shared_tiles, s));
+        OCC_TRY(mark(4));
         OCC_HIP(ops.down(sd, shared_tiles, s));
+    } else {
+        OCC_TRY(mark(4));
     }
-    OCC_TRY(mark(4));
+    OCC_TRY(mark(5));
     // Algorithms 6-7: SFD -> EPD, SwiGLU, weight modulation
     UpArgs up{};
     up.A = x_sfd;
@@ -442,7 +445,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     up.Ne = D.Ne;
     up.tab = tab;
     OCC_HIP(ops.up(up, routed_tiles, s));
-    OCC_TRY(mark(5));
+    OCC_TRY(mark(6));
     // Algorithm 8: EPD -> SFD, summed inside each group in fp32.  The first
     // contributor to every SFD row stores (so no zero-fill is needed), then
     // the other rows of the group add with atomics.  Small batches are bound
@@ -470,7 +473,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         dn.phase = 3;
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
-        OCC_TRY(mark(6));
+        OCC_TRY(mark(7));
         // stage one (SFD rows) and, in the same pass over each token, stage
         // two (Algorithm 9) with the combine's order of additions
         OCC_HIP(launch_merge_slots(y_epd, ids, bb.tok_epd, bb.brim0, tab, D.T, D.k, D.d, sfd_out,
@@ -479,20 +482,20 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         dn.phase = 0;
         dn.tile_off = bb.tile_off;
         OCC_HIP(ops.down(dn, routed_tiles, s));
-        OCC_TRY(mark(6));
+        OCC_TRY(mark(7));
     } else {
         dn.phase = 1;
         dn.tile_off = bb.tile_off_first;
         OCC_HIP(ops.down(dn, routed_tiles, s));
-        OCC_TRY(mark(6));
+        OCC_TRY(mark(7));
         dn.phase = 2;
         dn.tile_off = bb.tile_off_rest;
         OCC_HIP(ops.down(dn, routed_tiles, s));
     }
-    OCC_TRY(mark(7));
+    OCC_TRY(mark(8));
     // Algorithm 9: SFD -> ORI across groups (+ shared experts), cast once
     if (!det) OCC_HIP(launch_combine(sfd_out, bb.brim0, y_sh, D.T, D.Nd, D.d, bf16, y, s));
-    OCC_TRY(mark(8));
+    OCC_TRY(mark(9));
     return OCC_OK;
 }
 

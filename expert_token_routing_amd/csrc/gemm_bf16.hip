@@ -256,13 +256,15 @@ __device__ __forceinline__ void mma_slice(const uint16_t *sA, const uint16_t *sB
 // Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).  m0 must be
 // wave-uniform.  Issued as inline assembly because the compiler's builtin
-// does not model the LDS write; completion is tracked with vmcnt below.  M0
-// is reserved by the compiler, which these kernels never use it for (checked
-// in their assembly), so it is set here without a clobber.
+// does not model the LDS write; completion is tracked with vmcnt below.  The
+// LDS address is an input operand bound to M0 ("{m0}"), so the compiler
+// itself writes M0 before the instruction and knows the register is live
+// (M0 is reserved and may not be named as a clobber); the s_nop is the wait
+// state between that write and the load.
 __device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(g), "s"(m0)
+                 : "v"(g), "{m0}"(m0)
                  : "memory");
 }
 

@@ -86,10 +86,13 @@ __device__ __forceinline__ int kmaj(int k, int col) {
     return k * BM + ((((col >> 3) ^ kkey(k))) << 3) + (col & 7);
 }
 
+// Direct global->LDS load (see the forward GEMMs): the LDS address goes to
+// M0 through an input operand bound to that register, so the compiler writes
+// M0 itself and knows it is live.
 __device__ __forceinline__ void dma16(const void *g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(g), "s"(m0)
+                 : "v"(g), "{m0}"(m0)
                  : "memory");
 }
 

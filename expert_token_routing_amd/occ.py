@@ -28,8 +28,8 @@ OCC_FLAG_DETERMINISTIC = 2
 BSTAGES = ["dispatch", "dgrad_down", "dgrad_up", "shared", "combine", "wgrad_down", "wgrad_up",
            "route"]
 OCC_BSTAGE_COUNT = len(BSTAGES)
-STAGES = ["route", "brim", "dispatch", "shared", "gemm_up", "gemm_down_first", "gemm_down_rest",
-          "combine"]
+STAGES = ["route", "brim", "dispatch", "shared_up", "shared_down", "gemm_up", "gemm_down_first",
+          "gemm_down_rest", "combine"]
 OCC_STAGE_COUNT = len(STAGES)
 
 EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route",

@@ -174,18 +174,20 @@ enum {
     OCC_STAGE_ROUTE = 0,
     OCC_STAGE_BRIM = 1,
     OCC_STAGE_DISPATCH = 2,
-    OCC_STAGE_SHARED = 3,
-    OCC_STAGE_GEMM_UP = 4,
-    OCC_STAGE_GEMM_DOWN_FIRST = 5, /* first contributors, plain stores (one-launch
+    OCC_STAGE_SHARED_UP = 3,       /* shared experts' SwiGLU up-projection
+                                      (empty when n_shared = 0) */
+    OCC_STAGE_SHARED_DOWN = 4,     /* shared experts' down-projection */
+    OCC_STAGE_GEMM_UP = 5,
+    OCC_STAGE_GEMM_DOWN_FIRST = 6, /* first contributors, plain stores (one-launch
                                       merge: every row's atomic add;
                                       OCC_FLAG_DETERMINISTIC: every row's
                                       result stored, first contributors'
                                       into their SFD rows) */
-    OCC_STAGE_GEMM_DOWN_REST = 6,  /* the other rows, fp32 atomic adds (one-launch
+    OCC_STAGE_GEMM_DOWN_REST = 7,  /* the other rows, fp32 atomic adds (one-launch
                                       merge: empty; OCC_FLAG_DETERMINISTIC:
                                       the merge and the combine) */
-    OCC_STAGE_COMBINE = 7,         /* OCC_FLAG_DETERMINISTIC: empty */
-    OCC_STAGE_COUNT = 8
+    OCC_STAGE_COMBINE = 8,         /* OCC_FLAG_DETERMINISTIC: empty */
+    OCC_STAGE_COUNT = 9
 };
 
 /* A fixed string naming the status.  Never NULL. */

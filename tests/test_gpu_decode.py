@@ -83,8 +83,8 @@ def test_gated_forward_matches_oracle(wl):
     # routing decided on the device's fp32 logits, by the oracle, bit for bit
     ids_o, w_o = oracle.route(lg, wl.k, L)
     assert np.array_equal(ids, ids_o)
-    np.testing.assert_allclose(w, w_o, rtol=W_RTOL)
-    ref = oracle_rows(wl, inp, np.arange(wl.T), ids, w.astype(np.float64))
+    np.testing.assert_allclose(w, w_o, rtol=W_RTOL, atol=0)
+    ref = oracle_rows(wl, inp, np.arange(wl.T), ids_o, w_o)
     assert row_err(y.float().cpu().numpy(), ref).max() <= TOL[wl.dtype]
     # the same layer through occ_moe_forward on those logits: identical output
     desc = occ.desc_of(wl)
@@ -113,13 +113,16 @@ def test_forward_on_both_sides_of_the_tile_switch(T):
     torch.cuda.synchronize()
     v = occ.occ_forward_views(desc, ws)
     ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
-    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
+    w = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy()
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"])
+    assert np.array_equal(ids, ids_o)
+    np.testing.assert_allclose(w, w_o, rtol=W_RTOL, atol=0)
     tile_off = occ.ws_view(ws, v.brim.tile_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
     epd_off = occ.ws_view(ws, v.brim.epd_off, (wl.Ne + 1,), torch.int32).cpu().numpy()
     bm = 128 if T * wl.k < 96 * wl.Ne else 320  # tile capacity in rows
     assert np.array_equal(np.diff(tile_off), (np.diff(epd_off) + bm - 1) // bm)
     rows = synth.sample_rows(wl.T, 128, seed=T)
-    ref = oracle_rows(wl, inp, rows, ids, w)
+    ref = oracle_rows(wl, inp, rows, ids_o, w_o)
     assert row_err(y.float().cpu().numpy()[rows], ref).max() <= TOL[wl.dtype]
 
 

@@ -12,7 +12,7 @@ import torch
 import oracle
 from expert_token_routing_amd import occ, synth, workloads as W
 
-from gpu_common import TOL, bits, oracle_rows, row_err, to_dev
+from gpu_common import TOL, W_RTOL, bits, oracle_rows, row_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -138,7 +138,7 @@ def test_deterministic_backward_matches_oracle_and_repeats_bitwise():
         torch.cuda.synchronize()
         v = occ.occ_forward_views(desc, ws)
         ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
-        wts = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy().astype(np.float64)
+        wts = occ.ws_view(ws, v.w, (wl.T, wl.k), torch.float32).cpu().numpy()
         return y, out, ids, wts
 
     y0, g0, ids, wts = once()
@@ -146,7 +146,14 @@ def test_deterministic_backward_matches_oracle_and_repeats_bitwise():
     assert torch.equal(y0, y1)
     for key in g0:
         assert torch.equal(g0[key], g1[key]), key
-    ref = oracle.moe_backward(bits(inp["x"]), ids, wts, dy.double().cpu().numpy(),
+    # the training forward against the oracle: ids bit for bit, weights, y
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, L)
+    assert np.array_equal(ids, ids_o)
+    np.testing.assert_allclose(wts, w_o, rtol=W_RTOL, atol=0)
+    ref_y = oracle_rows(wl, inp, np.arange(wl.T), ids_o, w_o)
+    assert row_err(y0.float().cpu().numpy(), ref_y).max() <= TOL[wl.dtype]
+    # the oracle's backward on the oracle's own routing
+    ref = oracle.moe_backward(bits(inp["x"]), ids_o, w_o, dy.double().cpu().numpy(),
                               bits(inp["w_gate"]), bits(inp["w_up"]), bits(inp["w_down"]),
                               bits(inp["ws_gate"]), bits(inp["ws_up"]), bits(inp["ws_down"]),
                               logits=inp["logits"].numpy())

@@ -3,7 +3,8 @@ Eq. 1 output, and of its intermediates: the dispatched SFD replicas (a pure
 copy, bit-exact), the modulated EPD hidden states and the stage-one SFD sums
 (within tolerance).  Small ragged sizes are checked on every row; the full
 workload sizes, in the launch configuration the benchmark times, on a seeded
-sample of rows."""
+sample of rows, and the OLMoE-shaped workloads (T = 8192 and the pruned
+T = 32768) on every row."""
 import numpy as np
 import pytest
 import torch
@@ -56,23 +57,59 @@ def test_forward_small_all_rows(wl):
 FULL = [W.TINY_F32, W.OLMOE, W.DEEPSEEK, W.OLMOE_PRUNED, W.QWEN]
 
 
+def alg1_placement(wl, inp):
+    """Algorithm 1 on the batch's co-activation counts, computed by the oracle
+    (the placement the benchmark times)."""
+    ids0, _ = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"], wl.prune_rule,
+                           wl.prune_groups)
+    return oracle.placement(oracle.coact(ids0, wl.Ne, inp["placement"])["C"], wl.Nd)
+
+
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
 def test_forward_full_size_sampled_rows(wl):
     """Both merges of Algorithm 8 (atomic adds; first contributors stored and
-    the rest summed in slot order) on the same sampled rows."""
+    the rest summed in slot order) on the same sampled rows, under the
+    contiguous placement and under Algorithm 1's (the benchmark's launch
+    configuration: Algorithm 1, deterministic merge)."""
     rows = synth.sample_rows(wl.T, 96, seed=wl.index)
     inp = inputs(wl)
-    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, inp["placement"], wl.prune_rule,
-                              wl.prune_groups)
-    ref = oracle_rows(wl, inp, rows, ids_o, w_o)
     dev = to_dev(inp)
-    for flags in (0, occ.OCC_FLAG_DETERMINISTIC):
-        y, ws, v, _ = forward(wl, inp, dev=dev, flags=flags)
+    for L in (inp["placement"], alg1_placement(wl, inp)):
+        ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
+        ref = oracle_rows(wl, inp, rows, ids_o, w_o)
+        for flags in (0, occ.OCC_FLAG_DETERMINISTIC):
+            y, ws, v, _ = forward(wl, inp, L, dev=dev, flags=flags)
+            ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
+            assert np.array_equal(ids, ids_o), flags
+            err = row_err(y[rows], ref)
+            assert err.max() <= TOL[wl.dtype], \
+                f"{wl.name} flags {flags}: max per-row rel err {err.max():.3e}"
+            assert np.isfinite(y).all()
+            del ws
+
+
+@pytest.mark.parametrize("wl", [W.OLMOE, W.OLMOE_PRUNED], ids=lambda w: w.name)
+def test_forward_full_size_every_row(wl):
+    """The OLMoE-shaped layer (T = 8192) and its pruned form (T = 32768,
+    GROUPSUM over 2 of 8 groups) at full size: every row of y against Eq. 1
+    under both merges -- Occult's path reaches exactly the standard top-k
+    MoE output (paper, section 3.2) -- and, unpruned, under Algorithm 1's
+    placement too (Eq. 1 does not depend on the placement)."""
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    L0 = inp["placement"]
+    ids_o, w_o = oracle.route(inp["logits"].numpy(), wl.k, L0, wl.prune_rule, wl.prune_groups)
+    ref = oracle_rows(wl, inp, np.arange(wl.T), ids_o, w_o)
+    cases = [(L0, 0), (L0, occ.OCC_FLAG_DETERMINISTIC)]
+    if wl.prune_rule == W.PRUNE_OFF:
+        cases.append((alg1_placement(wl, inp), occ.OCC_FLAG_DETERMINISTIC))
+    for L, flags in cases:
+        y, ws, v, _ = forward(wl, inp, L, dev=dev, flags=flags)
         ids = occ.ws_view(ws, v.ids, (wl.T, wl.k), torch.int32).cpu().numpy()
         assert np.array_equal(ids, ids_o), flags
-        err = row_err(y[rows], ref)
-        assert err.max() <= TOL[wl.dtype], f"{wl.name} flags {flags}: max per-row rel err {err.max():.3e}"
-        assert np.isfinite(y).all()
+        err = row_err(y, ref)
+        assert err.max() <= TOL[wl.dtype], \
+            f"{wl.name} flags {flags}: max per-row rel err {err.max():.3e} at row {err.argmax()}"
         del ws
 
 

@@ -9,7 +9,7 @@ import torch
 import oracle
 from expert_token_routing_amd import occ, synth, workloads as W
 
-from gpu_common import W_RTOL, inputs, oracle_route
+from gpu_common import W_RTOL, inputs, oracle_route, weight_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,8 @@ def test_route_full_size(wl):
     ids_o, w_o = oracle.route(logits.numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
     assert np.array_equal(ids, ids_o)
     np.testing.assert_allclose(w, w_o, rtol=W_RTOL, atol=0)
+    # and within the error bound of the device's fp32 softmax arithmetic
+    assert np.all(np.abs(w - w_o) <= weight_bound(logits.numpy(), ids_o) * w_o)
     if wl.prune_rule:
         grp = np.repeat(np.arange(wl.Nd), wl.n)
         spans = np.array([len(set(grp[r].tolist())) for r in ids])
