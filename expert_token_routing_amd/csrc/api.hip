@@ -1,6 +1,7 @@
 // C ABI of the Occult MoE-layer library: argument checks, workspace layout,
 // and the stage sequence of the layer (declarations and contracts in occ.h).
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -10,6 +11,15 @@
 #pragma GCC visibility pop
 
 using namespace occ;
+
+// The allocation-free forward's workspace: a file-scope device array that
+// each GPU holds (at its own address) from the library's load until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol;
+// its device address on the current GPU is looked up once per device with
+// hipGetSymbolAddress (noalloc_scratch below) and that address is what
+// kernels receive.  Every call on one GPU uses the same array, so calls that
+// overlap on a GPU race.
+static __device__ __align__(256) unsigned char scratch[OCC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -218,6 +228,25 @@ BrimBufs brim_bufs(void *ws, const Layout &L) {
 }
 
 occ_status hip_status(hipError_t e) { return e == hipSuccess ? OCC_OK : OCC_ERR_HIP; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+occ_status noalloc_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return OCC_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return OCC_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return OCC_ERR_HIP;
+        if (reinterpret_cast<uintptr_t>(p) % kAlign != 0) return OCC_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return OCC_OK;
+}
 
 #define OCC_TRY(expr)                              \
     do {                                           \
@@ -507,6 +536,24 @@ occ_status occ_moe_forward(const occ_layer_desc *desc, const void *x, const floa
     if (!logits) return OCC_ERR_INVALID_ARG;
     return forward(desc, x, logits, nullptr, nullptr, nullptr, placement_host, w_gate, w_up,
                    w_down, ws_gate, ws_up, ws_down, y, workspace, ws_bytes, stage_events, stream);
+}
+
+occ_status occ_moe_forward_noalloc(const occ_layer_desc *desc, const void *x, const float *logits,
+                                   const int32_t *placement_host, const void *w_gate,
+                                   const void *w_up, const void *w_down, const void *ws_gate,
+                                   const void *ws_up, const void *ws_down, void *y,
+                                   void *const *stage_events, void *stream) {
+    OCC_TRY(check_desc(desc));
+    if (!logits) return OCC_ERR_INVALID_ARG;
+    // the backward pass reads the training forward's state from a caller
+    // workspace, which this variant does not have
+    if (desc->flags & OCC_FLAG_TRAIN) return OCC_ERR_UNSUPPORTED;
+    if (layout(*desc).total > OCC_NOALLOC_SCRATCH_BYTES) return OCC_ERR_WORKSPACE;
+    void *ws = nullptr;
+    OCC_TRY(noalloc_scratch(&ws));
+    return forward(desc, x, logits, nullptr, nullptr, nullptr, placement_host, w_gate, w_up,
+                   w_down, ws_gate, ws_up, ws_down, y, ws, OCC_NOALLOC_SCRATCH_BYTES,
+                   stage_events, stream);
 }
 
 occ_status occ_moe_forward_gated(const occ_layer_desc *desc, const void *x, const void *w_router,

@@ -25,6 +25,7 @@ OCC_F32, OCC_BF16 = 0, 1
 OCC_PRUNE_OFF, OCC_PRUNE_TRAVERSE, OCC_PRUNE_GROUPSUM, OCC_PRUNE_SIMILARITY = 0, 1, 2, 3
 OCC_FLAG_TRAIN = 1
 OCC_FLAG_DETERMINISTIC = 2
+OCC_NOALLOC_SCRATCH_BYTES = 128 << 20
 BSTAGES = ["dispatch", "dgrad_down", "dgrad_up", "shared", "combine", "wgrad_down", "wgrad_up",
            "route"]
 OCC_BSTAGE_COUNT = len(BSTAGES)
@@ -37,7 +38,7 @@ EXPORTED = ["occ_status_string", "occ_workspace_size", "occ_route",
             "occ_build_brim", "occ_moe_forward", "occ_moe_forward_routed", "occ_gate",
             "occ_moe_forward_gated", "occ_moe_backward", "occ_forward_views",
             "occ_coactivation_stats", "occ_place_experts", "occ_events_create",
-            "occ_events_destroy", "occ_event_elapsed_ms"]
+            "occ_events_destroy", "occ_event_elapsed_ms", "occ_moe_forward_noalloc"]
 
 
 class OccError(RuntimeError):
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
                                ctypes.c_int),
             "occ_moe_forward": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp],
                                 ctypes.c_int),
+            "occ_moe_forward_noalloc": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+                                        ctypes.c_int),
             "occ_moe_forward_routed": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         vp, vp], ctypes.c_int),
             "occ_gate": ([dp, vp, vp, vp, vp], ctypes.c_int),
@@ -240,6 +243,31 @@ def occ_moe_forward(desc: LayerDesc, x, logits, placement, w_gate, w_up, w_down,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
         "occ_moe_forward")
+
+
+def occ_moe_forward_noalloc(desc: LayerDesc, x, logits, placement, w_gate, w_up, w_down, ws_gate,
+                            ws_up, ws_down, y, stage_events=None, stream=None):
+    """occ_moe_forward with the library's static per-GPU scratch array as the
+    workspace (nothing allocated; shapes up to OCC_NOALLOC_SCRATCH_BYTES of
+    workspace; calls on one GPU must not overlap)."""
+    T, d, Ne, F = desc.T, desc.d, desc.Ne, desc.F
+    dt = torch.bfloat16 if desc.dtype == OCC_BF16 else torch.float32
+    L = _host_i32(placement, "placement", (desc.Nd, Ne // desc.Nd))
+    nsh, Fsh = desc.n_shared, desc.F_shared
+    sh = [None, None, None]
+    if nsh > 0:
+        sh = [_dev(ws_gate, "ws_gate", dt, (nsh, Fsh, d)), _dev(ws_up, "ws_up", dt, (nsh, Fsh, d)),
+              _dev(ws_down, "ws_down", dt, (nsh, d, Fsh))]
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * (OCC_STAGE_COUNT + 1))(*stage_events)
+    _check(lib().occ_moe_forward_noalloc(
+        ctypes.byref(desc), _dev(x, "x", dt, (T, d)),
+        _dev(logits, "logits", torch.float32, (T, Ne)), _hp(L),
+        _dev(w_gate, "w_gate", dt, (Ne, F, d)), _dev(w_up, "w_up", dt, (Ne, F, d)),
+        _dev(w_down, "w_down", dt, (Ne, d, F)), *sh, _dev(y, "y", dt, (T, d)),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
+        "occ_moe_forward_noalloc")
 
 
 def occ_moe_forward_routed(desc: LayerDesc, x, ids, w, placement, w_gate, w_up, w_down, ws_gate,

@@ -324,6 +324,33 @@ occ_status occ_moe_forward_routed(const occ_layer_desc *desc, const void *x, con
                                   void *y, void *workspace, size_t ws_bytes,
                                   void *const *stage_events, void *stream);
 
+/* Bytes of the device array that occ_moe_forward_noalloc uses as its
+ * workspace (128 MiB, held on every GPU the library runs on until the
+ * process ends). */
+#define OCC_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* occ_moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the intermediates live in a static
+ * device array of OCC_NOALLOC_SCRATCH_BYTES, one per GPU.  Nothing is
+ * allocated or freed; the caller still passes inputs and outputs, with the
+ * meaning, layouts and stream semantics of occ_moe_forward.  Shapes whose
+ * occ_workspace_size exceeds OCC_NOALLOC_SCRATCH_BYTES return
+ * OCC_ERR_WORKSPACE (e.g. the OLMoE shape, d = 2048, 64 experts of F = 1024,
+ * top-8, fits up to about 1,100 tokens, or 700 with
+ * OCC_FLAG_DETERMINISTIC); OCC_FLAG_TRAIN returns OCC_ERR_UNSUPPORTED (the
+ * backward pass reads its state from a caller workspace).  The first call on
+ * a GPU looks up the array's device address there; later calls reuse it.
+ * All calls on one GPU share that GPU's array and it keeps the last call's
+ * contents: calls that may overlap on one GPU (several streams or host
+ * threads) race and must be ordered by the caller.  The intermediates are
+ * not exposed (occ_forward_views needs a caller workspace). */
+occ_status occ_moe_forward_noalloc(const occ_layer_desc *desc, const void *x, const float *logits,
+                                   const int32_t *placement_host, const void *w_gate,
+                                   const void *w_up, const void *w_down, const void *ws_gate,
+                                   const void *ws_up, const void *ws_down, void *y,
+                                   void *const *stage_events, void *stream);
+
 /* Stages timed by occ_moe_backward when given events. */
 enum {
     OCC_BSTAGE_DISPATCH = 0,    /* dy ORI -> SFD (BRIM_0) */
