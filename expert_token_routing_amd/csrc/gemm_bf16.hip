@@ -40,9 +40,10 @@
 // A wave skips the MFMAs and the direct loads of blocks that hold no rows.
 // Workgroup b runs on
 // XCD b % 8; tiles are renumbered so that each XCD takes a contiguous range
-// of an expert-major tile order (column tiles outer, row tiles inner inside
-// an expert, except in the atomic merge phase): the workgroups sharing an
-// expert's weights and a row tile's activations share one L2.
+// of an expert-major tile order (inside an expert, bands of 8 row tiles
+// walked column by column, except in the atomic merge phase; a dense product
+// the same way): the workgroups sharing an expert's weights and a row tile's
+// activations share one L2.
 // 256-row tiles halve the weight bytes fetched per flop against 128-row
 // tiles (measured: 1.6 vs 2.5 GB beyond L2 per up-projection launch on the
 // OLMoE-shaped layer).  The 128-row build (the decode regime) shares all of
@@ -137,6 +138,29 @@ __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int 
     return true;
 }
 
+// Order of the tiles of one expert (or of a dense product): an r x c grid of
+// row x column tiles is walked in bands of OCC_GEMM_BAND row tiles, and
+// inside a band column by column, so the 32 workgroups an XCD runs at a time
+// hold 8 row tiles x 4 column tiles of one band (448 KB of distinct operand
+// bytes per 64-deep K slice at 320 x 256 tiles) rather than one row tile x 32
+// column tiles (the row-major order of a dense product: 1.06 MB) or, for an
+// expert of 14 row tiles walked column by column, 14 x 2-3 (650 KB).
+// Measured (bands of 1, 2, 4, 8 and unbounded): 8 is best, though by little
+// -- the Qwen-shaped layer's step -1.5%, the OLMoE- and DeepSeek-shaped ones
+// -0.5% against unbounded bands -- so L2 reuse is not what bounds these
+// GEMMs.  Local index `local` -> (row tile lm, column tn).
+#ifndef OCC_GEMM_BAND
+#define OCC_GEMM_BAND 8
+#endif
+__device__ __forceinline__ void band_order(int local, int r, int c, int &lm, int &tn) {
+    const int band = local / (OCC_GEMM_BAND * c);
+    const int rb0 = band * OCC_GEMM_BAND;
+    const int rb = min(OCC_GEMM_BAND, r - rb0);
+    const int idx = local - band * OCC_GEMM_BAND * c;
+    tn = idx / rb;
+    lm = rb0 + idx - tn * rb;
+}
+
 // Placement position owning row tile tm: the last p with tile_off[p] <= tm.
 __device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
     int lo = 0, hi = Ne;
@@ -182,15 +206,16 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
         const int p = find_pos(tile_off, Ne, tm);
         if (phase != 2) {
-            // Column tiles outermost inside each expert: the workgroups that
-            // run together on an XCD then share fewer weight column tiles
-            // (the larger share of the L2 misses).  Measured on the
-            // OLMoE-shaped layer: -4% in the up-projection and in the first
-            // merge phase; the atomic phase is faster in row order.
-            const int r = tile_off[p + 1] - tile_off[p];
-            const int local = (tm - tile_off[p]) * n_tiles + tn;
-            tn = local / r;
-            tm = tile_off[p] + local % r;
+            // Bands of row tiles, column tiles outermost inside a band: the
+            // workgroups that run together on an XCD then share fewer weight
+            // column tiles (the larger share of the L2 misses).  Column tiles
+            // outermost was measured on the OLMoE-shaped layer at -4% in the
+            // up-projection and in the first merge phase against row order;
+            // the atomic phase is faster in row order.
+            int lm;
+            band_order((tm - tile_off[p]) * n_tiles + tn, tile_off[p + 1] - tile_off[p], n_tiles,
+                       lm, tn);
+            tm = tile_off[p] + lm;
         }
         const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
         const int nf = phase == 1 || phase == 2 ? first_cnt[p] : 0;
@@ -202,6 +227,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     } else {
         const int m_tiles = (M + BM - 1) / BM;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
+        band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn);
         t.e = 0;
         t.seg = 0;
         split_rows(M, m_tiles, tm, t.m0, t.rows);
