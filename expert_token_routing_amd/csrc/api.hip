@@ -12,6 +12,23 @@
 
 using namespace occ;
 
+namespace occ {
+int compute_units() {
+    constexpr int kDevices = 64;
+    static int cached[kDevices] = {};  // 0: not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+    int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
+}
+}  // namespace occ
+
 // The allocation-free forward's workspace: a file-scope device array that
 // each GPU holds (at its own address) from the library's load until the
 // process ends.  In host code `scratch` is only a stand-in for the symbol;

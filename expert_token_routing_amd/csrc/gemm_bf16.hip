@@ -48,6 +48,8 @@
 // tiles (measured: 1.6 vs 2.5 GB beyond L2 per up-projection launch on the
 // OLMoE-shaped layer).  The 128-row build (the decode regime) shares all of
 // this with four two-block wave rows.
+#include <algorithm>
+
 #include "launch.h"
 
 namespace occ {
@@ -197,9 +199,9 @@ __device__ __forceinline__ void split_rows(int len, int n, int j, int &m0, int &
 // with the phase's row-tile schedule tile_off; shared tiles (seg_off NULL)
 // walk M rows.
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
-                                        int Ne, const PlaceTab &tab, int n_tiles, int n_step,
-                                        Tile &t, const int32_t *first_cnt = nullptr,
-                                        int phase = 0) {
+                                        int m_tiles_dense, int Ne, const PlaceTab &tab,
+                                        int n_tiles, int n_step, Tile &t,
+                                        const int32_t *first_cnt = nullptr, int phase = 0) {
     int tm, tn;
     if (seg_off) {
         const int m_tiles = tile_off[Ne];
@@ -225,7 +227,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
                    t.m0, t.rows);
         t.first = phase == 3 ? first_cnt[p] - t.m0 : 0;
     } else {
-        const int m_tiles = (M + BM - 1) / BM;
+        const int m_tiles = m_tiles_dense;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
         band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn);
         t.e = 0;
@@ -394,7 +396,8 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     __shared__ float s_w[BM];
     Tile t;
-    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + 127) / 128, 128, t)) return;
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.m_tiles, a.Ne, a.tab, (a.N + 127) / 128, 128, t))
+        return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N;
@@ -504,8 +507,8 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     __shared__ int s_dst[BM];
     Tile t;
-    if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t, a.first_cnt,
-                 a.phase))
+    if (!tile_of(a.seg_off, a.tile_off, a.M, a.m_tiles, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t,
+                 a.first_cnt, a.phase))
         return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
@@ -597,19 +600,47 @@ unsigned grid_for(size_t m_tiles, size_t n_tiles) {
     return static_cast<unsigned>(8 * ((total + 7) / 8));
 }
 
+// Row tiles of a dense product of M rows against n_tiles column tiles: the
+// fewest that hold every row (ceil(M / BM)), raised as far as the launch
+// still takes the same number of rounds of the GPU's workgroup slots, so the
+// last round is filled with shorter tiles instead of running partly empty
+// (the Qwen-shaped layer's shared down-projection: 205 x 8 tiles are 6.4
+// rounds of 256 CUs, run as 7; 224 x 8 tiles of 293 rows fill the 7 rounds).
+// At most one 16-row block per tile.
+int dense_row_tiles(int M, int n_tiles) {
+    const int m0 = static_cast<int>(ceil_div(M, BM));
+    const long slots = static_cast<long>(compute_units()) * OCC_GEMM_WG_PER_CU;
+    if (m0 == 0 || n_tiles == 0 || slots <= 0) return m0;
+    const long rounds = (static_cast<long>(m0) * n_tiles + slots - 1) / slots;
+    const long m = std::min<long>(rounds * slots / n_tiles, (M + 15) / 16);
+    return static_cast<int>(std::max<long>(m0, m));
+}
+
 }  // namespace
 
 hipError_t OCC_NAMED(launch_gemm_up_bf16)(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
-    const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, 128));
+    UpArgs b = a;
+    const int n_tiles = static_cast<int>(ceil_div(a.N, 128));
+    if (!a.seg_off) {
+        b.m_tiles = dense_row_tiles(a.M, n_tiles);
+        max_m_tiles = static_cast<size_t>(b.m_tiles);
+    }
+    const unsigned grid = grid_for(max_m_tiles, n_tiles);
     if (grid == 0) return hipSuccess;
-    OCC_NAMED(k_gemm_up)<<<grid, NT, 0, s>>>(a);
+    OCC_NAMED(k_gemm_up)<<<grid, NT, 0, s>>>(b);
     return hipGetLastError();
 }
 
 hipError_t OCC_NAMED(launch_gemm_down_bf16)(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
-    const unsigned grid = grid_for(max_m_tiles, ceil_div(a.N, BN));
+    DownArgs b = a;
+    const int n_tiles = static_cast<int>(ceil_div(a.N, BN));
+    if (!a.seg_off) {
+        b.m_tiles = dense_row_tiles(a.M, n_tiles);
+        max_m_tiles = static_cast<size_t>(b.m_tiles);
+    }
+    const unsigned grid = grid_for(max_m_tiles, n_tiles);
     if (grid == 0) return hipSuccess;
-    OCC_NAMED(k_gemm_down)<<<grid, NT, 0, s>>>(a);
+    OCC_NAMED(k_gemm_down)<<<grid, NT, 0, s>>>(b);
     return hipGetLastError();
 }
 

@@ -7,6 +7,9 @@
 
 namespace occ {
 
+// Compute units of the current device (read once per device; 256 on MI355X).
+int compute_units();
+
 // --- routing (route.hip) ---
 // prune_rule 0 none, 1 TRAVERSE, 2 GROUPSUM, 3 similarity (sim_rank: Ne x Ne
 // ranked table, used only by rule 3).
@@ -80,6 +83,7 @@ struct UpArgs {
     void *gu_out;
     int M, K, N, Ne;
     PlaceTab tab;
+    int m_tiles;  // dense mode: row tiles (set by the bf16 launchers)
 };
 hipError_t launch_gemm_up_bf16(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 
@@ -104,6 +108,7 @@ struct DownArgs {
     float *epd_out;  // phase 3
     int M, K, N, Ne, k_split, phase;
     PlaceTab tab;
+    int m_tiles;  // dense mode: row tiles (set by the bf16 launchers)
 };
 hipError_t launch_gemm_down_bf16(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 // The same with 128-row tiles (gemm_bf16_m128.hip), taken by bf16 batches
