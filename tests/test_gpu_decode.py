@@ -69,9 +69,25 @@ def gated_forward(wl, dev, L):
     return y, lg, ids, w
 
 
+def gate_error_bound(x, wr, d):
+    """Per (token, expert) bound on |device fp32 logit - exact logit|: fp32
+    accumulation of d exact bf16 products, d u / (1 - d u) sum |x_i w_i|."""
+    u = 2.0 ** -24
+    mag = np.abs(x.double().numpy()) @ np.abs(wr.double().numpy()).T
+    return d * u / (1 - d * u) * mag
+
+
 @pytest.mark.parametrize("wl", [W.OLMOE_DECODE, W.scaled(W.DEEPSEEK, 261)],
                          ids=["olmoe_decode", "deepseek_shared"])
 def test_gated_forward_matches_oracle(wl):
+    """The gated layer against the oracle's own pipeline: its fp64 gate
+    rounded to fp32, its router, its Eq. 1.  The device's logits differ from
+    the oracle's by at most E = (fp32 accumulation bound) + (the oracle's
+    fp32 rounding) per entry, so a token's ids must equal the oracle's bit
+    for bit unless two of its logits that decide the ordered top-k (the
+    k+1 largest) lie within 2E of each other; there the device's list must
+    still be a valid ordered top-k under that bound.  y and w are compared
+    on the tokens whose ids equal the oracle's."""
     inp = inputs(wl)  # the DeepSeek case shares the plain forward tests' tensors
     if inp["w_router"] is None:
         inp = dict(inp, w_router=synth.make_router_weights(wl))
@@ -80,13 +96,35 @@ def test_gated_forward_matches_oracle(wl):
     y, lg, ids, w = gated_forward(wl, dev, L)
     # the logits in the workspace are occ_gate's
     assert np.array_equal(lg, gpu_gate(wl, inp["x"], inp["w_router"]))
-    # routing decided on the device's fp32 logits, by the oracle, bit for bit
-    ids_o, w_o = oracle.route(lg, wl.k, L)
-    assert np.array_equal(ids, ids_o)
-    np.testing.assert_allclose(w, w_o, rtol=W_RTOL, atol=0)
-    ref = oracle_rows(wl, inp, np.arange(wl.T), ids_o, w_o)
-    assert row_err(y.float().cpu().numpy(), ref).max() <= TOL[wl.dtype]
-    # the same layer through occ_moe_forward on those logits: identical output
+    # the oracle's routing on its own logits
+    lg_o = oracle.gate(np.arange(wl.T), bits(inp["x"]), bits(inp["w_router"]))
+    ids_o, w_o = oracle.route(lg_o.astype(np.float32), wl.k, L)
+    E = gate_error_bound(inp["x"], inp["w_router"], wl.d) + 2.0 ** -24 * np.abs(lg_o)
+    Et = E.max(1)
+    srt = -np.sort(-lg_o, axis=1)[:, :wl.k + 1]
+    close = (srt[:, :-1] - srt[:, 1:] <= 2 * Et[:, None]).any(1)
+    same = (ids == ids_o).all(1)
+    # a differing token must be one whose deciding logits are within 2E
+    assert np.all(same | close), np.flatnonzero(~(same | close))[:10]
+    for t in np.flatnonzero(~same):
+        sel = ids[t].astype(np.int64)
+        assert len(set(sel.tolist())) == wl.k
+        l = lg_o[t]
+        # ordered within the bound, and no unselected expert clearly above
+        assert np.all(l[sel[:-1]] >= l[sel[1:]] - 2 * Et[t])
+        rest = np.setdiff1d(np.arange(wl.Ne), sel)
+        assert l[sel].min() >= l[rest].max() - 2 * Et[t]
+    print(f"{wl.name}: {(~same).sum()} of {wl.T} tokens route differently from the oracle "
+          f"({close.sum()} within the bound)")
+    assert same.mean() >= 0.99, same.mean()
+    rows = np.flatnonzero(same)
+    # weights: the fp32 softmax bound plus the logit error, |dw/w| <= 2 max E
+    rel = np.abs(w[rows] - w_o[rows]) / w_o[rows]
+    assert np.all(rel <= W_RTOL + 2 * Et[rows, None]), rel.max()
+    ref = oracle_rows(wl, inp, rows, ids_o[rows], w_o[rows])
+    assert row_err(y.float().cpu().numpy().astype(np.float64)[rows], ref).max() <= TOL[wl.dtype]
+    # the same layer through occ_moe_forward on the device's logits:
+    # identical routing, equal output up to the order of the fp32 atomic adds
     desc = occ.desc_of(wl)
     ws = occ.alloc_workspace(desc)
     y2 = torch.empty_like(y)
@@ -94,7 +132,6 @@ def test_gated_forward_matches_oracle(wl):
                         dev["w_up"], dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"],
                         y2, ws)
     torch.cuda.synchronize()
-    # equal up to the order of the fp32 atomic adds inside groups
     assert row_err(y2.float().cpu().numpy(), y.float().cpu().numpy()).max() <= 1e-2
 
 
