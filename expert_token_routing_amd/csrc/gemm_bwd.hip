@@ -63,6 +63,8 @@ constexpr int OPA = BMD * BK;                      // bf16 elements of the A til
 constexpr int STAGED = OPA + OP;
 static_assert(NSTAGE * STAGED * 2 + BMD * 4 <= 160 * 1024, "LDS");
 
+constexpr int kBand = 8;  // row tiles per band of the dgrad tile order
+
 // Block mi of wave row wm starts at this row: blocks are dealt to the wave
 // rows in turn, so the two wave rows sharing a SIMD hold ceil(blocks / 2).
 __device__ __forceinline__ int block_row(int wm, int mi) { return (wm + WAVES_M * mi) * 16; }
@@ -215,11 +217,14 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
     const int p = find_pos(a.tile_off, a.Ne, tm);
     if (a.phase != 2) {
-        // column tiles outermost inside each expert, as in the forward GEMMs
+        // bands of kBand row tiles, column tiles outermost inside a band, as
+        // in the forward GEMMs
         const int r = a.tile_off[p + 1] - a.tile_off[p];
         const int local = (tm - a.tile_off[p]) * n_tiles + tn;
-        tn = local / r;
-        tm = a.tile_off[p] + local % r;
+        const int band = local / (kBand * n_tiles), rb0 = band * kBand;
+        const int rb = min(kBand, r - rb0), idx = local - band * kBand * n_tiles;
+        tn = idx / rb;
+        tm = a.tile_off[p] + rb0 + idx - tn * rb;
     }
     const int seg0 = a.seg_off[p], len = a.seg_off[p + 1] - seg0;
     const int nf = a.phase ? a.first_cnt[p] : 0;

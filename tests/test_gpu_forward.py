@@ -164,7 +164,7 @@ def test_placement_invariance_and_rescheduling():
     inp = inputs(wl)
     L0 = inp["placement"]
     ids_o, _ = oracle.route(inp["logits"].numpy(), wl.k, L0)
-    L1 = occ.occ_place_experts(oracle.coact(ids_o, wl.Ne, L0)["C"].astype(np.int32), wl.Nd)
+    L1 = oracle.placement(oracle.coact(ids_o, wl.Ne, L0)["C"], wl.Nd)
     dev = to_dev(inp)
     y0, ws0, v0, _ = forward(wl, inp, L0, dev)
     y1, ws1, v1, _ = forward(wl, inp, L1, dev)

@@ -1,6 +1,8 @@
 """GPU parity of the integer steps against the oracle, bit for bit: routing
 ids (with both pruning rules), BRIM_0 / BRIM_1 and their condensed form, the
-co-activation counts C, P, N_sfd, CT and the intra share.  Full workload
+co-activation counts C, P, N_sfd, CT and the intra share.  The BRIM and the
+statistics are built on the oracle's routing, so every expected value comes
+from the oracle alone.  Full workload
 sizes (the sizes the benchmark runs) plus ragged and degenerate shapes."""
 import numpy as np
 import pytest
@@ -111,9 +113,12 @@ def gpu_brim(wl, ids_t, w_t, placement, dense=True):
 
 
 def check_brim(wl, placement, ids_g=None, w_g=None):
-    inp_logits = synth.make_logits(wl)
+    """The device's BRIM from the oracle's routing (ids, fp32 weights)
+    against the oracle's literal counter loops on the same routing."""
     if ids_g is None:
-        ids_g, w_g = gpu_route(wl, inp_logits, placement)
+        ids_g, w_g = oracle.route(synth.make_logits(wl).numpy(), wl.k, placement, wl.prune_rule,
+                                  wl.prune_groups)
+    w_g = np.asarray(w_g, dtype=np.float32)
     b = gpu_brim(wl, torch.from_numpy(ids_g), torch.from_numpy(w_g), placement)
     r = oracle.brim1(ids_g, w_g.astype(np.float64), wl.Ne, placement)
     assert np.array_equal(b["brim0"], r["brim0"])
@@ -167,7 +172,7 @@ def test_brim_rescheduled_placement():
     logits = synth.make_logits(wl)
     L0 = synth.contiguous_placement(wl)
     ids_o, _ = oracle.route(logits.numpy(), wl.k, L0)
-    L1 = occ.occ_place_experts(oracle.coact(ids_o, wl.Ne, L0)["C"].astype(np.int32), wl.Nd)
+    L1 = oracle.placement(oracle.coact(ids_o, wl.Ne, L0)["C"], wl.Nd)
     b0 = check_brim(wl, L0)
     b1 = check_brim(wl, L1)
     assert b1["sfd_off"][-1] < b0["sfd_off"][-1]  # rescheduling lowers CT here
@@ -191,7 +196,7 @@ def test_brim_expert_and_group_with_no_tokens():
     logits[:, 4:8] = -50.0   # group 1 never chosen
     logits[:, 13] = -50.0    # nor expert 13
     L = synth.contiguous_placement(wl)
-    ids, w = gpu_route(wl, logits, L)
+    ids, w = oracle.route(logits.numpy(), wl.k, L)
     assert not np.isin(ids, [4, 5, 6, 7, 13]).any()
     b = check_brim(wl, L, ids, w)
     assert b["sfd_off"][1] == b["sfd_off"][2]
@@ -202,7 +207,7 @@ def test_brim_expert_and_group_with_no_tokens():
 def test_coactivation_stats(wl):
     logits = synth.make_logits(wl)
     L = synth.contiguous_placement(wl)
-    ids, _ = gpu_route(wl, logits, L)
+    ids, _ = oracle.route(logits.numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
     desc = occ.desc_of(wl)
     C = torch.empty(wl.Ne, wl.Ne, dtype=torch.int32, device="cuda")
     P = torch.empty(wl.Ne, wl.Ne, dtype=torch.float32, device="cuda")
@@ -226,7 +231,7 @@ def test_coactivation_wide_expert_count_uses_global_histogram():
     wl = W.Workload("wide", 13, T=3000, d=64, Ne=128, k=6, Nd=8, F=64, n_c=16)
     logits = synth.make_logits(wl)
     L = synth.contiguous_placement(wl)
-    ids, _ = gpu_route(wl, logits, L)
+    ids, _ = oracle.route(logits.numpy(), wl.k, L)
     desc = occ.desc_of(wl)
     C = torch.empty(128, 128, dtype=torch.int32, device="cuda")
     P = torch.empty(128, 128, dtype=torch.float32, device="cuda")

@@ -192,11 +192,11 @@ def test_similarity_forward_full_size_sampled_rows():
     desc = occ.desc_of(wl)
     occ.occ_route_similarity(desc, dev["logits"], L, torch.from_numpy(rank).cuda(), ids, w)
     y, _, _ = routed_forward(wl, dev, ids, w, L)
-    ids_h, w_h = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
-    ids_o, _ = oracle.route_similarity(inp["logits"].numpy(), wl.k, L, wl.prune_groups, rank)
-    assert np.array_equal(ids_h, ids_o)
+    ids_o, w_o = oracle.route_similarity(inp["logits"].numpy(), wl.k, L, wl.prune_groups, rank)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=W_RTOL, atol=0)
     rows = synth.sample_rows(wl.T, 96, seed=11)
-    ref = oracle_rows(wl, inp, rows, ids_h, w_h)
+    ref = oracle_rows(wl, inp, rows, ids_o, w_o)
     assert row_err(y.float().cpu().numpy()[rows], ref).max() <= TOL[wl.dtype]
 
 
