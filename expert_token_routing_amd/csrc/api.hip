@@ -77,7 +77,7 @@ struct Layout {
     // training only (flags & OCC_FLAG_TRAIN): saved pre-activations and the
     // backward pass's buffers
     size_t gu, gu_sh, dy_sfd, dgu, dx_sfd, dw_part, zero_row, bt_all, bt_first, bt_rest, dgu_sh,
-        dx_sh, dense_seg, dense_tile;
+        dx_sh, dense_seg, dense_tile, wg_part;
     int dw_stride;
     size_t total;
 };
@@ -136,11 +136,18 @@ Layout layout(const occ_layer_desc &D) {
         L.bt_first = take((Ne + 1) * 4);
         L.bt_rest = take((Ne + 1) * 4);
         L.dense_seg = take(2 * 4);
-        L.dense_tile = take(2 * 4);
+        L.dense_tile = take(4 * 4);
         if (D.n_shared > 0) {
             L.gu_sh = take(T * 2 * Nsh * es);
             L.dgu_sh = take(T * 2 * Nsh * es);
             L.dx_sh = take(T * d * 4);
+            // the shared weight gradients' split-K partials (dense, K = T)
+            const size_t Fs = D.F_shared, nsh = D.n_shared;
+            const size_t p3 = wgrad_k_parts(D.n_shared, D.d, D.F_shared, D.T);
+            const size_t p4 = wgrad_k_parts(D.n_shared, 2 * D.F_shared, D.d, D.T);
+            const size_t need = std::max(p3 > 1 ? p3 * nsh * d * Fs : 0,
+                                         p4 > 1 ? p4 * nsh * 2 * Fs * d : 0);
+            L.wg_part = need ? take(need * 4) : 0;
         }
     }
     L.total = o;
@@ -245,6 +252,18 @@ BrimBufs brim_bufs(void *ws, const Layout &L) {
 }
 
 occ_status hip_status(hipError_t e) { return e == hipSuccess ? OCC_OK : OCC_ERR_HIP; }
+
+// Row tiles of a dense backward input-gradient product over T rows against
+// n_tiles column tiles: ceil(T / kBwdRowTile), raised as far as the launch
+// keeps the same number of rounds of the CUs (one workgroup each), so the
+// last round is filled with shorter tiles; at most one 16-row block per tile.
+int dense_row_tiles_bwd(int T, int n_tiles) {
+    const long m0 = (T + kBwdRowTile - 1) / kBwdRowTile, cus = compute_units();
+    if (m0 == 0 || n_tiles <= 0) return static_cast<int>(m0);
+    const long rounds = (m0 * n_tiles + cus - 1) / cus;
+    const long m = std::min<long>(rounds * cus / n_tiles, (T + 15) / 16);
+    return static_cast<int>(std::max(m0, m));
+}
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -738,8 +757,12 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     if (D.n_shared > 0) {
         int32_t *dseg = at<int32_t>(workspace, L.dense_seg);
         int32_t *dtile = at<int32_t>(workspace, L.dense_tile);
-        OCC_HIP(launch_dense_sched(D.T, kBwdRowTile, dseg, dtile, s));
-        const size_t dense_tiles = (T + kBwdRowTile - 1) / kBwdRowTile;
+        // one row-tile schedule per product: dg, du against F_shared columns,
+        // dx against d columns, each balanced over the CUs' rounds
+        const int m_gu = dense_row_tiles_bwd(D.T, ceil_div(D.F_shared, kBwdTile));
+        const int m_dx = dense_row_tiles_bwd(D.T, ceil_div(D.d, kBwdTile));
+        OCC_HIP(launch_dense_sched(D.T, m_gu, dseg, dtile, s));
+        OCC_HIP(launch_dense_sched(D.T, m_dx, dseg, dtile + 2, s));
         PlaceTab one{};
         one.Ne = 1;
         one.Nd = 1;
@@ -767,7 +790,7 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
             s1.Ne = 1;
             s1.epilogue = BWD_EPI_SWIGLU;
             s1.tab = one;
-            OCC_HIP(launch_bwd_dgrad(s1, dense_tiles, s));
+            OCC_HIP(launch_bwd_dgrad(s1, m_gu, s));
             BwdDgradArgs s2{};
             s2.A = dgu_sh;
             s2.lda = static_cast<int>(2 * Nsh);
@@ -775,7 +798,7 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
             s2.B1 = static_cast<const char *>(ws_gate) + sx * Fs * d * es;
             s2.B2 = static_cast<const char *>(ws_up) + sx * Fs * d * es;
             s2.seg_off = dseg;
-            s2.tile_off = dtile;
+            s2.tile_off = dtile + 2;
             s2.merge_out = dx_sh;
             s2.merge_store = sx == 0;
             s2.N = D.d;
@@ -784,7 +807,7 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
             s2.Ne = 1;
             s2.epilogue = BWD_EPI_MERGE;
             s2.tab = one;
-            OCC_HIP(launch_bwd_dgrad(s2, dense_tiles, s));
+            OCC_HIP(launch_bwd_dgrad(s2, m_dx, s));
         }
         BwdWgradArgs w3{};
         w3.A = dy;
@@ -800,6 +823,11 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
         w3.n_groups = D.n_shared;
         w3.rows = D.T;
         w3.tab = one;
+        // K = all T tokens against a small output: split into chunks summed
+        // in order (enough tiles for the CUs, still deterministic)
+        w3.k_parts = wgrad_k_parts(D.n_shared, D.d, D.F_shared, D.T);
+        w3.k_chunk = wgrad_k_chunk(D.T, w3.k_parts);
+        w3.part = w3.k_parts > 1 ? at<float>(workspace, L.wg_part) : nullptr;
         OCC_HIP(launch_bwd_wgrad(w3, s));
         BwdWgradArgs w4{};
         w4.A = dgu_sh;
@@ -816,6 +844,9 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
         w4.n_groups = D.n_shared;
         w4.rows = D.T;
         w4.tab = one;
+        w4.k_parts = wgrad_k_parts(D.n_shared, 2 * D.F_shared, D.d, D.T);
+        w4.k_chunk = wgrad_k_chunk(D.T, w4.k_parts);
+        w4.part = w4.k_parts > 1 ? at<float>(workspace, L.wg_part) : nullptr;
         OCC_HIP(launch_bwd_wgrad(w4, s));
     }
     OCC_TRY(mark(4));

@@ -38,12 +38,12 @@ __global__ __launch_bounds__(kMaxNe) void k_tile_sched(const int32_t *__restrict
     }
 }
 
-__global__ void k_dense_sched(int T, int bm, int32_t *seg_off, int32_t *tile_off) {
+__global__ void k_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off) {
     if (threadIdx.x == 0) {
         seg_off[0] = 0;
         seg_off[1] = T;
         tile_off[0] = 0;
-        tile_off[1] = (T + bm - 1) / bm;
+        tile_off[1] = m_tiles;
     }
 }
 
@@ -116,9 +116,9 @@ hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, i
     return hipGetLastError();
 }
 
-hipError_t launch_dense_sched(int T, int tile_rows, int32_t *seg_off, int32_t *tile_off,
+hipError_t launch_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off,
                               hipStream_t s) {
-    k_dense_sched<<<1, kWave, 0, s>>>(T, tile_rows, seg_off, tile_off);
+    k_dense_sched<<<1, kWave, 0, s>>>(T, m_tiles, seg_off, tile_off);
     return hipGetLastError();
 }
 

@@ -436,11 +436,19 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
     __shared__ int s_rows[kRowsLds];
     const int m_tiles = (a.M + BM - 1) / BM, n_tiles = (a.N + BN - 1) / BN;
+    const int parts = a.k_parts > 1 ? a.k_parts : 1;
     int tq, tn;
-    if (!map_tile(a.n_groups * m_tiles, n_tiles, tq, tn)) return;
+    if (!map_tile(parts * a.n_groups * m_tiles, n_tiles, tq, tn)) return;
+    // chunk of K (rows) this tile sums: the chunks are outermost, so the
+    // tiles an XCD runs together share their rows' operand strips
+    const int part = tq / (a.n_groups * m_tiles);
+    tq -= part * a.n_groups * m_tiles;
     const int grp = tq / m_tiles, tm = tq - grp * m_tiles;
-    const int seg = a.seg_off ? a.seg_off[grp] : 0;
-    const int len = a.seg_off ? a.seg_off[grp + 1] - seg : a.rows;
+    const int seg0 = a.seg_off ? a.seg_off[grp] : 0;
+    const int len_all = a.seg_off ? a.seg_off[grp + 1] - seg0 : a.rows;
+    const int k_begin = parts > 1 ? part * a.k_chunk : 0;
+    const int seg = seg0 + k_begin;
+    const int len = parts > 1 ? max(0, min(len_all - k_begin, a.k_chunk)) : len_all;
     const int e = a.seg_off ? a.tab.expert[grp] : grp;
     // M, N >= 256: the last tile of a dimension may overlap the previous one
     const int m0 = tm * BM, n0 = tn * BN;
@@ -515,15 +523,18 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
         }
     }
 
-    // C[e] rows m < msplit -> C1, the rest -> C2 (gate and up halves); each
-    // lane stores 4 consecutive columns of a row
+    // C[e] rows m < msplit -> C1, the rest -> C2 (gate and up halves), or
+    // with a split K this chunk's partial tile; each lane stores 4
+    // consecutive columns of a row
+    float *P = parts > 1 ? a.part + static_cast<size_t>(part) * a.n_groups * a.M * a.N : nullptr;
 #pragma unroll
     for (int mi = 0; mi < MI; mi++) {
         const int m = mload + wm * WM + mi * 16 + (l & 15);
         if (m < m0) continue;
-        float *row = m < a.msplit
-                         ? a.C1 + (static_cast<size_t>(e) * a.msplit + m) * a.N
-                         : a.C2 + (static_cast<size_t>(e) * (a.M - a.msplit) + (m - a.msplit)) * a.N;
+        float *row = P ? P + (static_cast<size_t>(grp) * a.M + m) * a.N
+                       : (m < a.msplit ? a.C1 + (static_cast<size_t>(e) * a.msplit + m) * a.N
+                                       : a.C2 + (static_cast<size_t>(e) * (a.M - a.msplit) +
+                                                 (m - a.msplit)) * a.N);
 #pragma unroll
         for (int ni = 0; ni < NI; ni++) {
             const int n = nload + wn * WN + ni * 16 + 4 * (l >> 4);
@@ -532,9 +543,63 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdWgradArgs a) {
     }
 }
 
+// The split weight gradients' partial tiles, added in chunk order: 4
+// consecutive columns per thread, written to C1 / C2 as the tiles would be.
+__global__ __launch_bounds__(256) void k_wgrad_reduce(const float *__restrict__ part, int parts,
+                                                      int n_groups, int M, int N, int msplit,
+                                                      float *__restrict__ C1,
+                                                      float *__restrict__ C2) {
+    const size_t total = static_cast<size_t>(n_groups) * M * N / 4;
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const size_t plane = static_cast<size_t>(n_groups) * M * N;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + i;
+    f32x4 acc = __builtin_nontemporal_load(src);
+    for (int p = 1; p < parts; p++) acc += __builtin_nontemporal_load(src + p * plane / 4);
+    const size_t o = 4 * i, n = o % N, gm = o / N;
+    const int grp = static_cast<int>(gm / M), m = static_cast<int>(gm % M);
+    float *row = m < msplit ? C1 + (static_cast<size_t>(grp) * msplit + m) * N
+                            : C2 + (static_cast<size_t>(grp) * (M - msplit) + (m - msplit)) * N;
+    *reinterpret_cast<f32x4 *>(row + n) = acc;
+}
+
 unsigned grid_for(size_t tiles) { return static_cast<unsigned>(8 * ((tiles + 7) / 8)); }
 
 }  // namespace
+
+// The split is chosen by an estimate in units of one 64-row K slice of one
+// tile: rounds of 256 CUs x slices per chunk, plus the ordered reduction's
+// traffic (each chunk's partials read once, the result written once, about
+// 14 MB per slice time at HBM speed), over 1..16 chunks of at least 1024
+// rows.  A fixed count of CUs keeps the choice (and so the summation order
+// and the workspace size) a function of the shape alone.  On the Qwen-shaped
+// layer's shared expert it picks 13 chunks for dW_down (176 tiles: 69% of
+// the CUs for the whole launch otherwise) and 8 for [dW_g; dW_u] (352
+// tiles, 1.4 rounds).
+int wgrad_k_parts(int n_groups, int M, int N, int rows) {
+    const long tiles = static_cast<long>(n_groups) * ceil_div(M, BM) * ceil_div(N, BN);
+    const long slices = (rows + BK - 1) / BK;
+    const double out_mb = static_cast<double>(n_groups) * M * N * 4 / 1e6;
+    if (tiles <= 0 || slices <= 0) return 1;
+    double best = 0;
+    int best_s = 1;
+    for (int s = 1; s <= 16; s++) {
+        const long chunk = (slices + s - 1) / s;
+        if (s > 1 && chunk < 16) break;
+        const long rounds = (tiles * s + 255) / 256;
+        const double t = static_cast<double>(rounds) * chunk + (s > 1 ? (s + 1) * out_mb / 14.0 : 0);
+        if (s == 1 || t < best) {
+            best = t;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
+
+int wgrad_k_chunk(int rows, int parts) {
+    const int slices = (rows + BK - 1) / BK;
+    return ((slices + parts - 1) / parts) * BK;
+}
 
 hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream_t s) {
     const unsigned grid = grid_for(max_m_tiles * ((a.N + BN - 1) / BN));
@@ -545,10 +610,18 @@ hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream
 }
 
 hipError_t launch_bwd_wgrad(const BwdWgradArgs &a, hipStream_t s) {
-    const unsigned grid = grid_for(static_cast<size_t>(a.n_groups) * ((a.M + BM - 1) / BM) *
-                                   ((a.N + BN - 1) / BN));
+    const int parts = a.k_parts > 1 && !a.seg_off && a.part ? a.k_parts : 1;
+    BwdWgradArgs b = a;
+    b.k_parts = parts;
+    const unsigned grid = grid_for(static_cast<size_t>(parts) * a.n_groups *
+                                   ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
     if (grid == 0) return hipSuccess;
-    k_bwd_wgrad<<<grid, NT, 0, s>>>(a);
+    k_bwd_wgrad<<<grid, NT, 0, s>>>(b);
+    if (parts > 1) {
+        const size_t total = static_cast<size_t>(a.n_groups) * a.M * a.N / 4;
+        k_wgrad_reduce<<<ceil_div(total, 256), 256, 0, s>>>(a.part, parts, a.n_groups, a.M, a.N,
+                                                           a.msplit, a.C1, a.C2);
+    }
     return hipGetLastError();
 }
 

@@ -167,6 +167,10 @@ hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream
 // both operands K-major (rows lda / ldb elements apart).  Rows m < msplit go
 // to C1[e] (msplit x N), the rest to C2[e].  M, N >= 256; tail rows of a
 // group read zero_row (at least 256 zero elements).
+// Dense launches (seg_off NULL) may split K (the rows) into k_parts chunks
+// of k_chunk rows: each chunk's fp32 tiles go to `part` (k_parts x n_groups
+// x M x N) and a second kernel adds them in chunk order into C1 / C2, so
+// the result stays deterministic.
 struct BwdWgradArgs {
     const void *A, *B;
     const int32_t *a_rows, *b_rows, *seg_off;
@@ -174,8 +178,15 @@ struct BwdWgradArgs {
     float *C1, *C2;
     int M, N, msplit, lda, ldb, a_col0, a_col_grp, b_col0, b_col_grp, n_groups, rows;
     PlaceTab tab;
+    int k_parts, k_chunk;
+    float *part;
 };
 hipError_t launch_bwd_wgrad(const BwdWgradArgs &a, hipStream_t s);
+// K chunks for a dense weight-gradient product of n_groups x M x N outputs
+// over `rows` rows (1: no split), chosen from the shape alone; rows per
+// chunk for that count.
+int wgrad_k_parts(int n_groups, int M, int N, int rows);
+int wgrad_k_chunk(int rows, int parts);
 
 // Row-tile schedules for `tile_rows`-row tiles from the expert segments
 // epd_off and first-contributor counts first_cnt (all rows, first, rest).
@@ -183,8 +194,8 @@ hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, i
                              int tile_rows, int32_t *tile_off, int32_t *tile_off_first,
                              int32_t *tile_off_rest, hipStream_t s);
 // A one-segment schedule for a dense GEMM over T rows: seg_off = {0, T},
-// tile_off = {0, ceil(T / tile_rows)}.
-hipError_t launch_dense_sched(int T, int tile_rows, int32_t *seg_off, int32_t *tile_off,
+// tile_off = {0, m_tiles} (the rows shared out evenly over m_tiles tiles).
+hipError_t launch_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off,
                               hipStream_t s);
 // Routing-weight and logit gradients: dw[t, j] = sum of dw_part over the
 // EPD row tok_epd[t*k + j]'s nparts partials (in order); dlogits through the

@@ -153,6 +153,20 @@ def test_backward_with_shared_experts():
     check(got, ref, ROUTED + SHARED)
 
 
+def test_backward_shared_experts_split_k():
+    """Shared experts over 4096 tokens: their weight gradients (K = all T
+    rows against a 256 x 320 or 640 x 256 output, a few tiles) are summed
+    in 4 chunks of 1024 rows, added in chunk order.  Every gradient against
+    the oracle, and bitwise equal across two runs."""
+    wl = shape("bwd_shared_splitk", T=4096, d=256, F=256, n_shared=2, F_shared=320, index=18)
+    inp = synth.make_all(wl)
+    got, ref = run(wl, inp=inp, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    check(got, ref, ROUTED + SHARED)
+    again, _ = run(wl, inp=inp, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    for key in SHARED + ["dx"]:
+        assert np.array_equal(again[key], got[key]), key
+
+
 def test_backward_olmoe_expert_shape():
     """d = 2048, F = 1024 (32 K slices in the input gradients, full-width
     weight tiles), fewer experts so that the fp64 oracle stays small."""
