@@ -160,6 +160,7 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
             }
 #pragma unroll
             for (int j = 0; j < kScanBatch; j++) {
+                if (c0 + j * kWave >= nchunks) break;  // wave-uniform: no empty steps
                 const int c = c0 + j * kWave + lane;
                 const int incl = wave_incl_scan(v[j]);
                 if (c < nchunks) {
