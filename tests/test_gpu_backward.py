@@ -233,3 +233,57 @@ def test_backward_full_size_sampled(flags):
             for i in range(len(sel)):
                 assert normwise(g[i], q[key][i]) <= NORM_TOL, (key, e, sel[i])
                 assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max()
+
+
+def test_backward_full_size_shared_experts_sampled():
+    """The DeepSeek-shaped layer at full size (T = 16384, two shared experts
+    of F = 1408), training forward + backward under the deterministic merge
+    as the benchmark runs it; the shared experts' weight gradients, which
+    sum over all T tokens in 8 and 4 ordered chunks, on sampled rows of both
+    experts, and sampled dx rows.  A shared expert is an expert that every
+    token selects with weight 1 (Eq. 1), so the oracle's per-expert gradient
+    rows give its gradients."""
+    from gpu_common import inputs
+    wl = W.DEEPSEEK
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    ids, w = check_train_forward(wl, inp, L, desc, ws, y, rows=synth.sample_rows(wl.T, 48, seed=23))
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(9)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    nsh, Fs = wl.n_shared, wl.F_shared
+    dWsg = torch.empty(nsh, Fs, wl.d, **f32)
+    dWsu = torch.empty_like(dWsg)
+    dWsd = torch.empty(nsh, wl.d, Fs, **f32)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                         dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], dx, dWg, dWu,
+                         dWd, dWsg, dWsu, dWsd, None, None, ws)
+    torch.cuda.synchronize()
+    dyd = dy.double().numpy()
+    rows = synth.sample_rows(wl.T, 24, seed=24)
+    r = oracle.moe_backward_rows(rows, bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                 bits(inp["w_up"]), bits(inp["w_down"]), bits(inp["ws_gate"]),
+                                 bits(inp["ws_up"]), bits(inp["ws_down"]))
+    assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
+    all_tok = np.zeros((wl.T, 1), np.int32)
+    ones = np.ones((wl.T, 1), np.float64)
+    fs, ns = np.array([0, 700, Fs - 1]), np.array([0, 1001, wl.d - 1])
+    for sx in range(nsh):
+        q = oracle.moe_wgrad_rows(bits(inp["x"]), all_tok, ones, dyd, bits(inp["ws_gate"][sx:sx + 1]),
+                                  bits(inp["ws_up"][sx:sx + 1]), bits(inp["ws_down"][sx:sx + 1]),
+                                  0, fs, ns)
+        for key, got, sel in (("dW_gate", dWsg, fs), ("dW_up", dWsu, fs), ("dW_down", dWsd, ns)):
+            g = got[sx].cpu().numpy()[sel]
+            for i in range(len(sel)):
+                assert normwise(g[i], q[key][i]) <= NORM_TOL, (key, sx, sel[i])
+                assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max()
