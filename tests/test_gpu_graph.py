@@ -99,3 +99,49 @@ def test_training_step_graph_replays():
                              dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], dx, *gr,
                              dw, dl, ws)
     check_replays(step, [y, dx, dw, dl] + gr)
+
+
+@pytest.mark.parametrize("flags", [0, occ.OCC_FLAG_DETERMINISTIC], ids=["atomic", "deterministic"])
+def test_shared_expert_graph_replays_follow_new_inputs(flags):
+    """A layer with shared experts, which run on a side stream forked from
+    the capturing stream, captured once and replayed on new token values
+    written into the same input buffer, the workspace cleared before each
+    replay: every replay must equal an eager run on the same values, so the
+    side stream's launches are part of the graph (not run once at capture)."""
+    wl = W.scaled(W.DEEPSEEK, 700, name="graph_shared_T700")
+    inp = synth.make_all(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=flags)
+    ws = occ.alloc_workspace(desc)
+    y = torch.empty(wl.T, wl.d, dtype=torch.bfloat16, device="cuda")
+    x = dev["x"].clone()
+
+    def step():
+        occ.occ_moe_forward(desc, x, dev["logits"], L, dev["w_gate"], dev["w_up"], dev["w_down"],
+                            dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm the stream once outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        x_new = torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(300 + i))
+        x.copy_(x_new.to(torch.bfloat16).cuda())
+        ws.zero_()
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph = y.clone()
+        ws.zero_()
+        step()
+        torch.cuda.synchronize()
+        if flags & occ.OCC_FLAG_DETERMINISTIC:
+            assert torch.equal(y_graph, y), i
+        else:
+            assert row_err(y_graph.float().cpu().numpy(), y.float().cpu().numpy()).max() <= 1e-2, i
