@@ -28,7 +28,9 @@ around it on the layer's stream during the timed steps.  `stage_roofline`
 puts every stage against its own bound with the method's algorithmic work
 (each operand moved once, stage one's fp32 SFD rows written once);
 `design_traffic` gives the HBM bytes the kernels really move, from the
-committed counter profiles, over those algorithmic bytes.  `cpu_baseline`
+committed counter profiles, over those algorithmic bytes.  `hbm_copy` is a
+plain 1 GiB device-to-device copy (the runtime's) timed on this GPU, read +
+write bytes per second, reported beside the 8 TB/s peak.  `cpu_baseline`
 times the oracle on a bounded sample of the same workload on this host.
 """
 from __future__ import annotations
@@ -131,6 +133,7 @@ def main():
         for w in (W.TINY_F32, W.OLMOE, W.DEEPSEEK, W.OLMOE_PRUNED, pruned_traverse):
             cfgs[w.name] = measure(args, w, headline=False)
         out["configs"] = cfgs
+    out["hbm_copy"] = copy_bandwidth()
     out["context"] = dict(CONTEXT, measured_ct_cut={
         k: v["ct_cut"] for k, v in [(out["config"]["workload"], out)] + list(
             out.get("configs", {}).items()) if v.get("ct_cut") is not None})
@@ -377,6 +380,34 @@ def measure(args, wl, headline):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
+
+
+def copy_bandwidth():
+    """A plain 1 GiB device-to-device copy (the runtime's), timed: bytes read
+    plus written per second, beside the 8 TB/s peak.  (The dispatch kernel's
+    row copies run faster than this copy, so it is a measured reference, not
+    a ceiling.)"""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    gbs = 2 * n / (ms / 1e3) / 1e9
+    return {"bytes": 2 * n, "ms": round(ms, 4), "GB_per_s": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def algorithmic_work(wl, n_sfd, active):
