@@ -478,14 +478,21 @@ def stage_rooflines(wl, stages, ms, flags, n_sfd, active, profiling):
                             "is latency-bound and counted at zero"}
     # the design's real traffic over the algorithmic bytes (counter profiles)
     design = {}
-    src = {"k_dispatch": "rows.hip", "k_gemm_up": "gemm_bf16.hip",
-           "k_gemm_down": "gemm_bf16.hip", "k_merge_slots": "rows.hip"}
+    src = {"k_dispatch": "rows.hip", "k_merge_slots": "rows.hip"}
     alg = {"k_dispatch": work["dispatch"][1], "k_merge_slots": work["combine"][1]}
     # k_gemm_up and k_gemm_down launch once for the routed experts and once
-    # for the shared ones: the counters are averaged per launch
-    n_up = 2 if wl.n_shared else 1
-    alg["k_gemm_up"] = (work["gemm_up"][1] + work.get("shared_up", (0, 0))[1]) / n_up
-    alg["k_gemm_down"] = (work["gemm_down"][1] + work.get("shared_down", (0, 0))[1]) / n_up
+    # for the shared ones, unless the shared product is large enough for the
+    # pipelined k_gemm_*_dense: the counters are averaged per launch
+    for gemm, cols in (("up", 2 * wl.n_shared * wl.F_shared), ("down", wl.d)):
+        kern = f"k_gemm_{gemm}"
+        launches = [work[f"gemm_{gemm}"][1]]
+        if wl.n_shared:
+            sh = work[f"shared_{gemm}"][1]
+            if dense_pipelined(wl.T, cols):
+                alg[f"{kern}_dense"], src[f"{kern}_dense"] = sh, "gemm_bf16.hip"
+            else:
+                launches.append(sh)
+        alg[kern], src[kern] = sum(launches) / len(launches), "gemm_bf16.hip"
     for kern, a in alg.items():
         tb = profiling.traffic_bytes(kern, wl.name, src[kern])
         if tb is not None:
@@ -494,25 +501,43 @@ def stage_rooflines(wl, stages, ms, flags, n_sfd, active, profiling):
     return out, design
 
 
+def dense_pipelined(M, cols):
+    """The library's size rule: a dense product (the shared experts) of at
+    least 8 rounds of 256 x 256 tiles on the GPU's CUs runs on the pipelined
+    four-wave build (kernels k_gemm_*_dense)."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return -(-M // 256) * -(-cols // 256) >= 8 * cus
+
+
 def dominant_roofline(wl, stages, n_sfd, active, profiling):
-    """The up-projection GEMM (k_gemm_up): its launches' algorithmic FLOPs over
-    their average duration (HIP events on the layer's stream).  With shared
-    experts it runs twice per step (shared, routed) and the figures are per
-    launch, averaged over the two."""
+    """The up-projection GEMM kernel that takes the most time per step: its
+    launches' algorithmic FLOPs over their average duration (HIP events on
+    the layer's stream).  The routed up-projection is k_gemm_up (k_gemm_up_m128
+    in the decode regime); the shared experts' runs on the same kernel
+    (then the figures are per launch, averaged over the two) unless it is
+    large enough for the pipelined k_gemm_up_dense."""
     from expert_token_routing_amd import workloads as W
 
     es = 2 if wl.dtype == W.DTYPE_BF16 else 4
     work = algorithmic_work(wl, n_sfd, active)
-    launches = [("gemm_up", work["gemm_up"])]
+    small = wl.T * wl.k < 96 * wl.Ne and es == 2
+    routed = "k_gemm_up_m128" if small else "k_gemm_up"
+    if es != 2:
+        routed = "k_gemm_up_f32"
+    kernels = {routed: [("gemm_up", work["gemm_up"])]}
     if wl.n_shared:
-        launches.append(("shared_up", work["shared_up"]))
+        shared = routed
+        if es == 2 and not small and dense_pipelined(wl.T, 2 * wl.n_shared * wl.F_shared):
+            shared = "k_gemm_up_dense"
+        kernels.setdefault(shared, []).append(("shared_up", work["shared_up"]))
+    kernel, launches = max(kernels.items(), key=lambda kv: sum(stages[s] for s, _ in kv[1]))
     n = len(launches)
     avg_ms = sum(stages[s] for s, _ in launches) / n
     flops = sum(f for _, (f, _b) in launches) / n
     nbytes = sum(b for _, (_f, b) in launches) / n
-    small = wl.T * wl.k < 96 * wl.Ne and es == 2 and not wl.n_shared
-    kernel = "k_gemm_up_m128" if small else "k_gemm_up"
-    traffic = profiling.traffic_bytes(kernel, wl.name, "gemm_bf16.hip")
+    traffic = profiling.traffic_bytes(kernel, wl.name, "gemm_bf16.hip") if es == 2 else None
     peak = PEAK_BF16_TFLOPS if es == 2 else PEAK_F32_TFLOPS
     if flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = flops / (avg_ms / 1e3) / 1e12
@@ -522,9 +547,8 @@ def dominant_roofline(wl, stages, n_sfd, active, profiling):
         achieved = nbytes / (avg_ms / 1e3) / 1e9
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
              "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    r.update({"traffic": traffic, "kernel": kernel if es == 2 else "k_gemm_up_f32",
-              "launches_per_step": n, "avg_ms": round(avg_ms, 5),
-              "flops_per_launch": flops, "bytes_per_launch": nbytes})
+    r.update({"traffic": traffic, "kernel": kernel, "launches_per_step": n,
+              "avg_ms": round(avg_ms, 5), "flops_per_launch": flops, "bytes_per_launch": nbytes})
     return r
 
 

@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libocc.so")
 ARCH = os.environ.get("OCC_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "route.hip", "brim.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "coact.hip", "similarity.hip", "gate.hip", "gemm_bf16_m128.hip", "gemm_bwd.hip", "backward.hip"]
+           "coact.hip", "similarity.hip", "gate.hip", "gemm_bf16_m128.hip", "gemm_bf16_dense.hip",
+           "gemm_bwd.hip", "backward.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -68,6 +68,16 @@ GemmOps gemm_ops(const occ_layer_desc &D) {
 }
 int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
 
+// Dense products (the shared experts) that fill at least kDensePipeRounds
+// rounds of the CUs with 256 x 256 tiles take the pipelined four-wave build;
+// cols is the product's MFMA output width (the up-projection's gate and up
+// columns together).
+bool dense_pipelined(const GemmOps &ops, int64_t M, int64_t cols) {
+    if (ops.up != launch_gemm_up_bf16) return false;  // fp32, or the decode regime
+    const int64_t tiles = ((M + 255) / 256) * ((cols + 255) / 256);
+    return tiles >= static_cast<int64_t>(kDensePipeRounds) * compute_units();
+}
+
 // Byte offsets of every buffer inside the workspace.  Sized for the worst
 // case N_sfd = T * min(k, Nd), so no data-dependent size is read back.
 struct Layout {
@@ -486,9 +496,11 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         sd.Ne = 1;
         sd.k_split = D.F_shared;
         sd.tab = tab;
-        OCC_HIP(ops.up(su, shared_tiles, s));
+        if (dense_pipelined(ops, D.T, 2ll * su.N)) OCC_HIP(launch_gemm_up_bf16_dense(su, shared_tiles, s));
+        else OCC_HIP(ops.up(su, shared_tiles, s));
         OCC_TRY(mark(4));
-        OCC_HIP(ops.down(sd, shared_tiles, s));
+        if (dense_pipelined(ops, D.T, sd.N)) OCC_HIP(launch_gemm_down_bf16_dense(sd, shared_tiles, s));
+        else OCC_HIP(ops.down(sd, shared_tiles, s));
     } else {
         OCC_TRY(mark(4));
     }

@@ -68,9 +68,10 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 #ifndef OCC_XCD_MAP
 #define OCC_XCD_MAP 1
 #endif
-// One source, two row-tile sizes: this file builds the kGemmBmBf16-row
-// kernels; gemm_bf16_m128.hip includes it with 128-row tiles and suffixed
-// kernel and launcher names.
+// One source, three builds: this file builds the kGemmBmBf16-row kernels;
+// gemm_bf16_m128.hip includes it with 128-row tiles, and gemm_bf16_dense.hip
+// with 256-row tiles, four waves and the pipelined K loop (OCC_GEMM_PIPE),
+// each with suffixed kernel and launcher names.
 #ifndef OCC_GEMM_TILE_M
 #define OCC_GEMM_TILE_M kGemmBmBf16
 #endif
@@ -313,8 +314,20 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
     }
 }
 
-// K loop shared by both GEMMs.  a_src[i] / b_src[i] point at the thread's
-// fetch chunk of its rows at k = 0.  A ring of NSTAGE LDS buffers is filled
+#ifndef OCC_GEMM_PIPE
+#define OCC_GEMM_PIPE 0
+#endif
+
+// Where a thread's direct loads read: its A rows (the tile's rows, gathered)
+// and its B rows (weight rows), at the thread's fetch chunk.  a_at(i, k0) is
+// load slot i's A address at K offset k0, b_at(i, bo) slot i's B address at
+// B offset bo.
+struct PtrSrc {  // one 64-bit address per slot
+    const uint16_t *a[A_LD], *b[B_LD];
+    __device__ const uint16_t *a_at(int i, int k0) const { return a[i] + k0; }
+    __device__ const uint16_t *b_at(int i, size_t bo) const { return b[i] + bo; }
+};
+// K loop shared by both GEMMs; src gives the direct loads' addresses.  A ring of NSTAGE LDS buffers is filled
 // by direct loads: slice kt+NSTAGE-1 is issued right after the barrier that
 // opens slice kt, so each load has NSTAGE-1 slices of MFMA work to land,
 // and the barrier also certifies that every wave has finished reading the
@@ -327,11 +340,11 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 // pre() runs once the first slices are issued: per-row tables the epilogue
 // needs are loaded there, their latency hidden under those slices' (the
 // loop's first barrier publishes what it writes to LDS).
-template <int NV, bool SWAP, class Pre>
-__device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
-                                       const uint16_t *const (&b_src)[B_LD], int K, int ksp,
-                                       size_t blk, uint16_t *smem, int wm, const int (&brow)[NI],
-                                       f32x4_t (&acc)[MI][NI], int na, Pre &pre) {
+#if !OCC_GEMM_PIPE
+template <int NV, bool SWAP, class Src, class Pre>
+__device__ __forceinline__ void k_loop(const Src &src, int K, int ksp, size_t blk, uint16_t *smem,
+                                       int wm, const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na,
+                                       Pre &pre) {
     constexpr int LOADS = A_LD + B_LD;
     const int per_slice = na + B_LD;  // loads the wave issues per slice
     const int nk = K / BK;
@@ -345,10 +358,10 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
 #pragma unroll
         for (int i = 0; i < A_LD; i++)
             if (i < na)
-                dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (i * (NT / kWave) + w) * kWave * 16));
+                dma16(src.a_at(i, k0), __builtin_amdgcn_readfirstlane(st + (i * (NT / kWave) + w) * kWave * 16));
 #pragma unroll
         for (int i = 0; i < B_LD; i++)
-            dma16(b_src[i] + bo, __builtin_amdgcn_readfirstlane(st + BM * BK * 2 + (i * (NT / kWave) + w) * kWave * 16));
+            dma16(src.b_at(i, bo), __builtin_amdgcn_readfirstlane(st + BM * BK * 2 + (i * (NT / kWave) + w) * kWave * 16));
     };
     constexpr int D = NSTAGE - 1;  // slices in flight ahead of the one consumed
     for (int kt = 0; kt < D && kt < nk; kt++) issue(kt);
@@ -364,19 +377,171 @@ __device__ __forceinline__ void k_loop(const uint16_t *const (&a_src)[A_LD],
     }
     __syncthreads();
 }
+#endif
+
+#if OCC_GEMM_PIPE
+// The pipelined K loop of the four-wave build (gemm_bf16_dense.hip: one
+// wave per SIMD, 128 x 128 per wave, 256 accumulators per lane).  With no
+// second wave on the SIMD to fill the gaps, the loop is software-pipelined
+// inside the wave: the fragments of a 32-deep step are double-buffered in
+// registers, so the next step's LDS reads, and the next slice's direct
+// loads, are issued between the current step's MFMAs.  One barrier per
+// 64-deep slice, after the slice's first step, once the next slice has
+// landed; it also certifies that every wave has read the slice whose buffer
+// the following loads overwrite.  Per 256 x 256 x 32 step a wave reads 16
+// fragments for 64 MFMAs (0.25 per MFMA against 0.33 in the eight-wave
+// build), and every wave issues all of its load slots (rows past the
+// tile's repeat its last row), since a load skipped under a branch would
+// split the MFMA stream into blocks.
+static_assert(NT == 256 && NSTAGE == 2 && BK == 64, "pipelined loop: 4 waves, two 64-deep slots");
+
+// Fragment registers of one 32-deep step: the wave's NV A blocks and NI B
+// blocks; the loop keeps two sets, one multiplied while the other is read.
+template <int NV>
+struct Frags {
+    bf16x8_t a[NV > 0 ? NV : 1];
+    bf16x8_t b[NI];
+};
+
+// Fragment reads with constant offsets: every block's 16 rows start at a
+// multiple of 16, so the swizzle key of a lane's row is (l & 15) >> 1 for
+// all of them and a lane's offset inside any block is the same.  `ab` / `bb`
+// point at that lane offset in the wave's first A / B block of one buffer
+// and one 32-deep half; block i then sits a constant number of rows further
+// (A: WAVES_M * 16 i; B: the up-projection pairs gate and up blocks 128
+// rows apart, the down-projection's are consecutive), so the compiler folds
+// it into the read's immediate offset.  Read r of a step: B blocks first,
+// since the MFMAs take every B block with A block 0 first.
+template <bool UP>
+__device__ constexpr int b_block_off(int ni) {
+    return UP ? (ni < NI / 2 ? 0 : 128) + (ni % (NI / 2)) * 16 : ni * 16;
+}
+template <int NV, bool UP>
+__device__ __forceinline__ void frag_read(Frags<NV> &f, int r, const uint16_t *ab, const uint16_t *bb) {
+    if (r < NI)
+        f.b[r] = *reinterpret_cast<const bf16x8_t *>(bb + b_block_off<UP>(r) * BK);
+    else
+        f.a[r - NI] = *reinterpret_cast<const bf16x8_t *>(ab + WAVES_M * 16 * (r - NI) * BK);
+}
+
+// One 32-deep step: the NV x NI MFMAs on `cur`, with the reads of the next
+// step's fragments (into `nxt`, when READ) spread over its first three
+// quarters and the `nd` direct loads dma(d) over all of it, at most one of
+// each after an MFMA (those that find no MFMA follow the last).  A
+// scheduling barrier after each MFMA keeps that order.  (The loads issued
+// in the step's first quarter or half instead were measured 2-5% slower in
+// both products.)
+template <int NV, bool SWAP, bool READ, class Dma>
+__device__ __forceinline__ void pipe_step(const Frags<NV> &cur, Frags<NV> &nxt, const uint16_t *ab,
+                                          const uint16_t *bb, f32x4_t (&acc)[MI][NI], int nd,
+                                          Dma &dma) {
+    constexpr int NM = NV * NI, NR = NV + NI, ND = A_LD + B_LD;
+    constexpr int RSPAN = NM * 3 / 4 > NR ? NM * 3 / 4 : NR;  // read r after MFMA r * RSPAN / NR
+    constexpr int DSPAN = NM > ND ? NM : ND;                  // load d after MFMA d * DSPAN / ND
+#pragma unroll
+    for (int m = 0; m < NM; m++) {
+        const int mi = m / NI, ni = m % NI;
+        acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[ni], cur.a[mi], acc[mi][ni], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
+        const int r = (m * NR + RSPAN - 1) / RSPAN;
+        if (READ && r < NR && r * RSPAN / NR == m) frag_read<NV, SWAP>(nxt, r, ab, bb);
+        const int d = (m * ND + DSPAN - 1) / DSPAN;
+        if (d < ND && d * DSPAN / ND == m && d < nd) dma(d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (READ) {
+#pragma unroll
+        for (int r = 0; r < NR; r++)
+            if (r * RSPAN / NR >= NM) frag_read<NV, SWAP>(nxt, r, ab, bb);
+    }
+#pragma unroll
+    for (int d = 0; d < ND; d++)
+        if (d * DSPAN / ND >= NM && d < nd) dma(d);
+}
+
+template <int NV, bool SWAP, class Src, class Pre>
+__device__ __forceinline__ void k_loop(const Src &src, int K, int ksp, size_t blk, uint16_t *smem,
+                                       int wm, const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int,
+                                       Pre &pre) {
+    constexpr int LOADS = A_LD + B_LD;
+    const int nk = K / BK;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int c0 = lane_id() >> 4;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
+    // Direct load d of slice kt: A rows (d < A_LD) or B rows.  The B offset
+    // of the slice (blocks of ksp along K) is computed once per slice.
+    auto b_off = [&](int kt) {
+        const int k0 = kt * BK;
+        return ksp == K ? static_cast<size_t>(k0)
+                        : static_cast<size_t>(k0 / ksp) * blk + static_cast<size_t>(k0 % ksp);
+    };
+    auto load = [&](int kt, size_t bo, int d) {
+        const uint32_t st = lds0 + static_cast<uint32_t>((kt & 1) * STAGE * 2);
+        if (d < A_LD) {
+            dma16(src.a_at(d, kt * BK), __builtin_amdgcn_readfirstlane(st + (d * (NT / kWave) + w) * kWave * 16));
+        } else {
+            const int i = d - A_LD;
+            dma16(src.b_at(i, bo), __builtin_amdgcn_readfirstlane(st + BM * BK * 2 + (i * (NT / kWave) + w) * kWave * 16));
+        }
+    };
+    for (int d = 0; d < LOADS; d++) load(0, b_off(0), d);
+    pre();
+    if (nk > 1)
+        for (int d = 0; d < LOADS; d++) load(1, b_off(1), d);
+    wait_vmcnt_le<LOADS>(nk > 1 ? LOADS : 0);
+    __syncthreads();
+    // Lane offsets of the two 32-deep halves of a slice (see frag_read).
+    const int key = (lane_id() & 15) >> 1;
+    const int h0 = (c0 ^ key) << 3, h1 = ((4 + c0) ^ key) << 3;
+    const int ao = (wm * 16 + (lane_id() & 15)) * BK, bo0 = (BM + brow[0]) * BK;
+    auto ab = [&](int slot, int h) { return smem + slot * STAGE + ao + h; };
+    auto bb = [&](int slot, int h) { return smem + slot * STAGE + bo0 + h; };
+    Frags<NV> f0, f1;
+#pragma unroll
+    for (int r = 0; r < NV + NI; r++) frag_read<NV, SWAP>(f0, r, ab(0, h0), bb(0, h0));
+    auto none = [](int) {};
+    int kt = 0;
+    for (; kt + 2 < nk; kt++) {  // slice kt; slice kt+2's loads go out during its second step
+        const int slot = kt & 1;
+        pipe_step<NV, SWAP, true>(f0, f1, ab(slot, h1), bb(slot, h1), acc, 0, none);
+        wait_vmcnt<0>();
+        __syncthreads();
+        const size_t bo = b_off(kt + 2);
+        auto dma = [&](int d) { load(kt + 2, bo, d); };
+        pipe_step<NV, SWAP, true>(f1, f0, ab(slot ^ 1, h0), bb(slot ^ 1, h0), acc, LOADS, dma);
+    }
+    if (kt + 1 < nk) {  // the last but one slice: nothing left to load
+        const int slot = kt & 1;
+        pipe_step<NV, SWAP, true>(f0, f1, ab(slot, h1), bb(slot, h1), acc, 0, none);
+        wait_vmcnt<0>();
+        __syncthreads();
+        pipe_step<NV, SWAP, true>(f1, f0, ab(slot ^ 1, h0), bb(slot ^ 1, h0), acc, 0, none);
+        kt++;
+    }
+    {  // the last slice
+        const int slot = kt & 1;
+        pipe_step<NV, SWAP, true>(f0, f1, ab(slot, h1), bb(slot, h1), acc, 0, none);
+        pipe_step<NV, SWAP, false>(f1, f0, ab(slot, h0), bb(slot, h0), acc, 0, none);
+    }
+    __syncthreads();
+}
+#endif
 
 // Runs the K loop with the wave's block count as a constant.
-template <bool SWAP, int NV = MI, class Pre>
-__device__ __forceinline__ void run_k_loop(int nv, const uint16_t *const (&a_src)[A_LD],
-                                           const uint16_t *const (&b_src)[B_LD], int K, int ksp,
-                                           size_t blk, uint16_t *smem, int wm,
-                                           const int (&brow)[NI], f32x4_t (&acc)[MI][NI], int na,
-                                           Pre &pre) {
+template <bool SWAP, int NV = MI, class Src, class Pre>
+__device__ __forceinline__ void run_k_loop(int nv, const Src &src, int K, int ksp, size_t blk,
+                                           uint16_t *smem, int wm, const int (&brow)[NI],
+                                           f32x4_t (&acc)[MI][NI], int na, Pre &pre) {
     if constexpr (NV == 0) {
-        k_loop<0, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+        k_loop<0, SWAP>(src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+    } else if constexpr (OCC_GEMM_PIPE) {
+        // a wave with rows multiplies all of its blocks (those past the
+        // tile's rows hold repeated rows whose results are not stored)
+        if (nv > 0) k_loop<MI, SWAP>(src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+        else k_loop<0, SWAP>(src, K, ksp, blk, smem, wm, brow, acc, na, pre);
     } else {
-        if (nv >= NV) k_loop<NV, SWAP>(a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
-        else run_k_loop<SWAP, NV - 1>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+        if (nv >= NV) k_loop<NV, SWAP>(src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+        else run_k_loop<SWAP, NV - 1>(nv, src, K, ksp, blk, smem, wm, brow, acc, na, pre);
     }
 }
 
@@ -402,22 +567,21 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
-    const uint16_t *a_src[A_LD];
+    const uint16_t *Wg = static_cast<const uint16_t *>(a.Wg) + static_cast<size_t>(t.e) * N * K;
+    const uint16_t *Wu = static_cast<const uint16_t *>(a.Wu) + static_cast<size_t>(t.e) * N * K;
+    PtrSrc src;
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
         const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
         const int row = t.seg + t.m0 + r;
-        const int src = a.a_rows ? a.a_rows[row] : row;
-        a_src[i] = A + static_cast<size_t>(src) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
+        const int arow = a.a_rows ? a.a_rows[row] : row;
+        src.a[i] = A + static_cast<size_t>(arow) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
-    const uint16_t *Wg = static_cast<const uint16_t *>(a.Wg) + static_cast<size_t>(t.e) * N * K;
-    const uint16_t *Wu = static_cast<const uint16_t *>(a.Wu) + static_cast<size_t>(t.e) * N * K;
-    const uint16_t *b_src[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
         const int rb = r0 + i * ROWS_PER_PASS;
         const int f = min(t.n0 + (rb & 127), N - 1);
-        b_src[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + fetch_chunk(rb) * 8;
+        src.b[i] = (rb < 128 ? Wg : Wu) + static_cast<size_t>(f) * K + fetch_chunk(rb) * 8;
     }
 
     const int l = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;  // wm < WAVES_M
@@ -438,7 +602,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     auto pre = [&] {
         if (tid < t.rows) s_w[tid] = a.row_w ? a.row_w[t.seg + t.m0 + tid] : 1.f;
     };
-    run_k_loop<true>(nv, a_src, b_src, K, K, 0, smem, wm, brow, acc, na, pre);
+    run_k_loop<true>(nv, src, K, K, 0, smem, wm, brow, acc, na, pre);
 
     // SwiGLU + modulation in registers (the sigmoid's division by the
     // hardware reciprocal: the result is rounded to bf16, and the IEEE
@@ -514,21 +678,20 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
     const int K = a.K, N = a.N, ksp = a.k_split;
     const uint16_t *A = static_cast<const uint16_t *>(a.A);
-    const uint16_t *a_src[A_LD];
+    // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
+    const uint16_t *W = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(t.e) * N * K;
+    PtrSrc src;
 #pragma unroll
     for (int i = 0; i < A_LD; i++) {
         const int r = min(r0 + i * ROWS_PER_PASS, t.rows - 1);
         const int row = t.seg + t.m0 + r;
-        const int src = a.rows ? a.rows[row] : row;
-        a_src[i] = A + static_cast<size_t>(src) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
+        const int arow = a.rows ? a.rows[row] : row;
+        src.a[i] = A + static_cast<size_t>(arow) * K + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
-    // W is (blocks of N x ksp) along K; routed experts have one block (ksp = K).
-    const uint16_t *W = static_cast<const uint16_t *>(a.W) + static_cast<size_t>(t.e) * N * K;
-    const uint16_t *b_src[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; i++) {
         const int n = min(t.n0 + r0 + i * ROWS_PER_PASS, N - 1);
-        b_src[i] = W + static_cast<size_t>(n) * ksp + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
+        src.b[i] = W + static_cast<size_t>(n) * ksp + fetch_chunk(r0 + i * ROWS_PER_PASS) * 8;
     }
     const size_t blk = static_cast<size_t>(N) * ksp;
 
@@ -558,7 +721,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
             s_dst[tid] = a.phase == 3 && tid >= t.first ? ~erow : a.dst_rows[erow];
         }
     };
-    run_k_loop<false>(nv, a_src, b_src, K, ksp, blk, smem, wm, brow, acc, na, pre);
+    run_k_loop<false>(nv, src, K, ksp, blk, smem, wm, brow, acc, na, pre);
 
     float *out = a.out;
 #pragma unroll
@@ -620,6 +783,10 @@ int dense_row_tiles(int M, int n_tiles) {
 
 hipError_t OCC_NAMED(launch_gemm_up_bf16)(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
     UpArgs b = a;
+#ifdef OCC_GEMM_DENSE_ONLY
+    // routed row-tile schedules are cut for the grouped builds' tile height
+    if (a.seg_off) return hipErrorInvalidValue;
+#endif
     const int n_tiles = static_cast<int>(ceil_div(a.N, 128));
     if (!a.seg_off) {
         b.m_tiles = dense_row_tiles(a.M, n_tiles);
@@ -633,6 +800,10 @@ hipError_t OCC_NAMED(launch_gemm_up_bf16)(const UpArgs &a, size_t max_m_tiles, h
 
 hipError_t OCC_NAMED(launch_gemm_down_bf16)(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
     DownArgs b = a;
+#ifdef OCC_GEMM_DENSE_ONLY
+    // routed row-tile schedules are cut for the grouped builds' tile height
+    if (a.seg_off) return hipErrorInvalidValue;
+#endif
     const int n_tiles = static_cast<int>(ceil_div(a.N, BN));
     if (!a.seg_off) {
         b.m_tiles = dense_row_tiles(a.M, n_tiles);

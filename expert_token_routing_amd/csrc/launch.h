@@ -117,6 +117,13 @@ constexpr int kGemmBmBf16Small = 128;
 constexpr int kSmallTileRows = 96;
 hipError_t launch_gemm_up_bf16_m128(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 hipError_t launch_gemm_down_bf16_m128(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
+// The same, four-wave and software-pipelined with 256 x 256 tiles
+// (gemm_bf16_dense.hip), for dense products only (seg_off NULL; a routed
+// launch returns hipErrorInvalidValue).  Taken by dense products of at least
+// kDensePipeRounds rounds of tiles on the CUs.
+constexpr int kDensePipeRounds = 8;
+hipError_t launch_gemm_up_bf16_dense(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
+hipError_t launch_gemm_down_bf16_dense(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 
 // --- the same two GEMMs in fp32 on the vector ALUs (gemm_f32.hip) ---
 hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s);

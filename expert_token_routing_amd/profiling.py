@@ -185,6 +185,7 @@ def _main(argv=None):
     else:
         sources = {"k_gemm_up": "gemm_bf16.hip", "k_gemm_down": "gemm_bf16.hip",
                    "k_gemm_up_m128": "gemm_bf16.hip", "k_gemm_down_m128": "gemm_bf16.hip",
+                   "k_gemm_up_dense": "gemm_bf16.hip", "k_gemm_down_dense": "gemm_bf16.hip",
                    "k_gate_bf16": "gate.hip", "k_sim_gram": "similarity.hip",
                    "k_dispatch": "rows.hip", "k_combine": "rows.hip",
                    "k_merge_slots": "rows.hip",
