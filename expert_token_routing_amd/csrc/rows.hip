@@ -173,13 +173,26 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     const int t = gw / SPLIT;
     if (t >= T) return;
     const int c0 = (gw - t * SPLIT) * (VPL * kWave) + lane;  // this lane's first float4 column
-    int p = 0x7fffffff, erow = 0;
+    // Independent loads first, so that their latencies overlap: the token's
+    // experts and EPD rows, its SFD row in every group (lane g: BRIM_0[g,
+    // t]; only the groups it uses are read below) and the shared experts'
+    // row.
+    int e = 0, erow = 0, grow = 0;
     if (lane < k) {
         const size_t o = static_cast<size_t>(t) * k + lane;
-        const int e = ids[o];
-        p = tab.grp[e] * tab.n + tab.slot[e];
+        e = ids[o];
         erow = tok_epd[o];
     }
+    if (lane < tab.Nd) grow = brim0[static_cast<size_t>(lane) * T + t];
+    f32x4 ys[VPL];
+    if constexpr (Y != 0) {
+        if (y_sh) {
+            const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
+#pragma unroll
+            for (int i = 0; i < VPL; i++) ys[i] = __builtin_nontemporal_load(src + min(c0 + kWave * i, row_vec4 - 1));
+        }
+    }
+    const int p = lane < k ? tab.grp[e] * tab.n + tab.slot[e] : 0x7fffffff;
     int rank = 0;
     for (int j = 0; j < k; j++) rank += __shfl(p, j) < p;
     int sp = 0, se = 0;  // lane r: position and EPD row of the r-th expert
@@ -194,7 +207,8 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     const int sg = sp / tab.n;
     const int prev_g = __shfl(sg, lane > 0 ? lane - 1 : 0);
     const int opens = lane == 0 || prev_g != sg;
-    const int src_row = lane < k && opens ? brim0[static_cast<size_t>(sg) * T + t] : se;
+    const int g_row = __shfl(grow, lane < k ? sg : 0);
+    const int src_row = lane < k && opens ? g_row : se;
     f32x4 acc[VPL], ya[VPL], cur[VPL], nxt[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
@@ -232,9 +246,8 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
     }
     if constexpr (Y != 0) {
         if (y_sh) {
-            const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
 #pragma unroll
-            for (int i = 0; i < VPL; i++) ya[i] += src[min(c0 + kWave * i, row_vec4 - 1)];
+            for (int i = 0; i < VPL; i++) ya[i] += ys[i];
         }
 #pragma unroll
         for (int i = 0; i < VPL; i++) {
