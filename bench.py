@@ -326,6 +326,11 @@ def measure(args, wl, headline):
 
     sroof, design = stage_rooflines(wl, stages, ms, main_flags, nsfd_alg1, active, profiling)
     roofline = dominant_roofline(wl, stages, nsfd_alg1, active, profiling)
+    if res_other is not None:
+        # the other merge's stages against the same algorithmic work (its
+        # combine is the separate pass of Algorithm 9 under the atomic merge)
+        res_other["stage_roofline"] = stage_rooflines(
+            wl, stages_o, res_other["ms_per_step"], other_flags, nsfd_alg1, active, profiling)[0]
 
     # --- training step: forward keeping the backward's state, then backward
     train = None
