@@ -13,8 +13,10 @@
 //         W_down is added in fp32 to its SFD row (several experts of one group
 //         share that row -- the intra-group pre-aggregation of section 3.1).
 //
-// Tiling: a 512-thread workgroup (8 waves, one workgroup per CU, two waves
-// per SIMD) computes a tile of up to 320 rows x 256 MFMA output columns.  The
+// Tiling (the grouped build; the dense build's four-wave pipelined loop is
+// described where it is defined): a 512-thread workgroup (8 waves, one
+// workgroup per CU, two waves per SIMD) computes a tile of up to 320 rows x
+// 256 MFMA output columns.  The
 // rows come in 16-row blocks dealt to the four wave rows in turn, and each
 // wave holds 128 columns of its blocks.  In the up GEMM the 256 columns
 // are 128 gate and 128 up rows of the same output features, so the SwiGLU
