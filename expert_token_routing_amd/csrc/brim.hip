@@ -33,6 +33,8 @@ constexpr int kBlocksPerChunk = kBrimChunk / kWave;  // 64-token blocks of a chu
 constexpr int kBrimThreads = 1024;  // count and fill: one thread per routing entry
 constexpr int kScanLds = 14336;     // (bin, chunk) counts the scan keeps in LDS
 constexpr int kScanBatch = 8;       // 64-chunk scan steps whose counts are loaded together
+constexpr int kRegBins = 8;        // bins per wave whose scans the scan can keep in registers
+constexpr int kLoadBatch = 8;      // loads a thread keeps in flight in the scan's copy loops
 
 // Is any position in [lo, hi) set in the 256-bit position mask em?
 __device__ __forceinline__ bool any_in(const uint64_t *em, int lo, int hi) {
@@ -139,8 +141,52 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     // the (chunk, bin) counts come in with one coalesced pass when they fit
     const bool staged = n <= static_cast<size_t>(kScanLds);
     if (staged) {
-        for (size_t i = threadIdx.x; i < n; i += blockDim.x) s_cc[i] = chunk_cnt[i];
+        // kLoadBatch loads in flight per thread, not one round trip each
+        for (size_t i0 = threadIdx.x; i0 < n; i0 += static_cast<size_t>(blockDim.x) * kLoadBatch) {
+            int v[kLoadBatch];
+#pragma unroll
+            for (int j = 0; j < kLoadBatch; j++) {
+                const size_t i = i0 + static_cast<size_t>(j) * blockDim.x;
+                v[j] = i < n ? chunk_cnt[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kLoadBatch; j++) {
+                const size_t i = i0 + static_cast<size_t>(j) * blockDim.x;
+                if (i < n) s_cc[i] = v[j];
+            }
+        }
         __syncthreads();
+    }
+    // Not staged, but every bin within one batch of scan steps and few bins
+    // per wave: the counts of all of a wave's bins are loaded at once and
+    // their scans stay in registers until the bin offsets are known, so that
+    // step 3 stores them without reading them back.
+    const bool in_regs = !staged && nchunks <= kWave * kScanBatch && NB <= nw * kRegBins;
+    int rv[kRegBins][kScanBatch];
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kRegBins; i++) {
+            const int b = wv + i * nw;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; j++) {
+                const int c = j * kWave + lane;
+                rv[i][j] = b < NB && c < nchunks ? chunk_cnt[static_cast<size_t>(b) * nchunks + c] : 0;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRegBins; i++) {
+            const int b = wv + i * nw;
+            if (b >= NB) break;  // wave-uniform
+            int run = 0;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; j++) {
+                if (j * kWave >= nchunks) break;  // wave-uniform
+                const int incl = wave_incl_scan(rv[i][j]);
+                rv[i][j] = run + incl - rv[i][j];
+                run += __shfl(incl, kWave - 1);
+            }
+            if (lane == 0) total[b] = run;
+        }
     }
 
     // 1. per bin, exclusive scan over chunks (64 chunks per wave step).  The
@@ -148,7 +194,7 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     //    kScanBatch steps is loaded before it is scanned: one round trip per
     //    batch instead of one per step (at 512 chunks x 124 bins the serial
     //    loads took the scan to 118 us).  Staged scans stay in LDS until step 3.
-    for (int b = wv; b < NB; b += nw) {
+    for (int b = in_regs ? NB : wv; b < NB; b += nw) {
         int run = 0;
         const size_t row = static_cast<size_t>(b) * nchunks;
         for (int c0 = 0; c0 < nchunks; c0 += kWave * kScanBatch) {
@@ -220,8 +266,32 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     __syncthreads();
 
     // 3. each (bin, chunk) start = start of the bin + rows of earlier chunks
-    for (size_t i = threadIdx.x; i < n; i += blockDim.x)
-        chunk_base[i] = (staged ? s_cc[i] : chunk_base[i]) + binoff[i / nchunks];
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kRegBins; i++) {
+            const int b = wv + i * nw;
+            if (b >= NB) break;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; j++) {
+                const int c = j * kWave + lane;
+                if (c < nchunks) chunk_base[static_cast<size_t>(b) * nchunks + c] = rv[i][j] + binoff[b];
+            }
+        }
+        return;
+    }
+    for (size_t i0 = threadIdx.x; i0 < n; i0 += static_cast<size_t>(blockDim.x) * kLoadBatch) {
+        int v[kLoadBatch];
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; j++) {
+            const size_t i = i0 + static_cast<size_t>(j) * blockDim.x;
+            v[j] = i < n ? (staged ? s_cc[i] : chunk_base[i]) : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; j++) {
+            const size_t i = i0 + static_cast<size_t>(j) * blockDim.x;
+            if (i < n) chunk_base[i] = v[j] + binoff[i / nchunks];
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
