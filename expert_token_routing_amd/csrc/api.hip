@@ -67,6 +67,12 @@ GemmOps gemm_ops(const occ_layer_desc &D) {
     return {launch_gemm_up_bf16, launch_gemm_down_bf16, kGemmBmBf16};
 }
 int tile_rows(const occ_layer_desc &D) { return gemm_ops(D).bm; }
+// The routed row-tile schedule fills the up-projection's last round of the
+// CUs on the 320-row build (column tiles of 128 features); the other builds
+// take ceil(rows / capacity) tiles per expert.
+int fill_cols(const occ_layer_desc &D) {
+    return gemm_ops(D).up == launch_gemm_up_bf16 ? static_cast<int>(ceil_div(D.F, 128)) : 0;
+}
 
 // Dense products (the shared experts) that fill at least kDensePipeRounds
 // rounds of the CUs with 256 x 256 tiles take the pipelined four-wave build;
@@ -378,7 +384,8 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const 
     int32_t *ids_ws = at<int32_t>(workspace, L.ids);
     float *w_ws = at<float>(workspace, L.w);
     OCC_HIP(launch_sanitize_ids(ids, w, desc->T, desc->k, desc->Ne, ids_ws, w_ws, s));
-    OCC_HIP(launch_brim(ids_ws, w_ws, desc->T, desc->k, tab, tile_rows(*desc), dense_brim1 != 0,
+    OCC_HIP(launch_brim(ids_ws, w_ws, desc->T, desc->k, tab, tile_rows(*desc), fill_cols(*desc),
+                        dense_brim1 != 0,
                         brim_bufs(workspace, L), s));
     *out_host = brim_view(workspace, L);
     return OCC_OK;
@@ -444,7 +451,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
     const size_t T = D.T;
     const GemmOps ops = gemm_ops(D);
     const size_t bm = ops.bm;
-    const size_t routed_tiles = (T * D.k + bm - 1) / bm + D.Ne;
+    const size_t routed_tiles = (T * D.k + bm - 1) / bm + D.Ne + kBrimMaxFill;
     const size_t shared_tiles = (T + bm - 1) / bm;
 
     OCC_TRY(mark(0));
@@ -462,7 +469,7 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         OCC_HIP(launch_sanitize_ids(ids_in, w_in, D.T, D.k, D.Ne, ids, w, s));
     OCC_TRY(mark(1));
     // Algorithms 3 and 5: BRIM_0, BRIM_1 (condensed), GEMM tile schedule
-    OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), 0, bb, s));
+    OCC_HIP(launch_brim(ids, w, D.T, D.k, tab, static_cast<int>(bm), fill_cols(D), 0, bb, s));
     OCC_TRY(mark(2));
     // Small batches (experts averaging fewer than 128 rows) merge in one
     // down-projection launch of atomic adds, whose SFD accumulator rows the

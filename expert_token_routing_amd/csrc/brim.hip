@@ -123,8 +123,53 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__re
         chunk_cnt[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = cnt[b];
 }
 
+// The grouped GEMMs' row-tile schedule, filled to whole rounds of the CUs
+// (run by one wave).  With ceil(rows / capacity) tiles per expert, the
+// up-projection's T0 x fill_cols tiles end in a partly empty round of the
+// `slots` workgroups the GPU runs at once; the experts take extra row tiles,
+// one at a time, until the count is the most that still fits the same number
+// of rounds: each to the expert whose tiles hold the most rows (rows / tiles
+// largest; ties to the lower placement position) among those whose tiles
+// could still lose a 16-row block.  An expert's rows are shared out evenly
+// over its tiles, so its tiles get shorter and the last round fills (at most
+// kBrimMaxFill extra tiles).
+__device__ void fill_rounds(const int *rows, int *vt, int Ne, int fill_cols, int slots) {
+    const int lane = lane_id();
+    int t0 = 0;
+    for (int p = lane; p < Ne; p += kWave) t0 += vt[p];
+    t0 = wave_sum_i(t0);
+    const int64_t cols = fill_cols, rounds = (static_cast<int64_t>(t0) * cols + slots - 1) / slots;
+    const int64_t room = rounds * slots / cols - t0;
+    const int extra = static_cast<int>(room < kBrimMaxFill ? room : kBrimMaxFill);
+    for (int it = 0; it < extra; it++) {
+        int best = -1, bv = 0, bt = 1;  // this lane's candidate: rows bv over bt tiles
+        for (int p = lane; p < Ne; p += kWave) {
+            const int v = rows[p], t = vt[p];
+            if (t == 0 || t >= (v + 15) / 16) continue;
+            if (best < 0 || static_cast<int64_t>(v) * bt > static_cast<int64_t>(bv) * t) {
+                best = p;
+                bv = v;
+                bt = t;
+            }
+        }
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            const int ob = __shfl_xor(best, off), ov = __shfl_xor(bv, off), ot = __shfl_xor(bt, off);
+            const int64_t lhs = static_cast<int64_t>(ov) * bt, rhs = static_cast<int64_t>(bv) * ot;
+            if (ob >= 0 && (best < 0 || lhs > rhs || (lhs == rhs && ob < best))) {
+                best = ob;
+                bv = ov;
+                bt = ot;
+            }
+        }
+        if (best < 0) break;  // the same on every lane
+        if (lane == 0) vt[best] += 1;
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ chunk_cnt,
                                                     int nchunks, int Nd, int Ne, int tile_rows,
+                                                    int fill_cols, int slots,
                                                     int32_t *__restrict__ chunk_base,
                                                     int32_t *__restrict__ sfd_off,
                                                     int32_t *__restrict__ epd_off,
@@ -134,6 +179,7 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ tile_off_rest) {
     __shared__ int total[kMaxBins];
     __shared__ int binoff[kMaxBins];
+    __shared__ int s_vt[kMaxNe];
     __shared__ int s_cc[kScanLds];
     const int NB = Nd + 2 * Ne;
     const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
@@ -232,12 +278,15 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
             sfd_off[lane] = ig - vg;
         }
         if (lane == kWave - 1) sfd_off[Nd] = ig;
+        // row tiles per expert: ceil(rows / tile_rows), raised by fill_rounds
+        for (int p = lane; p < Ne; p += kWave) s_vt[p] = (total[Nd + p] + tile_rows - 1) / tile_rows;
+        if (fill_cols > 0) fill_rounds(total + Nd, s_vt, Ne, fill_cols, slots);
         int run = 0, run_t = 0, run_f = 0, run_r = 0;
         for (int p0 = 0; p0 < Ne; p0 += kWave) {
             const int p = p0 + lane;
             const int v = p < Ne ? total[Nd + p] : 0;
             const int f = p < Ne ? total[Nd + Ne + p] : 0;
-            const int vt = (v + tile_rows - 1) / tile_rows;
+            const int vt = p < Ne ? s_vt[p] : 0;
             const int vf = (f + tile_rows - 1) / tile_rows;
             const int vr = (v - f + tile_rows - 1) / tile_rows;
             const int inc = wave_incl_scan(v), inc_t = wave_incl_scan(vt);
@@ -388,10 +437,12 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
 }  // namespace
 
 hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
-                       int tile_rows, int dense_brim1, const BrimBufs &b, hipStream_t s) {
+                       int tile_rows, int fill_cols, int dense_brim1, const BrimBufs &b,
+                       hipStream_t s) {
     const int nchunks = static_cast<int>(ceil_div(T, kBrimChunk));
     k_brim_count<<<nchunks, kBrimThreads, 0, s>>>(ids, T, k, tab, b.chunk_cnt);
-    k_brim_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, tab.Nd, tab.Ne, tile_rows, b.chunk_base,
+    k_brim_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, tab.Nd, tab.Ne, tile_rows, fill_cols,
+                                   compute_units(), b.chunk_base,
                                    b.sfd_off, b.epd_off, b.tile_off, b.first_cnt,
                                    b.tile_off_first, b.tile_off_rest);
     k_brim_fill<<<nchunks, kBrimThreads, 0, s>>>(ids, w, T, k, tab, b.chunk_base, b.sfd_off,

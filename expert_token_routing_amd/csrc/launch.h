@@ -40,8 +40,14 @@ struct BrimBufs {
     int32_t *down_rows, *first_cnt, *tile_off_first, *tile_off_rest;
     int32_t *chunk_cnt, *chunk_base;
 };
+// tile_rows: the grouped GEMMs' row-tile capacity.  fill_cols > 0: the
+// up-projection's column tiles; the experts then take extra row tiles (at
+// most kBrimMaxFill) until the up-projection's tiles fill their last round
+// of the CUs.
+constexpr int kBrimMaxFill = 64;
 hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
-                       int tile_rows, int dense_brim1, const BrimBufs &b, hipStream_t s);
+                       int tile_rows, int fill_cols, int dense_brim1, const BrimBufs &b,
+                       hipStream_t s);
 
 // --- row movers (rows.hip) ---
 // x_sfd[brim0[g, t]] = x[t] for every group the token uses; with zero_out,

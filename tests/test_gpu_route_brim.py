@@ -112,6 +112,30 @@ def gpu_brim(wl, ids_t, w_t, placement, dense=True):
                 brim1=v(b.brim1, (wl.n * N_sfd,)) if dense else None)
 
 
+def tile_schedule(wl, loads, bm):
+    """The grouped GEMMs' row tiles per expert: ceil(rows / bm), and on the
+    320-row build, extra tiles until the up-projection's tiles (ceil(F / 128)
+    column tiles per row tile) fill their last round of the CUs: one at a
+    time, at most 64, each to the expert whose tiles hold the most rows
+    (ties to the lower placement position) among those whose tiles could
+    still lose a 16-row block."""
+    from fractions import Fraction
+    vt = (loads + bm - 1) // bm
+    if bm != 320:
+        return vt
+    cols = -(-wl.F // 128)
+    slots = torch.cuda.get_device_properties(0).multi_processor_count
+    t0 = int(vt.sum())
+    rounds = -(-t0 * cols // slots)
+    for _ in range(min(rounds * slots // cols - t0, 64)):
+        cand = [p for p in range(len(vt)) if 0 < vt[p] < -(-loads[p] // 16)]
+        if not cand:
+            break
+        best = max(cand, key=lambda p: (Fraction(int(loads[p]), int(vt[p])), -p))
+        vt[best] += 1
+    return vt
+
+
 def check_brim(wl, placement, ids_g=None, w_g=None):
     """The device's BRIM from the oracle's routing (ids, fp32 weights)
     against the oracle's literal counter loops on the same routing."""
@@ -140,7 +164,7 @@ def check_brim(wl, placement, ids_g=None, w_g=None):
     # when the experts average fewer than 96 rows, else tiles of up to 320
     bm = (64 if wl.dtype != W.DTYPE_BF16 else 128 if wl.T * wl.k < 96 * wl.Ne else 320)
     loads = np.diff(b["epd_off"])
-    assert np.array_equal(np.diff(b["tile_off"]), (loads + bm - 1) // bm)
+    assert np.array_equal(np.diff(b["tile_off"]), tile_schedule(wl, loads, bm))
     # merge order: per expert, the EPD rows that are the first (lowest-slot)
     # contributor to their SFD row, then the others, each in token order
     pos = np.empty(wl.Ne, np.int64)
