@@ -685,7 +685,7 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     int32_t *bt_first = at<int32_t>(workspace, L.bt_first);
     int32_t *bt_rest = at<int32_t>(workspace, L.bt_rest);
     float *dx_sh = D.n_shared > 0 ? at<float>(workspace, L.dx_sh) : nullptr;
-    const size_t routed_tiles = (T * D.k + kBwdRowTile - 1) / kBwdRowTile + D.Ne;
+    const size_t routed_tiles = (T * D.k + kBwdRowTile - 1) / kBwdRowTile + D.Ne + kBrimMaxFill;
     const bool det = D.flags & OCC_FLAG_DETERMINISTIC;
     const bool one_launch = !det && static_cast<int64_t>(D.T) * D.k < 128ll * D.Ne;
 
@@ -694,8 +694,11 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     // K-major operands
     const size_t zero_elems = std::max<size_t>({d, 2 * F, 2 * Nsh, kBwdTile});
     OCC_HIP(launch_fill_i32(static_cast<int32_t *>(zero_row), zero_elems * es / 4, 0, s));
-    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdRowTile, bt_all, bt_first,
-                              bt_rest, s));
+    // the all-rows schedule filled for the SwiGLU backward's ceil(F / 256)
+    // column tiles (the input gradient's d / 256 then need no more rounds)
+    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdRowTile,
+                              static_cast<int>(ceil_div(F, kBwdTile)), bt_all, bt_first, bt_rest,
+                              s));
     // dy ORI -> SFD: the combine's transpose copies dy into each replica (and
     // zeroes the dx accumulator rows when the merge is one launch of adds)
     OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s,

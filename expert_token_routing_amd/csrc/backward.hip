@@ -7,20 +7,26 @@ namespace occ {
 namespace {
 
 // One workgroup, thread p owns placement position p; a serial scan over the
-// (at most 256) positions by thread 0 keeps it trivially deterministic.
+// (at most 256) positions by thread 0 keeps it trivially deterministic.  The
+// all-rows schedule is filled to whole rounds of the CUs for fill_cols
+// column tiles (fill_rounds), as the forward's is.
 __global__ __launch_bounds__(kMaxNe) void k_tile_sched(const int32_t *__restrict__ epd_off,
                                                        const int32_t *__restrict__ first_cnt,
-                                                       int Ne, int bm, int32_t *__restrict__ t_all,
+                                                       int Ne, int bm, int fill_cols, int slots,
+                                                       int32_t *__restrict__ t_all,
                                                        int32_t *__restrict__ t_first,
                                                        int32_t *__restrict__ t_rest) {
-    __shared__ int s_all[kMaxNe], s_first[kMaxNe], s_rest[kMaxNe];
+    __shared__ int s_len[kMaxNe], s_all[kMaxNe], s_first[kMaxNe], s_rest[kMaxNe];
     const int p = threadIdx.x;
     if (p < Ne) {
         const int len = epd_off[p + 1] - epd_off[p], f = first_cnt[p];
+        s_len[p] = len;
         s_all[p] = (len + bm - 1) / bm;
         s_first[p] = (f + bm - 1) / bm;
         s_rest[p] = (len - f + bm - 1) / bm;
     }
+    __syncthreads();
+    if (fill_cols > 0 && p < kWave) fill_rounds(s_len, s_all, Ne, fill_cols, slots, kBrimMaxFill);
     __syncthreads();
     if (p == 0) {
         int a = 0, f = 0, r = 0;
@@ -109,10 +115,10 @@ __global__ __launch_bounds__(kRbWaves *kWave) void k_route_backward(
 }  // namespace
 
 hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, int Ne,
-                             int tile_rows, int32_t *tile_off, int32_t *tile_off_first,
-                             int32_t *tile_off_rest, hipStream_t s) {
-    k_tile_sched<<<1, kMaxNe, 0, s>>>(epd_off, first_cnt, Ne, tile_rows, tile_off, tile_off_first,
-                                      tile_off_rest);
+                             int tile_rows, int fill_cols, int32_t *tile_off,
+                             int32_t *tile_off_first, int32_t *tile_off_rest, hipStream_t s) {
+    k_tile_sched<<<1, kMaxNe, 0, s>>>(epd_off, first_cnt, Ne, tile_rows, fill_cols, compute_units(),
+                                      tile_off, tile_off_first, tile_off_rest);
     return hipGetLastError();
 }
 

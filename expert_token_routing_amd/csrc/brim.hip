@@ -123,50 +123,6 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__re
         chunk_cnt[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = cnt[b];
 }
 
-// The grouped GEMMs' row-tile schedule, filled to whole rounds of the CUs
-// (run by one wave).  With ceil(rows / capacity) tiles per expert, the
-// up-projection's T0 x fill_cols tiles end in a partly empty round of the
-// `slots` workgroups the GPU runs at once; the experts take extra row tiles,
-// one at a time, until the count is the most that still fits the same number
-// of rounds: each to the expert whose tiles hold the most rows (rows / tiles
-// largest; ties to the lower placement position) among those whose tiles
-// could still lose a 16-row block.  An expert's rows are shared out evenly
-// over its tiles, so its tiles get shorter and the last round fills (at most
-// kBrimMaxFill extra tiles).
-__device__ void fill_rounds(const int *rows, int *vt, int Ne, int fill_cols, int slots) {
-    const int lane = lane_id();
-    int t0 = 0;
-    for (int p = lane; p < Ne; p += kWave) t0 += vt[p];
-    t0 = wave_sum_i(t0);
-    const int64_t cols = fill_cols, rounds = (static_cast<int64_t>(t0) * cols + slots - 1) / slots;
-    const int64_t room = rounds * slots / cols - t0;
-    const int extra = static_cast<int>(room < kBrimMaxFill ? room : kBrimMaxFill);
-    for (int it = 0; it < extra; it++) {
-        int best = -1, bv = 0, bt = 1;  // this lane's candidate: rows bv over bt tiles
-        for (int p = lane; p < Ne; p += kWave) {
-            const int v = rows[p], t = vt[p];
-            if (t == 0 || t >= (v + 15) / 16) continue;
-            if (best < 0 || static_cast<int64_t>(v) * bt > static_cast<int64_t>(bv) * t) {
-                best = p;
-                bv = v;
-                bt = t;
-            }
-        }
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            const int ob = __shfl_xor(best, off), ov = __shfl_xor(bv, off), ot = __shfl_xor(bt, off);
-            const int64_t lhs = static_cast<int64_t>(ov) * bt, rhs = static_cast<int64_t>(bv) * ot;
-            if (ob >= 0 && (best < 0 || lhs > rhs || (lhs == rhs && ob < best))) {
-                best = ob;
-                bv = ov;
-                bt = ot;
-            }
-        }
-        if (best < 0) break;  // the same on every lane
-        if (lane == 0) vt[best] += 1;
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
 __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ chunk_cnt,
                                                     int nchunks, int Nd, int Ne, int tile_rows,
                                                     int fill_cols, int slots,
@@ -280,7 +236,7 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
         if (lane == kWave - 1) sfd_off[Nd] = ig;
         // row tiles per expert: ceil(rows / tile_rows), raised by fill_rounds
         for (int p = lane; p < Ne; p += kWave) s_vt[p] = (total[Nd + p] + tile_rows - 1) / tile_rows;
-        if (fill_cols > 0) fill_rounds(total + Nd, s_vt, Ne, fill_cols, slots);
+        if (fill_cols > 0) fill_rounds(total + Nd, s_vt, Ne, fill_cols, slots, kBrimMaxFill);
         int run = 0, run_t = 0, run_f = 0, run_r = 0;
         for (int p0 = 0; p0 < Ne; p0 += kWave) {
             const int p = p0 + lane;

@@ -118,4 +118,89 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
 
 inline unsigned ceil_div(size_t a, size_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
+// Maximum of an unsigned 64-bit value over the wave (both halves moved by
+// the same DPP steps as the scans above; 0 is the identity).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = static_cast<uint32_t>(dpp_i<CTRL, ROW_MASK>(0, static_cast<int>(v)));
+    const uint32_t hi = static_cast<uint32_t>(dpp_i<CTRL, ROW_MASK>(0, static_cast<int>(v >> 32)));
+    return static_cast<uint64_t>(hi) << 32 | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<kDppRowShr1, 0xf>(v), v = o > v ? o : v;
+    o = dpp_u64<kDppRowShr2, 0xf>(v), v = o > v ? o : v;
+    o = dpp_u64<kDppRowShr4, 0xf>(v), v = o > v ? o : v;
+    o = dpp_u64<kDppRowShr8, 0xf>(v), v = o > v ? o : v;
+    o = dpp_u64<kDppRowBcast15, 0xa>(v), v = o > v ? o : v;
+    o = dpp_u64<kDppRowBcast31, 0xc>(v), v = o > v ? o : v;
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), kWave - 1);
+    return static_cast<uint64_t>(hi) << 32 | lo;
+}
+
+// A grouped GEMM's row-tile schedule, filled to whole rounds of the CUs
+// (run by one wave; vt[p] holds ceil(rows[p] / capacity) on entry, p < Ne
+// <= 256).  With those tiles, a product of T0 row tiles x fill_cols column
+// tiles ends in a partly empty round of the `slots` workgroups the GPU runs
+// at once; the experts take extra row tiles, one at a time, until the count
+// is the most that still fits the same number of rounds: each to the expert
+// whose tiles hold the most rows (rows / tiles largest; ties to the lower
+// placement position) among those whose tiles could still lose a 16-row
+// block.  An expert's rows are shared out evenly over its tiles, so its
+// tiles get shorter and the last round fills (at most max_fill extra tiles).
+// Lane l keeps experts l + 64 j in registers; each step takes the wave's
+// largest key floor(rows / tiles * 2^40) * 256 + (255 - p) (a 64-bit DPP max
+// over the lanes), which orders the experts exactly as their rows / tiles
+// while an expert has at most 4096 tiles.
+__device__ inline uint64_t fill_key(int rows, int tiles, int p) {
+    if (tiles == 0 || tiles >= (rows + 15) / 16) return 0;  // cannot split further
+    // rows / tiles <= the tile capacity (< 512): the fp64 quotient is
+    // correctly rounded and its 40 fractional bits keep distinct ratios of
+    // experts with at most 4096 tiles apart (no integer division)
+    const double r = static_cast<double>(rows) / static_cast<double>(tiles);
+    return static_cast<uint64_t>(r * 1099511627776.0) << 8 | static_cast<uint64_t>(255 - p);
+}
+__device__ inline void fill_rounds(const int *rows, int *vt, int Ne, int fill_cols, int slots,
+                                   int max_fill) {
+    const int lane = lane_id();
+    int v[4], t[4];
+    uint64_t key[4];
+    int t0 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int p = lane + kWave * j;
+        v[j] = p < Ne ? rows[p] : 0;
+        t[j] = p < Ne ? vt[p] : 0;
+        key[j] = p < Ne ? fill_key(v[j], t[j], p) : 0;
+        t0 += t[j];
+    }
+    t0 = wave_sum_i(t0);
+    const int64_t cols = fill_cols, rounds = (static_cast<int64_t>(t0) * cols + slots - 1) / slots;
+    const int64_t room = rounds * slots / cols - t0;
+    const int extra = static_cast<int>(room < max_fill ? room : max_fill);
+    for (int it = 0; it < extra; it++) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int j = 1; j < 4; j++) best = key[j] > best ? key[j] : best;
+        best = wave_max_u64(best);
+        if (best == 0) break;  // wave-uniform
+        const int p = 255 - static_cast<int>(best & 255);
+        if ((p & (kWave - 1)) == lane) {
+            const int j = p / kWave;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (q == j) {
+                    t[q] += 1;
+                    key[q] = fill_key(v[q], t[q], p);
+                }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int p = lane + kWave * j;
+        if (p < Ne) vt[p] = t[j];
+    }
+}
+
 }  // namespace occ

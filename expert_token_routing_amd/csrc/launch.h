@@ -152,8 +152,9 @@ hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream
 // contributors are stored to epd_out[a_rows[pos]] instead.
 enum { BWD_EPI_SWIGLU = 0, BWD_EPI_MERGE = 1 };
 // Row capacity of the input-gradient tiles: the row schedules tile_off are
-// built with it (ceil(rows / kBwdRowTile) tiles per segment, rows shared out
-// evenly in 16-row blocks).
+// built with it (ceil(rows / kBwdRowTile) tiles per segment, the all-rows
+// schedule filled to whole rounds of the CUs; rows shared out evenly in
+// 16-row blocks).
 constexpr int kBwdRowTile = 320;
 struct BwdDgradArgs {
     const void *A;
@@ -204,8 +205,8 @@ int wgrad_k_chunk(int rows, int parts);
 // Row-tile schedules for `tile_rows`-row tiles from the expert segments
 // epd_off and first-contributor counts first_cnt (all rows, first, rest).
 hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, int Ne,
-                             int tile_rows, int32_t *tile_off, int32_t *tile_off_first,
-                             int32_t *tile_off_rest, hipStream_t s);
+                             int tile_rows, int fill_cols, int32_t *tile_off,
+                             int32_t *tile_off_first, int32_t *tile_off_rest, hipStream_t s);
 // A one-segment schedule for a dense GEMM over T rows: seg_off = {0, T},
 // tile_off = {0, m_tiles} (the rows shared out evenly over m_tiles tiles).
 hipError_t launch_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off,
