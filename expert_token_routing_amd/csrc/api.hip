@@ -385,8 +385,7 @@ occ_status occ_build_brim(const occ_layer_desc *desc, const int32_t *ids, const 
     float *w_ws = at<float>(workspace, L.w);
     OCC_HIP(launch_sanitize_ids(ids, w, desc->T, desc->k, desc->Ne, ids_ws, w_ws, s));
     OCC_HIP(launch_brim(ids_ws, w_ws, desc->T, desc->k, tab, tile_rows(*desc), fill_cols(*desc),
-                        dense_brim1 != 0,
-                        brim_bufs(workspace, L), s));
+                        dense_brim1 != 0, brim_bufs(workspace, L), s));
     *out_host = brim_view(workspace, L);
     return OCC_OK;
 }
@@ -503,11 +502,15 @@ static occ_status forward(const occ_layer_desc *desc, const void *x, const float
         sd.Ne = 1;
         sd.k_split = D.F_shared;
         sd.tab = tab;
-        if (dense_pipelined(ops, D.T, 2ll * su.N)) OCC_HIP(launch_gemm_up_bf16_dense(su, shared_tiles, s));
-        else OCC_HIP(ops.up(su, shared_tiles, s));
+        if (dense_pipelined(ops, D.T, 2ll * su.N))
+            OCC_HIP(launch_gemm_up_bf16_dense(su, shared_tiles, s));
+        else
+            OCC_HIP(ops.up(su, shared_tiles, s));
         OCC_TRY(mark(4));
-        if (dense_pipelined(ops, D.T, sd.N)) OCC_HIP(launch_gemm_down_bf16_dense(sd, shared_tiles, s));
-        else OCC_HIP(ops.down(sd, shared_tiles, s));
+        if (dense_pipelined(ops, D.T, sd.N))
+            OCC_HIP(launch_gemm_down_bf16_dense(sd, shared_tiles, s));
+        else
+            OCC_HIP(ops.down(sd, shared_tiles, s));
     } else {
         OCC_TRY(mark(4));
     }
@@ -695,10 +698,12 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     const size_t zero_elems = std::max<size_t>({d, 2 * F, 2 * Nsh, kBwdTile});
     OCC_HIP(launch_fill_i32(static_cast<int32_t *>(zero_row), zero_elems * es / 4, 0, s));
     // the all-rows schedule filled for the SwiGLU backward's ceil(F / 256)
-    // column tiles (the input gradient's d / 256 then need no more rounds)
-    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdRowTile,
-                              static_cast<int>(ceil_div(F, kBwdTile)), bt_all, bt_first, bt_rest,
-                              s));
+    // column tiles (the input gradient's product runs on the same schedule),
+    // where the forward's is filled too (not in the decode regime, whose
+    // products stream their weights and gain nothing from more tiles)
+    const int bwd_fill = fill_cols(D) > 0 ? static_cast<int>(ceil_div(F, kBwdTile)) : 0;
+    OCC_HIP(launch_tile_sched(bb.epd_off, bb.first_cnt, D.Ne, kBwdRowTile, bwd_fill, bt_all,
+                              bt_first, bt_rest, s));
     // dy ORI -> SFD: the combine's transpose copies dy into each replica (and
     // zeroes the dx accumulator rows when the merge is one launch of adds)
     OCC_HIP(launch_dispatch(dy, D.T, D.Nd, d * es, bb.brim0, dy_sfd, s,

@@ -189,7 +189,8 @@ __global__ __launch_bounds__(kRowWaves *kWave) void k_merge_slots(
         if (y_sh) {
             const f32x4 *src = y_sh + static_cast<size_t>(t) * row_vec4;
 #pragma unroll
-            for (int i = 0; i < VPL; i++) ys[i] = __builtin_nontemporal_load(src + min(c0 + kWave * i, row_vec4 - 1));
+            for (int i = 0; i < VPL; i++)
+                ys[i] = __builtin_nontemporal_load(src + min(c0 + kWave * i, row_vec4 - 1));
         }
     }
     const int p = lane < k ? tab.grp[e] * tab.n + tab.slot[e] : 0x7fffffff;
