@@ -135,7 +135,10 @@ typedef struct occ_layer_desc {
  *            [epd_off[p], epd_off[p+1]) and the first first_cnt[p] of them
  *            are first contributors.
  *   first_cnt Ne, indexed by placement position.
- *   tile_off Ne+1.  Row-tile schedule of the grouped GEMMs (internal). */
+ *   tile_off Ne+1.  Row-tile schedule of the grouped GEMMs (internal):
+ *            position p's row tiles are [tile_off[p], tile_off[p+1]), at
+ *            least ceil(rows / tile capacity) of them, more where that fills
+ *            the up-projection's last round of the GPU's compute units. */
 typedef struct occ_brim {
     int32_t *brim0;
     int32_t *sfd_off;
