@@ -206,11 +206,13 @@ def test_brim_rescheduled_placement():
     dict(T=1), dict(T=5), dict(T=1023), dict(T=1025), dict(T=3000, Nd=1),
     dict(T=2000, Ne=16, Nd=16, k=4), dict(T=1500, k=1), dict(T=999, Ne=256, Nd=64, k=8),
     dict(T=1100, Ne=60, Nd=4, k=4),
+    # schedules that take extra row tiles, with several experts per lane
+    dict(T=9000, Ne=256, Nd=64, k=8, F=1024), dict(T=20000, Ne=130, Nd=10, k=5, F=1408),
 ])
 def test_brim_ragged_and_degenerate(shape):
-    base = dict(Ne=64, Nd=8, k=8)
+    base = dict(Ne=64, Nd=8, k=8, F=64)
     base.update(shape)
-    wl = W.Workload("brim_edge", 11, d=64, F=64, n_c=4, **base)
+    wl = W.Workload("brim_edge", 11, d=64, n_c=4, **base)
     check_brim(wl, synth.contiguous_placement(wl))
 
 
