@@ -160,6 +160,62 @@ def summarize_traffic(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd:
     return "\n".join(lines) + "\n"
 
 
+def agent_info(out_dir: str) -> dict:
+    """The GPU agent's row of a rocprofv3 run (SIMD, CU and XCC counts)."""
+    for p in find(out_dir, "agent_info.csv"):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r.get("Agent_Type") == "GPU":
+                    return r
+    return {}
+
+
+def summarize_counters(out_dirs: list[str], commands: list[str], title: str,
+                       kernels: list[str] | None = None) -> str:
+    """Markdown table of per-dispatch counter means for the GEMM kernels and
+    the rates derived from them: the clock (GRBM_GUI_ACTIVE per XCC over the
+    dispatch's duration), the share of SIMD cycles the matrix pipes were
+    busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCC times the
+    SIMDs), LDS bank conflicts per LDS access cycle and the share of wave
+    cycles spent waiting on counters (s_waitcnt)."""
+    info = agent_info(out_dirs[0])
+    simds, xcc = int(info.get("Simd_Count", 1024)), int(info.get("Num_Xcc", 8))
+    vals: dict[str, dict[str, list[float]]] = {}
+    dur: dict[str, dict[tuple, int]] = {}
+    for i, d in enumerate(out_dirs):
+        for r in counter_rows(d):
+            k = short_name(r["Kernel_Name"])
+            if kernels and k not in kernels:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, {})[(i, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) -
+                                                            int(r["Start_Timestamp"]))
+    mean = lambda v: sum(v) / len(v) if v else None
+    lines = [f"# {title}", "", "Commands (run from the repository root on one MI355X):", "", "```"]
+    lines += commands + ["```", "",
+                         f"GPU: {simds} SIMDs in {xcc} XCCs. Counters are per dispatch, averaged; the "
+                         "dispatches of a counter run are serialized and slower than in a timed run.", "",
+                         "| kernel | dispatches per run | avg us | clock GHz | matrix pipes busy % | "
+                         "LDS bank conflicts per access % | wave cycles waiting % |",
+                         "|---|---|---|---|---|---|---|"]
+    order = sorted(vals, key=lambda k: -sum(dur[k].values()))
+    for k in order:
+        c = {n: mean(v) for n, v in vals[k].items()}
+        us = mean(list(dur[k].values())) / 1e3
+        gui = c.get("GRBM_GUI_ACTIVE")
+        clk = gui / xcc / (us * 1e3) if gui else None
+        busy = (100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / xcc * simds)
+                if gui and c.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None else None)
+        bank = (100 * c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+                if c.get("SQ_LDS_IDX_ACTIVE") else None)
+        wait = (100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+                if c.get("SQ_WAVE_CYCLES") else None)
+        f = lambda x, fmt: "—" if x is None else fmt.format(x)
+        lines.append(f"| {k} | {len(dur[k]) // len(out_dirs)} | {us:.1f} | {f(clk, '{:.2f}')} | {f(busy, '{:.1f}')} | "
+                     f"{f(bank, '{:.2f}')} | {f(wait, '{:.1f}')} |")
+    return "\n".join(lines) + "\n"
+
+
 def _main(argv=None):
     import argparse
 
@@ -179,8 +235,17 @@ def _main(argv=None):
     t.add_argument("--copy-bytes", type=int, default=1 << 30)
     t.add_argument("--title", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--kernels", default="")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        text = summarize_counters(a.dirs, a.command, a.title,
+                                  [k for k in a.kernels.split(",") if k] or None)
+    elif a.cmd == "stats":
         text = summarize_stats(a.dir, a.command, a.title)
     else:
         sources = {"k_gemm_up": "gemm_bf16.hip", "k_gemm_down": "gemm_bf16.hip",
