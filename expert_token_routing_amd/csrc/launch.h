@@ -178,7 +178,8 @@ hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream
 // seg_off NULL, n_groups blocks of `rows` rows, e = block):
 //   C_e[m, n] = sum over the group's rows pos of A[a_rows[pos]][a_col + m] *
 //               B[b_rows[pos]][b_col + n],   a_col = a_col0 + group * a_col_grp
-// both operands K-major (rows lda / ldb elements apart).  Rows m < msplit go
+// both operands K-major (rows lda / ldb elements apart); at most one of
+// a_rows, b_rows is given (hipErrorInvalidValue otherwise).  Rows m < msplit go
 // to C1[e] (msplit x N), the rest to C2[e].  M, N >= 256; tail rows of a
 // group read zero_row (at least 256 zero elements).
 // Dense launches (seg_off NULL) may split K (the rows) into k_parts chunks

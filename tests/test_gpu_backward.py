@@ -147,6 +147,19 @@ def test_backward_row_tile_split_edges(flags):
     check(got, ref, ROUTED)
 
 
+def test_backward_long_expert_segments():
+    """Experts of 8191-8193 and 16385 rows: the weight-gradient GEMMs keep
+    a gathered operand's row indices in LDS windows of 8192 rows, so these
+    segments fill one window exactly, leave one row for a second window, or
+    span three; deterministic merge."""
+    counts = [8191, 8192, 8193, 16385, 12000, 3]
+    wl = shape("bwd_long_segments", T=sum(counts) // 2, d=256, F=256, Ne=6, k=2, Nd=2, index=19)
+    inp = synth.make_all(wl)
+    inp["logits"] = routed_to_counts(counts, wl.k, seed=19)
+    got, ref = run(wl, inp=inp, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    check(got, ref, ROUTED)
+
+
 def test_backward_with_shared_experts():
     wl = shape("bwd_shared", T=500, d=256, F=256, n_shared=2, F_shared=320, index=14)
     got, ref = run(wl)
