@@ -78,7 +78,7 @@ __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ ids, int 
         c.pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
     }
     __syncthreads();
-    if (threadIdx.x < nt) {
+    if (static_cast<int>(threadIdx.x) < nt) {
         const int tok = threadIdx.x;
         uint64_t em[4] = {0, 0, 0, 0}, gm = 0;
         for (int j = 0; j < k; j++) {

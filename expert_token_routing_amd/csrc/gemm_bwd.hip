@@ -84,7 +84,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 // ---- K-major operand tiles: rows of 256 columns for one k each
 __device__ __forceinline__ int kkey(int k) { return ((k & 7) ^ ((k >> 1) & 4)) << 1; }
-__device__ __forceinline__ int kmaj(int k, int col) {
+[[maybe_unused]] __device__ __forceinline__ int kmaj(int k, int col) {
     return k * BM + ((((col >> 3) ^ kkey(k))) << 3) + (col & 7);
 }
 

@@ -65,8 +65,8 @@ __device__ void select_topk(const TokenLogits<NI> &l, int Ne, int k, uint64_t al
 #pragma unroll
     for (int i = 0; i < NI; i++) {
         const uint64_t eq = __ballot(key[i] == thr);
-        take[i] = key[i] > thr || (key[i] == thr && __popcll(eq & below) < need);
-        need -= min(need, __popcll(eq));
+        take[i] = key[i] > thr || (key[i] == thr && static_cast<int>(__popcll(eq & below)) < need);
+        need -= min(need, static_cast<int>(__popcll(eq)));
     }
     // place in the list: selected experts with a larger key, or an equal key
     // and a lower index
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
     if (prune_rule != 0 && G < Nd) {
         uint64_t span = 0;
         for (int j = 0; j < k; j++) span |= 1ull << s_grp[sel[j]];
-        if (__popcll(span) > G) {
+        if (static_cast<int>(__popcll(span)) > G) {
             uint64_t chosen = 0;
             if (prune_rule == 1 || prune_rule == 3) {
                 // TRAVERSE (and similarity-based pruning): groups of the top-k
