@@ -2,7 +2,9 @@
 // collaboration pruning (section 3.3), routing-score-based or
 // expert-similarity-based.
 //
-// One 64-lane wave per token; lane l holds the logits of experts l, l+64, ...
+// Without pruning and with at most 64 experts, k_route_rows takes one
+// 16-lane row per token (below).  Otherwise one 64-lane wave per token;
+// lane l holds the logits of experts l, l+64, ...
 // Softmax max and denominator are wave reductions.  The top k are selected
 // without cross-lane shuffles: each logit maps to an unsigned key that keeps
 // its order, the k-th largest key is found bit by bit from wave ballots
@@ -141,6 +143,112 @@ __device__ void replace_similar(const int32_t *__restrict__ sim_rank, int Ne, in
     }
 }
 
+// The plain top k (no pruning) for Ne <= 64 experts: one DPP
+// row of 16 lanes per token, four tokens per wave; lane r holds the logits
+// of experts r, r + 16, r + 32, r + 48.  Row maxima and sums are four
+// row-shift steps, after which lane 15 of the row holds the result, and a
+// row broadcast spreads it over the row.  The top k are k rounds of a row
+// maximum of the logits' order-keeping keys followed by a row minimum of
+// the expert indices that hold it, so ties go to the lower index as in the
+// wave kernel; round i's winner is recorded by lane i (lane i - 16 for
+// i >= 16) and cleared by its owner.  The softmax denominator
+// takes 6 addition levels, as in the wave kernel (two inside the lane,
+// four across the row): the same error bound, possibly another rounding.
+constexpr int kRouteRowThreads = 256;  // 16 tokens per workgroup
+
+// Lane 15 of each row of 16 lanes, copied to the whole row (the
+// row_newbcast DPP control of gfx90a and later).
+constexpr int kDppRowNewBcast15 = 0x15F;
+__device__ __forceinline__ int row_bcast15(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kDppRowNewBcast15, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float row_bcast15(float v) { return __int_as_float(row_bcast15(__float_as_int(v))); }
+
+template <int N>  // N = ceil(k / 16) rounds per recording lane (1)
+__global__ __launch_bounds__(kRouteRowThreads) void k_route_rows(const float *__restrict__ logits,
+                                                                 int T, int Ne, int k,
+                                                                 int32_t *__restrict__ ids,
+                                                                 float *__restrict__ w) {
+    const int lane = lane_id(), r = lane & 15;
+    const int t = (blockIdx.x * kRouteRowThreads + static_cast<int>(threadIdx.x)) >> 4;
+    const bool live = t < T;  // a row past T computes on -inf and stores nothing
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int e = r + 16 * j;
+        v[j] = live && e < Ne ? logits[static_cast<size_t>(t) * Ne + e] : -INFINITY;
+    }
+    // row maximum
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    m = fmaxf(m, dpp_f<kDppRowShr1, 0xf>(-INFINITY, m));
+    m = fmaxf(m, dpp_f<kDppRowShr2, 0xf>(-INFINITY, m));
+    m = fmaxf(m, dpp_f<kDppRowShr4, 0xf>(-INFINITY, m));
+    m = fmaxf(m, dpp_f<kDppRowShr8, 0xf>(-INFINITY, m));
+    m = row_bcast15(m);
+    // denominator: two levels in the lane, four across the row
+    float ex[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) ex[j] = r + 16 * j < Ne ? expf(v[j] - m) : 0.f;
+    float s = (ex[0] + ex[1]) + (ex[2] + ex[3]);
+    s += dpp_f<kDppRowShr1, 0xf>(0.f, s);
+    s += dpp_f<kDppRowShr2, 0xf>(0.f, s);
+    s += dpp_f<kDppRowShr4, 0xf>(0.f, s);
+    s += dpp_f<kDppRowShr8, 0xf>(0.f, s);
+    s = row_bcast15(s);
+    uint32_t key[4];  // 0: not an expert, or already chosen
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float x = v[j] == v[j] ? v[j] : -INFINITY;  // NaN ranks as -inf
+        key[j] = r + 16 * j < Ne ? logit_key(x) : 0u;
+    }
+    uint32_t mine_key[N];
+    int mine_e[N];
+#pragma unroll
+    for (int q = 0; q < N; q++) {
+        mine_key[q] = 0;
+        mine_e[q] = 0;
+    }
+    for (int i = 0; i < k; i++) {
+        // the row's largest key ...
+        uint32_t b = max(max(key[0], key[1]), max(key[2], key[3]));
+        b = max(b, static_cast<uint32_t>(dpp_i<kDppRowShr1, 0xf>(0, static_cast<int>(b))));
+        b = max(b, static_cast<uint32_t>(dpp_i<kDppRowShr2, 0xf>(0, static_cast<int>(b))));
+        b = max(b, static_cast<uint32_t>(dpp_i<kDppRowShr4, 0xf>(0, static_cast<int>(b))));
+        b = max(b, static_cast<uint32_t>(dpp_i<kDppRowShr8, 0xf>(0, static_cast<int>(b))));
+        b = static_cast<uint32_t>(row_bcast15(static_cast<int>(b)));
+        // ... and the lowest expert that holds it, as the largest 255 - e
+        // (e < 64, so 0 marks a lane without one)
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 3; j >= 0; j--) c = key[j] == b ? 255u - (r + 16 * j) : c;
+        c = max(c, static_cast<uint32_t>(dpp_i<kDppRowShr1, 0xf>(0, static_cast<int>(c))));
+        c = max(c, static_cast<uint32_t>(dpp_i<kDppRowShr2, 0xf>(0, static_cast<int>(c))));
+        c = max(c, static_cast<uint32_t>(dpp_i<kDppRowShr4, 0xf>(0, static_cast<int>(c))));
+        c = max(c, static_cast<uint32_t>(dpp_i<kDppRowShr8, 0xf>(0, static_cast<int>(c))));
+        const int e = 255 - row_bcast15(static_cast<int>(c));
+#pragma unroll
+        for (int j = 0; j < 4; j++) key[j] = r + 16 * j == e ? 0u : key[j];
+#pragma unroll
+        for (int q = 0; q < N; q++)
+            if (i == r + 16 * q) {
+                mine_key[q] = b;
+                mine_e[q] = e;
+            }
+    }
+#pragma unroll
+    for (int q = 0; q < N; q++) {
+        const int slot = r + 16 * q;
+        if (live && slot < k) {
+            // the logit back from its key (exact; -0 reads as +0, NaN as -inf)
+            const uint32_t kb = mine_key[q];
+            const float l = __uint_as_float((kb & 0x80000000u) ? (kb & 0x7fffffffu) : ~kb);
+            const size_t o = static_cast<size_t>(t) * k + slot;
+            ids[o] = mine_e[q];
+            w[o] = expf(l - m) / s;
+        }
+    }
+}
+
 // Caller-supplied routing made safe for the BRIM kernels: a token's id that
 // is out of range or repeats an earlier one is replaced by the lowest expert
 // not yet in the token's list, with weight 0.  Valid tokens are copied
@@ -266,6 +374,12 @@ __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(const float *__res
 hipError_t launch_route(const float *logits, int T, int Ne, int k, int prune_rule, int G,
                         const PlaceTab &tab, const int32_t *sim_rank, int32_t *ids, float *w,
                         hipStream_t s) {
+    if (prune_rule == 0 && Ne <= kWave) {
+        const dim3 g(ceil_div(static_cast<size_t>(T) * 16, kRouteRowThreads)), b(kRouteRowThreads);
+        if (k <= 16) k_route_rows<1><<<g, b, 0, s>>>(logits, T, Ne, k, ids, w);
+        else k_route_rows<2><<<g, b, 0, s>>>(logits, T, Ne, k, ids, w);
+        return hipGetLastError();
+    }
     const dim3 grid(ceil_div(T, kRouteWaves)), block(kRouteWaves * kWave);
     const int ni = (Ne + kWave - 1) / kWave;
     switch (ni) {

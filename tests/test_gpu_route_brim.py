@@ -77,6 +77,27 @@ def test_route_signed_zeros_and_infinities():
         assert np.array_equal(ids, ids_o), Ne
 
 
+@pytest.mark.parametrize("Ne,k,rule", [(64, 8, W.PRUNE_OFF), (60, 4, W.PRUNE_OFF),
+                                       (64, 8, W.PRUNE_GROUPSUM), (200, 6, W.PRUNE_OFF)])
+def test_route_nan_logits_rank_last(Ne, k, rule):
+    """A NaN logit ranks as -inf: the ids are those of the logits with every
+    NaN replaced by -inf (ties to the lower index), so they stay distinct and
+    in range; the weights are unspecified then."""
+    wl = W.Workload(f"nan_{Ne}", 9, T=1031, d=64, Ne=Ne, k=k, Nd=4, F=64,
+                    prune_rule=rule, prune_groups=2 if rule else 0)
+    rng = np.random.default_rng(Ne + k)
+    lg = rng.standard_normal((1031, Ne)).astype(np.float32)
+    lg[rng.random((1031, Ne)) < 0.2] = np.nan
+    lg[:7] = np.nan                        # rows of NaN only
+    lg[7:11, : Ne // 2] = -np.inf          # -inf beside NaN
+    lg[7:11, Ne // 2:] = np.nan
+    L = synth.contiguous_placement(wl)
+    ids, _ = gpu_route(wl, torch.from_numpy(lg), L)
+    ids_o, _ = oracle.route(np.where(np.isnan(lg), -np.inf, lg).astype(np.float32), k, L, rule,
+                            wl.prune_groups)
+    assert np.array_equal(ids, ids_o)
+
+
 def test_route_ties_and_wide_expert_counts():
     # integer-valued logits: many exact ties, broken toward the lower index
     for Ne, k, Nd in [(8, 2, 2), (64, 8, 8), (256, 8, 16), (130, 5, 10), (32, 32, 4)]:
