@@ -54,21 +54,23 @@ __device__ __forceinline__ bool has_pos(const uint64_t *em, int p) {
     return (em[p >> 6] >> (p & 63)) & 1ull;
 }
 
-// Shared state of one chunk: its ids (s_id[token * k + j]), placement
-// tables, and per token the 256-bit mask of its placement positions and
-// the mask of its groups.
+// Shared state of a chunk of at most NTOK tokens: its ids (id[token * k +
+// j]), placement tables, and per token the 256-bit mask of its placement
+// positions and the mask of its groups.
+template <int NTOK>
 struct ChunkIds {
-    uint8_t id[kBrimChunk * kMaxK];
-    uint64_t em[kBrimChunk][4];
-    uint64_t gm[kBrimChunk];
+    uint8_t id[NTOK * kMaxK];
+    uint64_t em[NTOK][4];
+    uint64_t gm[NTOK];
     uint8_t grp[kMaxNe];
     int16_t pos[kMaxNe];
 };
 
 // Coalesced load of the chunk's ids and the placement tables; then, one
 // thread per token, the position and group masks.  Ends with a barrier.
+template <int NTOK>
 __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ ids, int t0, int nt, int k,
-                                           const PlaceTab &tab, ChunkIds &c) {
+                                           const PlaceTab &tab, ChunkIds<NTOK> &c) {
     const int n = tab.n;
     const size_t base = static_cast<size_t>(t0) * k;
     for (int i = threadIdx.x; i < nt * k; i += blockDim.x)
@@ -78,8 +80,7 @@ __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ ids, int 
         c.pos[e] = static_cast<int16_t>(tab.grp[e] * n + tab.slot[e]);
     }
     __syncthreads();
-    if (static_cast<int>(threadIdx.x) < nt) {
-        const int tok = threadIdx.x;
+    for (int tok = threadIdx.x; tok < nt; tok += blockDim.x) {
         uint64_t em[4] = {0, 0, 0, 0}, gm = 0;
         for (int j = 0; j < k; j++) {
             const int e = c.id[tok * k + j];
@@ -96,19 +97,16 @@ __device__ __forceinline__ void load_chunk(const int32_t *__restrict__ ids, int 
 
 // Entry (tok, j) with placement position q is its token's first contributor
 // to its group's SFD row when no lower position of that group is set.
-__device__ __forceinline__ bool first_contrib(const ChunkIds &c, int tok, int q, int n) {
+template <int NTOK>
+__device__ __forceinline__ bool first_contrib(const ChunkIds<NTOK> &c, int tok, int q, int n) {
     return !any_in(c.em[tok], (q / n) * n, q);
 }
 
-__global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__restrict__ ids,
-                                                             int T, int k, PlaceTab tab,
-                                                             int32_t *__restrict__ chunk_cnt) {
-    __shared__ int cnt[kMaxBins];
-    __shared__ ChunkIds c;
-    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
-    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
-    for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
-    load_chunk(ids, t0, nt, k, tab, c);
+// Adds the chunk's tokens to the bin counts cnt (LDS, zeroed; no barrier).
+template <int NTOK>
+__device__ __forceinline__ void count_bins(const ChunkIds<NTOK> &c, int nt, int k,
+                                           const PlaceTab &tab, int *cnt) {
+    const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n;
     for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
         const int tok = i / k, q = c.pos[c.id[i]];
         atomicAdd(&cnt[Nd + q], 1);
@@ -118,9 +116,75 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__re
         const int g = i / nt, tok = i - g * nt;
         if ((c.gm[tok] >> g) & 1ull) atomicAdd(&cnt[g], 1);
     }
+}
+
+__global__ __launch_bounds__(kBrimThreads) void k_brim_count(const int32_t *__restrict__ ids,
+                                                             int T, int k, PlaceTab tab,
+                                                             int32_t *__restrict__ chunk_cnt) {
+    __shared__ int cnt[kMaxBins];
+    __shared__ ChunkIds<kBrimChunk> c;
+    const int NB = tab.Nd + 2 * tab.Ne;
+    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
+    load_chunk(ids, t0, nt, k, tab, c);
+    count_bins(c, nt, k, tab, cnt);
     __syncthreads();
     for (int b = threadIdx.x; b < NB; b += blockDim.x)
         chunk_cnt[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = cnt[b];
+}
+
+// Across bins, from the bins' totals (run by one wave): groups give
+// sfd_off; experts (placement order) give epd_off; first-contributor bins
+// start at their expert's first EPD row (binoff: each bin's first row).
+// ceil(rows / tile_rows) gives the GEMM row-tile schedules: all rows
+// (up-projection, raised by fill_rounds when fill_cols > 0), first
+// contributors and the rest (merge).  s_vt: LDS scratch of Ne entries.
+__device__ void bin_offsets(const int *total, int Nd, int Ne, int tile_rows, int fill_cols,
+                            int slots, int *s_vt, int *binoff, int32_t *__restrict__ sfd_off,
+                            int32_t *__restrict__ epd_off, int32_t *__restrict__ tile_off,
+                            int32_t *__restrict__ first_cnt, int32_t *__restrict__ tile_off_first,
+                            int32_t *__restrict__ tile_off_rest) {
+    const int lane = lane_id();
+    const int vg = lane < Nd ? total[lane] : 0;
+    const int ig = wave_incl_scan(vg);
+    if (lane < Nd) {
+        binoff[lane] = ig - vg;
+        sfd_off[lane] = ig - vg;
+    }
+    if (lane == kWave - 1) sfd_off[Nd] = ig;
+    // row tiles per expert: ceil(rows / tile_rows), raised by fill_rounds
+    for (int p = lane; p < Ne; p += kWave) s_vt[p] = (total[Nd + p] + tile_rows - 1) / tile_rows;
+    if (fill_cols > 0) fill_rounds(total + Nd, s_vt, Ne, fill_cols, slots, kBrimMaxFill);
+    int run = 0, run_t = 0, run_f = 0, run_r = 0;
+    for (int p0 = 0; p0 < Ne; p0 += kWave) {
+        const int p = p0 + lane;
+        const int v = p < Ne ? total[Nd + p] : 0;
+        const int f = p < Ne ? total[Nd + Ne + p] : 0;
+        const int vt = p < Ne ? s_vt[p] : 0;
+        const int vf = (f + tile_rows - 1) / tile_rows;
+        const int vr = (v - f + tile_rows - 1) / tile_rows;
+        const int inc = wave_incl_scan(v), inc_t = wave_incl_scan(vt);
+        const int inc_f = wave_incl_scan(vf), inc_r = wave_incl_scan(vr);
+        if (p < Ne) {
+            binoff[Nd + p] = run + inc - v;
+            binoff[Nd + Ne + p] = run + inc - v;
+            epd_off[p] = run + inc - v;
+            tile_off[p] = run_t + inc_t - vt;
+            tile_off_first[p] = run_f + inc_f - vf;
+            tile_off_rest[p] = run_r + inc_r - vr;
+            first_cnt[p] = f;
+        }
+        run += __shfl(inc, kWave - 1);
+        run_t += __shfl(inc_t, kWave - 1);
+        run_f += __shfl(inc_f, kWave - 1);
+        run_r += __shfl(inc_r, kWave - 1);
+    }
+    if (lane == 0) {
+        epd_off[Ne] = run;
+        tile_off[Ne] = run_t;
+        tile_off_first[Ne] = run_f;
+        tile_off_rest[Ne] = run_r;
+    }
 }
 
 __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ chunk_cnt,
@@ -222,52 +286,10 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     }
     __syncthreads();
 
-    // 2. across bins: groups give sfd_off; experts (placement order) give
-    //    epd_off; first-contributor bins start at their expert's first EPD
-    //    row.  ceil(rows / tile_rows) gives the GEMM row-tile schedules: all
-    //    rows (up-projection), first contributors and the rest (merge).
-    if (wv == 0) {
-        const int vg = lane < Nd ? total[lane] : 0;
-        const int ig = wave_incl_scan(vg);
-        if (lane < Nd) {
-            binoff[lane] = ig - vg;
-            sfd_off[lane] = ig - vg;
-        }
-        if (lane == kWave - 1) sfd_off[Nd] = ig;
-        // row tiles per expert: ceil(rows / tile_rows), raised by fill_rounds
-        for (int p = lane; p < Ne; p += kWave) s_vt[p] = (total[Nd + p] + tile_rows - 1) / tile_rows;
-        if (fill_cols > 0) fill_rounds(total + Nd, s_vt, Ne, fill_cols, slots, kBrimMaxFill);
-        int run = 0, run_t = 0, run_f = 0, run_r = 0;
-        for (int p0 = 0; p0 < Ne; p0 += kWave) {
-            const int p = p0 + lane;
-            const int v = p < Ne ? total[Nd + p] : 0;
-            const int f = p < Ne ? total[Nd + Ne + p] : 0;
-            const int vt = p < Ne ? s_vt[p] : 0;
-            const int vf = (f + tile_rows - 1) / tile_rows;
-            const int vr = (v - f + tile_rows - 1) / tile_rows;
-            const int inc = wave_incl_scan(v), inc_t = wave_incl_scan(vt);
-            const int inc_f = wave_incl_scan(vf), inc_r = wave_incl_scan(vr);
-            if (p < Ne) {
-                binoff[Nd + p] = run + inc - v;
-                binoff[Nd + Ne + p] = run + inc - v;
-                epd_off[p] = run + inc - v;
-                tile_off[p] = run_t + inc_t - vt;
-                tile_off_first[p] = run_f + inc_f - vf;
-                tile_off_rest[p] = run_r + inc_r - vr;
-                first_cnt[p] = f;
-            }
-            run += __shfl(inc, kWave - 1);
-            run_t += __shfl(inc_t, kWave - 1);
-            run_f += __shfl(inc_f, kWave - 1);
-            run_r += __shfl(inc_r, kWave - 1);
-        }
-        if (lane == 0) {
-            epd_off[Ne] = run;
-            tile_off[Ne] = run_t;
-            tile_off_first[Ne] = run_f;
-            tile_off_rest[Ne] = run_r;
-        }
-    }
+    // 2. across bins (wave 0)
+    if (wv == 0)
+        bin_offsets(total, Nd, Ne, tile_rows, fill_cols, slots, s_vt, binoff, sfd_off, epd_off,
+                    tile_off, first_cnt, tile_off_first, tile_off_rest);
     __syncthreads();
 
     // 3. each (bin, chunk) start = start of the bin + rows of earlier chunks
@@ -299,30 +321,21 @@ __global__ __launch_bounds__(1024) void k_brim_scan(const int32_t *__restrict__ 
     }
 }
 
-__global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
-    const int32_t *__restrict__ ids, const float *__restrict__ w, int T, int k, PlaceTab tab,
-    const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ sfd_off,
-    const int32_t *__restrict__ epd_off, const int32_t *__restrict__ first_cnt, int dense,
+// Chunk [t0, t0 + nt) of the batch (NBLK 64-token blocks at most), ids and
+// masks in c: its bin rows, s_base[b] being the first row of bin b that the
+// chunk fills; s_epd / s_first / s_sfd: epd_off, first_cnt, sfd_off in LDS;
+// bmask zeroed, everything visible to the workgroup.  Writes BRIM_0, the
+// condensed BRIM_1 (epd_src, epd_w, tok_epd), the merge order and, when
+// dense, BRIM_1 as matrices.
+template <int NBLK, int NTOK>
+__device__ __forceinline__ void fill_chunk(
+    const float *__restrict__ w, int T, int k, const PlaceTab &tab, int t0, int nt,
+    const ChunkIds<NTOK> &c, unsigned long long (*bmask)[kMaxBins], int (*bpre)[kMaxBins],
+    const int *s_base, const int *s_epd, const int *s_first, const int *s_sfd, int dense,
     int32_t *__restrict__ brim0, int32_t *__restrict__ epd_src, float *__restrict__ epd_w,
-    int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows,
-    int32_t *__restrict__ brim1) {
-    // bit (tok mod 64) of bmask[tok / 64][b]: token tok is in bin b
-    __shared__ unsigned long long bmask[kBlocksPerChunk][kMaxBins];
-    __shared__ int bpre[kBlocksPerChunk][kMaxBins];
-    __shared__ int s_base[kMaxBins];
-    __shared__ int s_epd[kMaxNe + 1], s_first[kMaxNe], s_sfd[kMaxNd + 1];
-    __shared__ ChunkIds c;
+    int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows, int32_t *__restrict__ brim1) {
     const int Nd = tab.Nd, Ne = tab.Ne, n = tab.n, NB = Nd + 2 * Ne;
-    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
-    for (int i = threadIdx.x; i < kBlocksPerChunk * NB; i += blockDim.x)
-        bmask[i / NB][i % NB] = 0ull;
-    for (int b = threadIdx.x; b < NB; b += blockDim.x)
-        s_base[b] = chunk_base[static_cast<size_t>(b) * gridDim.x + blockIdx.x];
-    for (int e = threadIdx.x; e < Ne; e += blockDim.x) s_first[e] = first_cnt[e];
-    for (int e = threadIdx.x; e <= Ne; e += blockDim.x) s_epd[e] = epd_off[e];
-    for (int g = threadIdx.x; g <= Nd; g += blockDim.x) s_sfd[g] = sfd_off[g];
-    load_chunk(ids, t0, nt, k, tab, c);
-
+    const int nblk = (nt + kWave - 1) / kWave;
     // bin membership bits (LDS atomic OR, so the result does not depend on timing)
     for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
         const int tok = i / k, q = c.pos[c.id[i]];
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
     __syncthreads();
     for (int b = threadIdx.x; b < NB; b += blockDim.x) {
         int run = s_base[b];
-        for (int q = 0; q < kBlocksPerChunk; q++) {
+        for (int q = 0; q < nblk; q++) {
             bpre[q][b] = run;
             run += __popcll(bmask[q][b]);
         }
@@ -390,11 +403,92 @@ __global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
     }
 }
 
+__global__ __launch_bounds__(kBrimThreads) void k_brim_fill(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int T, int k, PlaceTab tab,
+    const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ sfd_off,
+    const int32_t *__restrict__ epd_off, const int32_t *__restrict__ first_cnt, int dense,
+    int32_t *__restrict__ brim0, int32_t *__restrict__ epd_src, float *__restrict__ epd_w,
+    int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows,
+    int32_t *__restrict__ brim1) {
+    // bit (tok mod 64) of bmask[tok / 64][b]: token tok is in bin b
+    __shared__ unsigned long long bmask[kBlocksPerChunk][kMaxBins];
+    __shared__ int bpre[kBlocksPerChunk][kMaxBins];
+    __shared__ int s_base[kMaxBins];
+    __shared__ int s_epd[kMaxNe + 1], s_first[kMaxNe], s_sfd[kMaxNd + 1];
+    __shared__ ChunkIds<kBrimChunk> c;
+    const int Nd = tab.Nd, Ne = tab.Ne, NB = Nd + 2 * Ne;
+    const int t0 = blockIdx.x * kBrimChunk, nt = min(kBrimChunk, T - t0);
+    for (int i = threadIdx.x; i < kBlocksPerChunk * NB; i += blockDim.x)
+        bmask[i / NB][i % NB] = 0ull;
+    for (int b = threadIdx.x; b < NB; b += blockDim.x)
+        s_base[b] = chunk_base[static_cast<size_t>(b) * gridDim.x + blockIdx.x];
+    for (int e = threadIdx.x; e < Ne; e += blockDim.x) s_first[e] = first_cnt[e];
+    for (int e = threadIdx.x; e <= Ne; e += blockDim.x) s_epd[e] = epd_off[e];
+    for (int g = threadIdx.x; g <= Nd; g += blockDim.x) s_sfd[g] = sfd_off[g];
+    load_chunk(ids, t0, nt, k, tab, c);
+    fill_chunk<kBlocksPerChunk>(w, T, k, tab, t0, nt, c, bmask, bpre, s_base, s_epd, s_first, s_sfd,
+                                dense, brim0, epd_src, epd_w, tok_epd, down_rows, brim1);
+}
+
+// A small batch (at most kBrimSmallT tokens and kBrimSmallEntries routing
+// entries) in one workgroup: the counts, the offsets and schedules across
+// bins and the fill of k_brim_count, k_brim_scan and k_brim_fill, with the
+// whole batch as one chunk, in one launch (the three launches' fixed
+// latencies dominate such batches: 15.5 -> 9.8 us at 256 tokens of top-2;
+// at 512 tokens of top-8 one workgroup was 10% slower than the three
+// kernels).  Same results, entry by entry.
+constexpr int kSmallBlocks = kBrimSmallT / kWave;
+
+__global__ __launch_bounds__(kBrimThreads) void k_brim_small(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int T, int k, PlaceTab tab,
+    int tile_rows, int fill_cols, int slots, int dense, int32_t *__restrict__ sfd_off,
+    int32_t *__restrict__ epd_off, int32_t *__restrict__ tile_off, int32_t *__restrict__ first_cnt,
+    int32_t *__restrict__ tile_off_first, int32_t *__restrict__ tile_off_rest,
+    int32_t *__restrict__ brim0, int32_t *__restrict__ epd_src, float *__restrict__ epd_w,
+    int32_t *__restrict__ tok_epd, int32_t *__restrict__ down_rows,
+    int32_t *__restrict__ brim1) {
+    __shared__ unsigned long long bmask[kSmallBlocks][kMaxBins];
+    __shared__ int bpre[kSmallBlocks][kMaxBins];
+    __shared__ int cnt[kMaxBins], binoff[kMaxBins], s_vt[kMaxNe];
+    __shared__ int s_epd[kMaxNe + 1], s_first[kMaxNe], s_sfd[kMaxNd + 1];
+    __shared__ ChunkIds<kBrimSmallT> c;
+    const int Nd = tab.Nd, Ne = tab.Ne, NB = Nd + 2 * Ne;
+    for (int i = threadIdx.x; i < kSmallBlocks * NB; i += blockDim.x)
+        bmask[i / NB][i % NB] = 0ull;
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) cnt[b] = 0;
+    load_chunk(ids, 0, T, k, tab, c);
+    count_bins(c, T, k, tab, cnt);
+    __syncthreads();
+    if (threadIdx.x < kWave)
+        bin_offsets(cnt, Nd, Ne, tile_rows, fill_cols, slots, s_vt, binoff, sfd_off, epd_off,
+                    tile_off, first_cnt, tile_off_first, tile_off_rest);
+    __syncthreads();
+    // the fill's LDS copies of the offsets, from the bins' totals and starts
+    for (int e = threadIdx.x; e < Ne; e += blockDim.x) {
+        s_first[e] = cnt[Nd + Ne + e];
+        s_epd[e] = binoff[Nd + e];
+    }
+    if (threadIdx.x == 0) s_epd[Ne] = binoff[Nd + Ne - 1] + cnt[Nd + Ne - 1];
+    for (int g = threadIdx.x; g < Nd; g += blockDim.x) s_sfd[g] = binoff[g];
+    if (threadIdx.x == 0) s_sfd[Nd] = binoff[Nd - 1] + cnt[Nd - 1];
+    __syncthreads();
+    fill_chunk<kSmallBlocks>(w, T, k, tab, 0, T, c, bmask, bpre, binoff, s_epd, s_first, s_sfd,
+                             dense, brim0, epd_src, epd_w, tok_epd, down_rows, brim1);
+}
+
 }  // namespace
 
 hipError_t launch_brim(const int32_t *ids, const float *w, int T, int k, const PlaceTab &tab,
                        int tile_rows, int fill_cols, int dense_brim1, const BrimBufs &b,
                        hipStream_t s) {
+    if (T <= kBrimSmallT && T * k <= kBrimSmallEntries) {
+        k_brim_small<<<1, kBrimThreads, 0, s>>>(ids, w, T, k, tab, tile_rows, fill_cols,
+                                                compute_units(), dense_brim1, b.sfd_off,
+                                                b.epd_off, b.tile_off, b.first_cnt,
+                                                b.tile_off_first, b.tile_off_rest, b.brim0,
+                                                b.epd_src, b.epd_w, b.tok_epd, b.down_rows, b.brim1);
+        return hipGetLastError();
+    }
     const int nchunks = static_cast<int>(ceil_div(T, kBrimChunk));
     k_brim_count<<<nchunks, kBrimThreads, 0, s>>>(ids, T, k, tab, b.chunk_cnt);
     k_brim_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, tab.Nd, tab.Ne, tile_rows, fill_cols,

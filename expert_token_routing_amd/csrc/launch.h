@@ -34,6 +34,10 @@ hipError_t launch_sim_rank(const double *gram, int Ne, double *t2, int32_t *rank
 
 // --- BRIM (brim.hip) ---
 constexpr int kBrimChunk = 128;  // tokens per BRIM workgroup
+// Batches of at most kBrimSmallT tokens and kBrimSmallEntries routing
+// entries build the BRIM in one workgroup (more entries are faster over
+// the three kernels' several workgroups).
+constexpr int kBrimSmallT = 512, kBrimSmallEntries = 1024;
 struct BrimBufs {
     int32_t *brim0, *sfd_off, *epd_off, *tile_off, *epd_src, *tok_epd, *brim1;
     float *epd_w;

@@ -225,6 +225,12 @@ def test_brim_rescheduled_placement():
 
 @pytest.mark.parametrize("shape", [
     dict(T=1), dict(T=5), dict(T=1023), dict(T=1025), dict(T=3000, Nd=1),
+    # batches of up to 512 tokens and 1024 routing entries take the
+    # one-workgroup BRIM: its edges and its largest tables
+    dict(T=128, k=8), dict(T=129, k=8), dict(T=512, k=2), dict(T=513, k=1),
+    dict(T=512, Ne=256, Nd=64, k=32), dict(T=32, Ne=256, Nd=64, k=32),
+    dict(T=64, Ne=256, Nd=1, k=3), dict(T=200, Ne=130, Nd=10, k=5, F=1408),
+    dict(T=500, Ne=8, Nd=2, k=2, F=1408),  # 320-row tiles: the schedule takes extra row tiles
     dict(T=2000, Ne=16, Nd=16, k=4), dict(T=1500, k=1), dict(T=999, Ne=256, Nd=64, k=8),
     dict(T=1100, Ne=60, Nd=4, k=4),
     # schedules that take extra row tiles, with several experts per lane
