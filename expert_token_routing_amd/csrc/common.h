@@ -118,6 +118,26 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
 
 inline unsigned ceil_div(size_t a, size_t b) { return static_cast<unsigned>((a + b - 1) / b); }
 
+// Placement position owning row tile tm of a grouped GEMM: the last p < Ne
+// with tile_off[p] <= tm (tile_off non-decreasing from 0, tm < tile_off[Ne]),
+// i.e. the count of such p minus one.  The lanes read the schedule in one
+// round trip (four entries each at most) and wave ballots count, instead of
+// a binary search's log2(Ne) dependent loads at the start of every tile.
+// Every lane of the wave must call it; all get the same result.
+__device__ __forceinline__ int tile_owner(const int32_t *tile_off, int Ne, int tm) {
+    const int lane = lane_id();
+    int v[kMaxNe / kWave];
+#pragma unroll
+    for (int j = 0; j < kMaxNe / kWave; j++) {
+        const int p = lane + kWave * j;
+        v[j] = p < Ne ? tile_off[p] : 0x7fffffff;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxNe / kWave; j++) cnt += __popcll(__ballot(v[j] <= tm));
+    return cnt - 1;
+}
+
 // Maximum of an unsigned 64-bit value over the wave (both halves moved by
 // the same DPP steps as the scans above; 0 is the identity).
 template <int CTRL, int ROW_MASK>

@@ -166,17 +166,6 @@ __device__ __forceinline__ void band_order(int local, int r, int c, int &lm, int
     lm = rb0 + idx - tn * rb;
 }
 
-// Placement position owning row tile tm: the last p with tile_off[p] <= tm.
-__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
-    int lo = 0, hi = Ne;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_off[mid] <= tm) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
 struct Tile {
     int e;     // expert
     int seg;   // first row of the expert's segment
@@ -209,7 +198,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     if (seg_off) {
         const int m_tiles = tile_off[Ne];
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
-        const int p = find_pos(tile_off, Ne, tm);
+        const int p = tile_owner(tile_off, Ne, tm);
         if (phase != 2) {
             // Bands of row tiles, column tiles outermost inside a band: the
             // workgroups that run together on an XCD then share fewer weight

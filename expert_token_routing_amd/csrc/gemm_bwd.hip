@@ -161,16 +161,6 @@ __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int 
     return true;
 }
 
-__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
-    int lo = 0, hi = Ne;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_off[mid] <= tm) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
 // Issues the direct loads of one K-major operand slice: 64 k-rows of 256
 // columns.  Wave w, load i moves slice rows 2 (8 i + w) and +1, lane l the
 // physical chunk l & 31 of row l >> 5; row[i] points at column 0 of the
@@ -215,7 +205,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     int tm, tn;
     const int m_tiles = a.tile_off[a.Ne], n_tiles = (a.N + BN - 1) / BN;
     if (!map_tile(m_tiles, n_tiles, tm, tn)) return;
-    const int p = find_pos(a.tile_off, a.Ne, tm);
+    const int p = tile_owner(a.tile_off, a.Ne, tm);
     if (a.phase != 2) {
         // bands of kBand row tiles, column tiles outermost inside a band, as
         // in the forward GEMMs

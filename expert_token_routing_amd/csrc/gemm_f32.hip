@@ -6,9 +6,14 @@
 //
 // A 256-thread workgroup computes 64 rows x 64 output columns; thread
 // (ty, tx) owns rows ty + 16*i and columns tx + 16*j (i, j < 4), so the LDS
-// reads of a 16-thread row are consecutive.  K slices of 16 are staged
-// K-major in LDS.  Tile scheduling follows the same per-expert row-tile
-// schedule as the bf16 kernels, with 64-row tiles.
+// reads of a 16-thread row are consecutive.  K slices of 64 are staged
+// K-major in LDS; the next slice's loads go out into registers before the
+// current one is multiplied, so that a tile waits for one load round trip
+// per 64-deep slice (16-deep slices loaded one at a time left the small
+// fp32 layers' GEMMs waiting on a round trip every 16 k).  Every output
+// accumulates its k in ascending order, one fma each.  Tile scheduling
+// follows the same per-expert row-tile schedule as the bf16 kernels, with
+// 64-row tiles.
 #include "launch.h"
 
 namespace occ {
@@ -16,18 +21,10 @@ namespace {
 
 constexpr int BM = kGemmBmF32;  // 64
 constexpr int BN = 64;
-constexpr int BK = 16;
+constexpr int BK = 16;           // k per load step (K is a multiple of 16)
+constexpr int NS = 4;            // load steps per LDS slice
+constexpr int BKS = BK * NS;     // 64-deep LDS slices
 constexpr int PAD = 4;
-
-__device__ __forceinline__ int find_pos(const int32_t *tile_off, int Ne, int tm) {
-    int lo = 0, hi = Ne;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_off[mid] <= tm) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
 
 struct Tile {
     int e, seg, m0, rows, n0;
@@ -43,7 +40,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     const int tm = blockIdx.x / n_tiles, tn = blockIdx.x % n_tiles;
     if (seg_off) {
         if (tm >= tile_off[Ne]) return false;
-        const int p = find_pos(tile_off, Ne, tm);
+        const int p = tile_owner(tile_off, Ne, tm);
         const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
         const int nf = phase == 1 || phase == 2 ? first_cnt[p] : 0;
         t.e = tab.expert[p];
@@ -63,11 +60,14 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     return true;
 }
 
-// Stage a 64 x 16 slice (rows of `src`, K-contiguous, starting at k0) into
-// LDS as [k][row].  Thread tid loads 4 consecutive k of row tid / 4.
-__device__ __forceinline__ void stage(float (*dst)[BM + PAD], const float *const src_row, int k0) {
-    const int q = (threadIdx.x & 3) * 4, r = threadIdx.x >> 2;
-    const float4 v = *reinterpret_cast<const float4 *>(src_row + k0 + q);
+// A 64 x 16 step of an operand (rows K-contiguous): thread tid holds 4
+// consecutive k of row tid / 4, loaded as one 16-byte vector; put() writes
+// it into the LDS slice as [k][row].
+__device__ __forceinline__ f32x4 take(const float *const src_row, int k0) {
+    return *reinterpret_cast<const f32x4 *>(src_row + k0 + (threadIdx.x & 3) * 4);
+}
+__device__ __forceinline__ void put(float (*dst)[BM + PAD], int kk0, const f32x4 &v) {
+    const int q = kk0 + (threadIdx.x & 3) * 4, r = threadIdx.x >> 2;
     dst[q + 0][r] = v.x;
     dst[q + 1][r] = v.y;
     dst[q + 2][r] = v.z;
@@ -75,7 +75,7 @@ __device__ __forceinline__ void stage(float (*dst)[BM + PAD], const float *const
 }
 
 __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
-    __shared__ float sA[BK][BM + PAD], sG[BK][BN + PAD], sU[BK][BN + PAD];
+    __shared__ float sA[BKS][BM + PAD], sG[BKS][BN + PAD], sU[BKS][BN + PAD];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t)) return;
     const int K = a.K, N = a.N;
@@ -90,29 +90,49 @@ __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
 
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     float ag[4][4] = {}, au[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();
-        stage(sA, a_row, k0);
-        stage(sG, g_row, k0);
-        stage(sU, u_row, k0);
-        __syncthreads();
+    f32x4 ra[NS], rg[NS], ru[NS];
+    auto load = [&](int k0) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk++) {
-            float av[4], gv[4], uv[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                gv[j] = sG[kk][tx + 16 * j];
-                uv[j] = sU[kk][tx + 16 * j];
+        for (int s = 0; s < NS; s++)
+            if (k0 + BK * s < K) {
+                ra[s] = take(a_row, k0 + BK * s);
+                rg[s] = take(g_row, k0 + BK * s);
+                ru[s] = take(u_row, k0 + BK * s);
             }
+    };
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += BKS) {
+        __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+        for (int s = 0; s < NS; s++)
+            if (k0 + BK * s < K) {
+                put(sA, BK * s, ra[s]);
+                put(sG, BK * s, rg[s]);
+                put(sU, BK * s, ru[s]);
+            }
+        __syncthreads();
+        if (k0 + BKS < K) load(k0 + BKS);
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            if (k0 + BK * s >= K) break;
+#pragma unroll
+            for (int kk = BK * s; kk < BK * (s + 1); kk++) {
+                float av[4], gv[4], uv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    ag[i][j] = fmaf(av[i], gv[j], ag[i][j]);
-                    au[i][j] = fmaf(av[i], uv[j], au[i][j]);
+                    gv[j] = sG[kk][tx + 16 * j];
+                    uv[j] = sU[kk][tx + 16 * j];
                 }
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        ag[i][j] = fmaf(av[i], gv[j], ag[i][j]);
+                        au[i][j] = fmaf(av[i], uv[j], au[i][j]);
+                    }
+            }
         }
     }
     float *out = static_cast<float *>(a.out);
@@ -133,7 +153,7 @@ __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
 }
 
 __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
-    __shared__ float sA[BK][BM + PAD], sB[BK][BN + PAD];
+    __shared__ float sA[BKS][BM + PAD], sB[BKS][BN + PAD];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t, a.first_cnt,
                  a.phase))
@@ -149,23 +169,44 @@ __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
 
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += BK) {
+    f32x4 ra[NS], rb[NS];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const int k = k0 + BK * s;
+            if (k < K) {
+                ra[s] = take(a_row, k);
+                // step k lies in block k / ksp (ksp is a multiple of 16)
+                rb[s] = take(W + (k / ksp) * blk + static_cast<size_t>(n_ld) * ksp, k % ksp);
+            }
+        }
+    };
+    load(0);
+    for (int k0 = 0; k0 < K; k0 += BKS) {
         __syncthreads();
-        stage(sA, a_row, k0);
-        // K slice k0 lies in block k0 / ksp (ksp is a multiple of 16)
-        stage(sB, W + (k0 / ksp) * blk + static_cast<size_t>(n_ld) * ksp, k0 % ksp);
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+            if (k0 + BK * s < K) {
+                put(sA, BK * s, ra[s]);
+                put(sB, BK * s, rb[s]);
+            }
         __syncthreads();
+        if (k0 + BKS < K) load(k0 + BKS);
 #pragma unroll
-        for (int kk = 0; kk < BK; kk++) {
-            float av[4], bv[4];
+        for (int s = 0; s < NS; s++) {
+            if (k0 + BK * s >= K) break;
 #pragma unroll
-            for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
+            for (int kk = BK * s; kk < BK * (s + 1); kk++) {
+                float av[4], bv[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++) bv[j] = sB[kk][tx + 16 * j];
+                for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+                for (int j = 0; j < 4; j++) bv[j] = sB[kk][tx + 16 * j];
 #pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+            }
         }
     }
 #pragma unroll
