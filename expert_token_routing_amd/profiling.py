@@ -254,7 +254,8 @@ def _main(argv=None):
                    "k_gate_bf16": "gate.hip", "k_sim_gram": "similarity.hip",
                    "k_dispatch": "rows.hip", "k_combine": "rows.hip",
                    "k_merge_slots": "rows.hip",
-                   "k_route": "route.hip", "k_brim_fill": "brim.hip"}
+                   "k_route": "route.hip", "k_route_rows": "route.hip",
+                   "k_brim_fill": "brim.hip", "k_brim_small": "brim.hip"}
         text = summarize_traffic(a.fetch_dir, a.write_dir, a.fetch_command, a.write_command,
                                  a.workload, a.copy_bytes, sources, a.title)
     with open(a.out, "w") as f:
