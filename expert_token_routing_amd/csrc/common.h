@@ -25,7 +25,7 @@ constexpr int kMaxBins = kMaxNd + 2 * kMaxNe;  // BRIM bins: groups, experts, fi
 #define OCC_GEMM_BM 320
 #endif
 constexpr int kGemmBmBf16 = OCC_GEMM_BM;
-constexpr int kGemmBmF32 = 64;
+constexpr int kGemmBmF32 = 32;
 
 // The expert placement, passed by value as a kernel argument (no device copy,
 // validated on the host).  Position p = g*n + j holds expert `expert[p]`.

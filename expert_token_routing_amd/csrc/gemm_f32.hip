@@ -4,27 +4,28 @@
 // 8), on the vector ALUs.  On MI355X fp32 vector FMA and fp32 MFMA have the
 // same peak, so a plain LDS-tiled kernel suffices for the fp32 workloads.
 //
-// A 256-thread workgroup computes 64 rows x 64 output columns; thread
-// (ty, tx) owns rows ty + 16*i and columns tx + 16*j (i, j < 4), so the LDS
-// reads of a 16-thread row are consecutive.  K slices of 64 are staged
-// K-major in LDS; the next slice's loads go out into registers before the
-// current one is multiplied, so that a tile waits for one load round trip
-// per 64-deep slice (16-deep slices loaded one at a time left the small
-// fp32 layers' GEMMs waiting on a round trip every 16 k).  Every output
-// accumulates its k in ascending order, one fma each.  Tile scheduling
-// follows the same per-expert row-tile schedule as the bf16 kernels, with
-// 64-row tiles.
+// A 256-thread workgroup computes 32 rows x 32 output columns; thread
+// (ty, tx) owns rows ty + 16*i and columns tx + 16*j (i, j < 2), so the LDS
+// reads of a 16-thread row are consecutive.  The fp32 layers here are small
+// (hundreds of tokens), where a tile's length, not the CUs' throughput,
+// sets the time: 32 x 32 tiles give four times the workgroups of 64 x 64
+// ones, each a quarter of the serial FMAs per thread.  K slices of 64 are
+// staged K-major in LDS; the next slice's loads go out into registers
+// before the current one is multiplied, so that a tile waits for one load
+// round trip per 64-deep slice.  Every output accumulates its k in
+// ascending order, one fma each.  Tile scheduling follows the same
+// per-expert row-tile schedule as the bf16 kernels, with 32-row tiles.
 #include "launch.h"
 
 namespace occ {
 namespace {
 
-constexpr int BM = kGemmBmF32;  // 64
-constexpr int BN = 64;
-constexpr int BK = 16;           // k per load step (K is a multiple of 16)
-constexpr int NS = 4;            // load steps per LDS slice
-constexpr int BKS = BK * NS;     // 64-deep LDS slices
+constexpr int BM = kGemmBmF32;  // 32
+constexpr int BN = 32;
+constexpr int BKS = 64;          // k per LDS slice (K is a multiple of 16)
 constexpr int PAD = 4;
+constexpr int NT = 256;
+static_assert(BM == 32 && BN == 32, "thread (ty, tx) owns 2 x 2 outputs");
 
 struct Tile {
     int e, seg, m0, rows, n0;
@@ -60,75 +61,84 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     return true;
 }
 
-// A 64 x 16 step of an operand (rows K-contiguous): thread tid holds 4
-// consecutive k of row tid / 4, loaded as one 16-byte vector; put() writes
-// it into the LDS slice as [k][row].
+// Loads of a 64-deep slice of a 32-row operand (rows K-contiguous): thread
+// tid moves 4 consecutive k (k4 = 4 (tid & 15)) of rows (tid >> 4) and
+// (tid >> 4) + 16, one 16-byte vector each; put() writes them into the LDS
+// slice as [k][row].  A vector past K (a multiple of 16) is not loaded.
+__device__ __forceinline__ int k4_of() { return (threadIdx.x & 15) * 4; }
 __device__ __forceinline__ f32x4 take(const float *const src_row, int k0) {
-    return *reinterpret_cast<const f32x4 *>(src_row + k0 + (threadIdx.x & 3) * 4);
+    return *reinterpret_cast<const f32x4 *>(src_row + k0 + k4_of());
 }
-__device__ __forceinline__ void put(float (*dst)[BM + PAD], int kk0, const f32x4 &v) {
-    const int q = kk0 + (threadIdx.x & 3) * 4, r = threadIdx.x >> 2;
+__device__ __forceinline__ void put(float (*dst)[BM + PAD], int h, const f32x4 &v) {
+    const int q = k4_of(), r = (threadIdx.x >> 4) + 16 * h;
     dst[q + 0][r] = v.x;
     dst[q + 1][r] = v.y;
     dst[q + 2][r] = v.z;
     dst[q + 3][r] = v.w;
 }
 
-__global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
+__global__ __launch_bounds__(NT) void k_gemm_up_f32(UpArgs a) {
     __shared__ float sA[BKS][BM + PAD], sG[BKS][BN + PAD], sU[BKS][BN + PAD];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t)) return;
     const int K = a.K, N = a.N;
-    const int r_ld = threadIdx.x >> 2;
-    const int row_ld = t.seg + t.m0 + min(r_ld, t.rows - 1);
-    const int src = a.a_rows ? a.a_rows[row_ld] : row_ld;
-    const float *a_row = static_cast<const float *>(a.A) + static_cast<size_t>(src) * K;
-    const int f_ld = min(t.n0 + r_ld, N - 1);
-    const size_t wbase = static_cast<size_t>(t.e) * N * K + static_cast<size_t>(f_ld) * K;
-    const float *g_row = static_cast<const float *>(a.Wg) + wbase;
-    const float *u_row = static_cast<const float *>(a.Wu) + wbase;
+    const int r_ld = threadIdx.x >> 4;
+    const float *a_row[2], *g_row[2], *u_row[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int row_ld = t.seg + t.m0 + min(r_ld + 16 * h, t.rows - 1);
+        const int src = a.a_rows ? a.a_rows[row_ld] : row_ld;
+        a_row[h] = static_cast<const float *>(a.A) + static_cast<size_t>(src) * K;
+        const int f_ld = min(t.n0 + r_ld + 16 * h, N - 1);
+        const size_t wbase = static_cast<size_t>(t.e) * N * K + static_cast<size_t>(f_ld) * K;
+        g_row[h] = static_cast<const float *>(a.Wg) + wbase;
+        u_row[h] = static_cast<const float *>(a.Wu) + wbase;
+    }
 
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float ag[4][4] = {}, au[4][4] = {};
-    f32x4 ra[NS], rg[NS], ru[NS];
+    float ag[2][2] = {}, au[2][2] = {};
+    f32x4 ra[2], rg[2], ru[2];
     auto load = [&](int k0) {
+        if (k0 + k4_of() < K) {
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            if (k0 + BK * s < K) {
-                ra[s] = take(a_row, k0 + BK * s);
-                rg[s] = take(g_row, k0 + BK * s);
-                ru[s] = take(u_row, k0 + BK * s);
+            for (int h = 0; h < 2; h++) {
+                ra[h] = take(a_row[h], k0);
+                rg[h] = take(g_row[h], k0);
+                ru[h] = take(u_row[h], k0);
             }
+        }
     };
     load(0);
     for (int k0 = 0; k0 < K; k0 += BKS) {
         __syncthreads();
+        if (k0 + k4_of() < K) {
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            if (k0 + BK * s < K) {
-                put(sA, BK * s, ra[s]);
-                put(sG, BK * s, rg[s]);
-                put(sU, BK * s, ru[s]);
+            for (int h = 0; h < 2; h++) {
+                put(sA, h, ra[h]);
+                put(sG, h, rg[h]);
+                put(sU, h, ru[h]);
             }
+        }
         __syncthreads();
         if (k0 + BKS < K) load(k0 + BKS);
+        const int kn = min(BKS, K - k0);  // a multiple of 16
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
-            if (k0 + BK * s >= K) break;
+        for (int s16 = 0; s16 < BKS; s16 += 16) {
+            if (s16 >= kn) break;
 #pragma unroll
-            for (int kk = BK * s; kk < BK * (s + 1); kk++) {
-                float av[4], gv[4], uv[4];
+            for (int kk = s16; kk < s16 + 16; kk++) {
+                float av[2], gv[2], uv[2];
 #pragma unroll
-                for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
+                for (int i = 0; i < 2; i++) av[i] = sA[kk][ty + 16 * i];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int j = 0; j < 2; j++) {
                     gv[j] = sG[kk][tx + 16 * j];
                     uv[j] = sU[kk][tx + 16 * j];
                 }
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
+                    for (int j = 0; j < 2; j++) {
                         ag[i][j] = fmaf(av[i], gv[j], ag[i][j]);
                         au[i][j] = fmaf(av[i], uv[j], au[i][j]);
                     }
@@ -137,13 +147,13 @@ __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
     }
     float *out = static_cast<float *>(a.out);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 2; i++) {
         const int r = ty + 16 * i;
         if (r >= t.rows) continue;
         const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
         const float wr = a.row_w ? a.row_w[row] : 1.f;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < 2; j++) {
             const int f = t.n0 + tx + 16 * j;
             if (f >= N) continue;
             const float g = ag[i][j];
@@ -152,71 +162,79 @@ __global__ __launch_bounds__(256) void k_gemm_up_f32(UpArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
+__global__ __launch_bounds__(NT) void k_gemm_down_f32(DownArgs a) {
     __shared__ float sA[BKS][BM + PAD], sB[BKS][BN + PAD];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.Ne, a.tab, (a.N + BN - 1) / BN, t, a.first_cnt,
                  a.phase))
         return;
     const int K = a.K, N = a.N, ksp = a.k_split;
-    const int r_ld = threadIdx.x >> 2;
-    const int row_ld = t.seg + t.m0 + min(r_ld, t.rows - 1);
-    const float *a_row = static_cast<const float *>(a.A) +
-                         static_cast<size_t>(a.rows ? a.rows[row_ld] : row_ld) * K;
-    const int n_ld = min(t.n0 + r_ld, N - 1);
+    const int r_ld = threadIdx.x >> 4;
+    const float *a_row[2];
+    size_t b_row[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int row_ld = t.seg + t.m0 + min(r_ld + 16 * h, t.rows - 1);
+        a_row[h] = static_cast<const float *>(a.A) +
+                   static_cast<size_t>(a.rows ? a.rows[row_ld] : row_ld) * K;
+        b_row[h] = static_cast<size_t>(min(t.n0 + r_ld + 16 * h, N - 1)) * ksp;
+    }
     const float *W = static_cast<const float *>(a.W) + static_cast<size_t>(t.e) * N * K;
     const size_t blk = static_cast<size_t>(N) * ksp;
 
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float acc[4][4] = {};
-    f32x4 ra[NS], rb[NS];
+    float acc[2][2] = {};
+    f32x4 ra[2], rb[2];
     auto load = [&](int k0) {
+        const int k = k0 + k4_of();
+        if (k < K) {
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const int k = k0 + BK * s;
-            if (k < K) {
-                ra[s] = take(a_row, k);
-                // step k lies in block k / ksp (ksp is a multiple of 16)
-                rb[s] = take(W + (k / ksp) * blk + static_cast<size_t>(n_ld) * ksp, k % ksp);
+            for (int h = 0; h < 2; h++) {
+                ra[h] = take(a_row[h], k0);
+                // k lies in block k / ksp (ksp is a multiple of 16, so the
+                // thread's 4 k do too)
+                rb[h] = *reinterpret_cast<const f32x4 *>(W + (k / ksp) * blk + b_row[h] + k % ksp);
             }
         }
     };
     load(0);
     for (int k0 = 0; k0 < K; k0 += BKS) {
         __syncthreads();
+        if (k0 + k4_of() < K) {
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-            if (k0 + BK * s < K) {
-                put(sA, BK * s, ra[s]);
-                put(sB, BK * s, rb[s]);
+            for (int h = 0; h < 2; h++) {
+                put(sA, h, ra[h]);
+                put(sB, h, rb[h]);
             }
+        }
         __syncthreads();
         if (k0 + BKS < K) load(k0 + BKS);
+        const int kn = min(BKS, K - k0);  // a multiple of 16
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
-            if (k0 + BK * s >= K) break;
+        for (int s16 = 0; s16 < BKS; s16 += 16) {
+            if (s16 >= kn) break;
 #pragma unroll
-            for (int kk = BK * s; kk < BK * (s + 1); kk++) {
-                float av[4], bv[4];
+            for (int kk = s16; kk < s16 + 16; kk++) {
+                float av[2], bv[2];
 #pragma unroll
-                for (int i = 0; i < 4; i++) av[i] = sA[kk][ty + 16 * i];
+                for (int i = 0; i < 2; i++) av[i] = sA[kk][ty + 16 * i];
 #pragma unroll
-                for (int j = 0; j < 4; j++) bv[j] = sB[kk][tx + 16 * j];
+                for (int j = 0; j < 2; j++) bv[j] = sB[kk][tx + 16 * j];
 #pragma unroll
-                for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int j = 0; j < 4; j++) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+                    for (int j = 0; j < 2; j++) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
             }
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 2; i++) {
         const int r = ty + 16 * i;
         if (r >= t.rows) continue;
         const size_t row = static_cast<size_t>(t.seg) + t.m0 + r;
         const int erow = a.rows ? a.rows[row] : static_cast<int>(row);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < 2; j++) {
             const int c = t.n0 + tx + 16 * j;
             if (c >= N) continue;
             if (!a.dst_rows) a.out[row * N + c] = acc[i][j];
@@ -232,14 +250,14 @@ __global__ __launch_bounds__(256) void k_gemm_down_f32(DownArgs a) {
 hipError_t launch_gemm_up_f32(const UpArgs &a, size_t max_m_tiles, hipStream_t s) {
     const size_t grid = max_m_tiles * ceil_div(a.N, BN);
     if (grid == 0) return hipSuccess;
-    k_gemm_up_f32<<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+    k_gemm_up_f32<<<static_cast<unsigned>(grid), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream_t s) {
     const size_t grid = max_m_tiles * ceil_div(a.N, BN);
     if (grid == 0) return hipSuccess;
-    k_gemm_down_f32<<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+    k_gemm_down_f32<<<static_cast<unsigned>(grid), NT, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -181,9 +181,9 @@ def check_brim(wl, placement, ids_g=None, w_g=None):
         grp[row] = g
     tt = np.repeat(np.arange(T), k)
     assert np.array_equal(b["epd_src"][rows], b["brim0"][grp[ids_g.reshape(-1)], tt])
-    # the library's row-tile capacity: 64 for fp32; bf16 takes 128-row tiles
+    # the library's row-tile capacity: 32 for fp32; bf16 takes 128-row tiles
     # when the experts average fewer than 96 rows, else tiles of up to 320
-    bm = (64 if wl.dtype != W.DTYPE_BF16 else 128 if wl.T * wl.k < 96 * wl.Ne else 320)
+    bm = (32 if wl.dtype != W.DTYPE_BF16 else 128 if wl.T * wl.k < 96 * wl.Ne else 320)
     loads = np.diff(b["epd_off"])
     assert np.array_equal(np.diff(b["tile_off"]), tile_schedule(wl, loads, bm))
     # merge order: per expert, the EPD rows that are the first (lowest-slot)
