@@ -508,12 +508,12 @@ def stage_rooflines(wl, stages, ms, flags, n_sfd, active, profiling):
 
 def dense_pipelined(M, cols):
     """The library's size rule: a dense product (the shared experts) of at
-    least 8 rounds of 256 x 256 tiles on the GPU's CUs runs on the pipelined
+    least 4 rounds of 256 x 256 tiles on the GPU's CUs runs on the pipelined
     four-wave build (kernels k_gemm_*_dense)."""
     import torch
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return -(-M // 256) * -(-cols // 256) >= 8 * cus
+    return -(-M // 256) * -(-cols // 256) >= 4 * cus
 
 
 def dominant_roofline(wl, stages, n_sfd, active, profiling):

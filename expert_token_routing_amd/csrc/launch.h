@@ -131,7 +131,7 @@ hipError_t launch_gemm_down_bf16_m128(const DownArgs &a, size_t max_m_tiles, hip
 // (gemm_bf16_dense.hip), for dense products only (seg_off NULL; a routed
 // launch returns hipErrorInvalidValue).  Taken by dense products of at least
 // kDensePipeRounds rounds of tiles on the CUs.
-constexpr int kDensePipeRounds = 8;
+constexpr int kDensePipeRounds = 4;
 hipError_t launch_gemm_up_bf16_dense(const UpArgs &a, size_t max_m_tiles, hipStream_t s);
 hipError_t launch_gemm_down_bf16_dense(const DownArgs &a, size_t max_m_tiles, hipStream_t s);
 

@@ -1,6 +1,6 @@
 """GPU parity of the shared experts' large dense products.  A dense product
-that fills at least 8 rounds of the CUs with 256 x 256 tiles (T x output
-width >= 8 x 256 x 65,536 on 256 CUs) takes the four-wave, software-
+that fills at least 4 rounds of the CUs with 256 x 256 tiles (T x output
+width >= 4 x 256 x 65,536 on 256 CUs) takes the four-wave, software-
 pipelined GEMM build; these shapes reach that size while driving the
 pipelined loop's edge cases: one, two, three and four 64-deep K slices, a
 ragged last row tile (T not a multiple of 256), a partial last column tile,
@@ -43,7 +43,7 @@ def pipelined(M, cols):
     """Whether the library's size rule sends a dense product to the
     pipelined build on this GPU."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return -(-M // 256) * -(-cols // 256) >= 8 * cus
+    return -(-M // 256) * -(-cols // 256) >= 4 * cus
 
 
 def sample(T, seed):
