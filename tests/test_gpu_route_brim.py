@@ -100,7 +100,10 @@ def test_route_nan_logits_rank_last(Ne, k, rule):
 
 def test_route_ties_and_wide_expert_counts():
     # integer-valued logits: many exact ties, broken toward the lower index
-    for Ne, k, Nd in [(8, 2, 2), (64, 8, 8), (256, 8, 16), (130, 5, 10), (32, 32, 4)]:
+    # Ne <= 64 without pruning takes the 16-lanes-per-token kernel (k up to
+    # 32: two recorded rounds per lane), the others the wave kernel
+    for Ne, k, Nd in [(8, 2, 2), (8, 8, 2), (12, 5, 3), (64, 8, 8), (60, 17, 4), (256, 8, 16),
+                      (130, 5, 10), (32, 32, 4)]:
         wl = W.Workload(f"ties_{Ne}", 9, T=777, d=64, Ne=Ne, k=k, Nd=Nd, F=64)
         g = torch.Generator().manual_seed(Ne)
         logits = torch.randint(-3, 4, (777, Ne), generator=g).float()
