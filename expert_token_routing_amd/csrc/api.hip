@@ -93,7 +93,7 @@ struct Layout {
     // training only (flags & OCC_FLAG_TRAIN): saved pre-activations and the
     // backward pass's buffers
     size_t gu, gu_sh, dy_sfd, dgu, dx_sfd, dw_part, zero_row, bt_all, bt_first, bt_rest, dgu_sh,
-        dx_sh, dense_seg, dense_tile, wg_part;
+        dx_sh, wt_sh, dense_seg, dense_tile, wg_part;
     int dw_stride;
     size_t total;
 };
@@ -157,6 +157,9 @@ Layout layout(const occ_layer_desc &D) {
             L.gu_sh = take(T * 2 * Nsh * es);
             L.dgu_sh = take(T * 2 * Nsh * es);
             L.dx_sh = take(T * d * 4);
+            // the shared gate and up weights transposed, d x 2 F_shared per
+            // expert (the input gradient's contraction index contiguous)
+            L.wt_sh = take(Nsh * d * 2 * es);
             // the shared weight gradients' split-K partials (dense, K = T)
             const size_t Fs = D.F_shared, nsh = D.n_shared;
             const size_t p3 = wgrad_k_parts(D.n_shared, D.d, D.F_shared, D.T);
@@ -787,9 +790,7 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
         // one row-tile schedule per product: dg, du against F_shared columns,
         // dx against d columns, each balanced over the CUs' rounds
         const int m_gu = dense_row_tiles_bwd(D.T, ceil_div(D.F_shared, kBwdTile));
-        const int m_dx = dense_row_tiles_bwd(D.T, ceil_div(D.d, kBwdTile));
         OCC_HIP(launch_dense_sched(D.T, m_gu, dseg, dtile, s));
-        OCC_HIP(launch_dense_sched(D.T, m_dx, dseg, dtile + 2, s));
         PlaceTab one{};
         one.Ne = 1;
         one.Nd = 1;
@@ -818,24 +819,34 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
             s1.epilogue = BWD_EPI_SWIGLU;
             s1.tab = one;
             OCC_HIP(launch_bwd_dgrad(s1, m_gu, s));
-            BwdDgradArgs s2{};
-            s2.A = dgu_sh;
-            s2.lda = static_cast<int>(2 * Nsh);
-            s2.a_col = static_cast<int>(sx * 2 * Fs);
-            s2.B1 = static_cast<const char *>(ws_gate) + sx * Fs * d * es;
-            s2.B2 = static_cast<const char *>(ws_up) + sx * Fs * d * es;
-            s2.seg_off = dseg;
-            s2.tile_off = dtile + 2;
-            s2.merge_out = dx_sh;
-            s2.merge_store = sx == 0;
-            s2.N = D.d;
-            s2.K = static_cast<int>(2 * Fs);
-            s2.ksplit = D.F_shared;
-            s2.Ne = 1;
-            s2.epilogue = BWD_EPI_MERGE;
-            s2.tab = one;
-            OCC_HIP(launch_bwd_dgrad(s2, m_dx, s));
         }
+        // dx_sh = sum over the shared experts of dg W_g + du W_u: one dense
+        // product with K = 2 n_shared F_shared against the weights
+        // transposed (expert sx's block holds W_g^T then W_u^T), on the
+        // forward's down-projection build, whose operands both have the
+        // contraction index contiguous (no LDS transpose reads)
+        void *wt_sh = at<void>(workspace, L.wt_sh);
+        const size_t Fs = D.F_shared, blk = d * 2 * Fs;
+        OCC_HIP(launch_transpose_bf16(ws_gate, D.F_shared, D.d, Fs * d, wt_sh,
+                                      static_cast<int>(2 * Fs), blk, D.n_shared, s));
+        OCC_HIP(launch_transpose_bf16(ws_up, D.F_shared, D.d, Fs * d,
+                                      static_cast<char *>(wt_sh) + Fs * es,
+                                      static_cast<int>(2 * Fs), blk, D.n_shared, s));
+        DownArgs s2{};
+        s2.A = dgu_sh;
+        s2.W = wt_sh;
+        s2.out = dx_sh;
+        s2.M = D.T;
+        s2.K = static_cast<int>(2 * Nsh);
+        s2.N = D.d;
+        s2.Ne = 1;
+        s2.k_split = static_cast<int>(2 * Fs);
+        s2.tab = one;
+        const GemmOps ops = gemm_ops(D);
+        if (dense_pipelined(ops, D.T, D.d))
+            OCC_HIP(launch_gemm_down_bf16_dense(s2, 0, s));
+        else
+            OCC_HIP(ops.down(s2, 0, s));
         BwdWgradArgs w3{};
         w3.A = dy;
         w3.lda = D.d;

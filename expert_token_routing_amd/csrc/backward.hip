@@ -53,6 +53,37 @@ __global__ void k_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *til
     }
 }
 
+// dst[c * ldd + r] = src[r * C + c] for 64 x 64 tiles of bf16 bits staged
+// through LDS: each thread loads two 16-byte row pieces and stores two
+// 16-byte pieces of the transposed rows; blockIdx.z selects the matrix.
+constexpr int kTr = 64;
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restrict__ src, int C,
+                                                       size_t src_z, uint16_t *__restrict__ dst,
+                                                       int ldd, size_t dst_z) {
+    __shared__ uint16_t s[kTr][kTr + 2];
+    const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr, t = threadIdx.x, ch = t & 7;
+    src += blockIdx.z * src_z;
+    dst += blockIdx.z * dst_z;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int r = (t >> 3) + 32 * i;
+        const u16x8_t v =
+            *reinterpret_cast<const u16x8_t *>(src + static_cast<size_t>(r0 + r) * C + c0 + ch * 8);
+#pragma unroll
+        for (int j = 0; j < 8; j++) s[r][ch * 8 + j] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int c = (t >> 3) + 32 * i;
+        u16x8_t v;
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = s[ch * 8 + j][c];
+        *reinterpret_cast<u16x8_t *>(dst + static_cast<size_t>(c0 + c) * ldd + r0 + ch * 8) = v;
+    }
+}
+
 constexpr int kRbWaves = 4;  // tokens per workgroup
 
 // One wave per token.  Lane j < k sums its EPD row's dw partials in order;
@@ -125,6 +156,15 @@ hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, i
 hipError_t launch_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off,
                               hipStream_t s) {
     k_dense_sched<<<1, kWave, 0, s>>>(T, m_tiles, seg_off, tile_off);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void *src, int R, int C, size_t src_z, void *dst, int ldd,
+                                 size_t dst_z, int nz, hipStream_t s) {
+    if (R % kTr || C % kTr || ldd < R || nz < 1) return hipErrorInvalidValue;
+    if (R == 0 || C == 0) return hipSuccess;
+    k_transpose_bf16<<<dim3(C / kTr, R / kTr, nz), 256, 0, s>>>(
+        static_cast<const uint16_t *>(src), C, src_z, static_cast<uint16_t *>(dst), ldd, dst_z);
     return hipGetLastError();
 }
 

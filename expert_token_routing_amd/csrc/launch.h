@@ -216,6 +216,11 @@ hipError_t launch_tile_sched(const int32_t *epd_off, const int32_t *first_cnt, i
 // tile_off = {0, m_tiles} (the rows shared out evenly over m_tiles tiles).
 hipError_t launch_dense_sched(int T, int m_tiles, int32_t *seg_off, int32_t *tile_off,
                               hipStream_t s);
+// nz bf16 matrices of R x C, the z-th at src + z * src_z (elements), each
+// written transposed: dst[z * dst_z + c * ldd + r] = src[z * src_z + r * C + c].
+// R and C multiples of 64, ldd >= R, 16-byte aligned rows.
+hipError_t launch_transpose_bf16(const void *src, int R, int C, size_t src_z, void *dst, int ldd,
+                                 size_t dst_z, int nz, hipStream_t s);
 // Routing-weight and logit gradients: dw[t, j] = sum of dw_part over the
 // EPD row tok_epd[t*k + j]'s nparts partials (in order); dlogits through the
 // full softmax of the logits (logits may be NULL: dw only).

@@ -300,3 +300,41 @@ def test_backward_full_size_shared_experts_sampled():
             for i in range(len(sel)):
                 assert normwise(g[i], q[key][i]) <= NORM_TOL, (key, sx, sel[i])
                 assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max()
+
+
+def test_backward_shared_input_gradient_pipelined_build():
+    """A batch long enough (T = 32768, d = 2048: 128 x 8 tiles of 256 x 256,
+    four rounds of the CUs) that the shared experts' input gradient
+    dg W_g + du W_u runs on the pipelined dense build, over the transposed
+    shared weights; sampled dx rows against the oracle."""
+    wl = shape("bwd_shared_pipe", T=32768, d=2048, F=256, n_shared=1, F_shared=512, index=19)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert (wl.T // 256) * (wl.d // 256) >= 4 * cus
+    inp = synth.make_all(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    ids, w = check_train_forward(wl, inp, L, desc, ws, y, rows=synth.sample_rows(wl.T, 32, seed=25))
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(10)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    dWsg = torch.empty(1, wl.F_shared, wl.d, **f32)
+    dWsu = torch.empty_like(dWsg)
+    dWsd = torch.empty(1, wl.d, wl.F_shared, **f32)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                         dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], dx, dWg, dWu,
+                         dWd, dWsg, dWsu, dWsd, None, None, ws)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(wl.T, 24, seed=26)
+    r = oracle.moe_backward_rows(rows, bits(inp["x"]), ids, w, dy.double().numpy(),
+                                 bits(inp["w_gate"]), bits(inp["w_up"]), bits(inp["w_down"]),
+                                 bits(inp["ws_gate"]), bits(inp["ws_up"]), bits(inp["ws_down"]))
+    assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
