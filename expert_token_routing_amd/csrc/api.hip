@@ -93,7 +93,7 @@ struct Layout {
     // training only (flags & OCC_FLAG_TRAIN): saved pre-activations and the
     // backward pass's buffers
     size_t gu, gu_sh, dy_sfd, dgu, dx_sfd, dw_part, zero_row, bt_all, bt_first, bt_rest, dgu_sh,
-        dx_sh, wt_sh, dense_seg, dense_tile, wg_part;
+        dx_sh, wt_sh, wt_down, dense_seg, dense_tile, wg_part;
     int dw_stride;
     size_t total;
 };
@@ -160,6 +160,9 @@ Layout layout(const occ_layer_desc &D) {
             // the shared gate and up weights transposed, d x 2 F_shared per
             // expert (the input gradient's contraction index contiguous)
             L.wt_sh = take(Nsh * d * 2 * es);
+            // and the shared down-projection weights, F_shared x d per
+            // expert, for dh_sh = dy W_d read K-contiguous
+            L.wt_down = take(Nsh * d * es);
             // the shared weight gradients' split-K partials (dense, K = T)
             const size_t Fs = D.F_shared, nsh = D.n_shared;
             const size_t p3 = wgrad_k_parts(D.n_shared, D.d, D.F_shared, D.T);
@@ -796,12 +799,20 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
         one.Nd = 1;
         one.n = 1;
         void *dgu_sh = at<void>(workspace, L.dgu_sh);
+        // the shared W_d transposed (F_shared x d per expert), so that
+        // dh_sh = dy W_d reads both operands K-contiguous.  (The routed
+        // experts keep transpose reads: there the copy of all their W_d
+        // costs what the faster product saves.)
+        void *wt_down = at<void>(workspace, L.wt_down);
+        OCC_HIP(launch_transpose_bf16(ws_down, D.d, D.F_shared, d * D.F_shared, wt_down, D.d,
+                                      static_cast<size_t>(D.F_shared) * d, D.n_shared, s));
         for (int sx = 0; sx < D.n_shared; sx++) {
             const size_t Fs = D.F_shared;
             BwdDgradArgs s1{};
             s1.A = dy;
             s1.lda = D.d;
-            s1.B1 = static_cast<const char *>(ws_down) + sx * d * Fs * es;
+            s1.B1 = static_cast<const char *>(wt_down) + sx * Fs * d * es;
+            s1.b_kcontig = 1;
             s1.seg_off = dseg;
             s1.tile_off = dtile;
             s1.gu = at<void>(workspace, L.gu_sh);

@@ -23,7 +23,11 @@
 // wave row's 16-row blocks), K in 64-deep slices through two LDS buffers
 // filled by direct global->LDS loads, as in the forward GEMMs.
 //   k_bwd_dgrad  A = gathered K-contiguous rows, B = an expert's weights read
-//                K-major; routed row tiles over expert segments.  Epilogues:
+//                K-major (or, for the shared experts' dh, their W_d copied
+//                transposed beforehand and read like A, which measured 2%
+//                faster on that product family; for the routed experts the
+//                copy of all their W_d would cost what it saves); routed row
+//                tiles over expert segments.  Epilogues:
 //                SwiGLU backward (dh -> dg, du and the routing-weight
 //                gradient's per-tile partial sums) or the fp32 merge of EPD
 //                rows into their SFD rows (first contributors store, the rest
@@ -198,7 +202,9 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- dgrad ----
 
-template <int EPI>
+// BKC: B1 holds the weights transposed (expert e's N x K block, row n
+// K-contiguous), loaded and read like A instead of through transpose reads.
+template <int EPI, bool BKC>
 __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGED];
     __shared__ int s_dst[EPI == BWD_EPI_MERGE ? BMD : 1];
@@ -258,6 +264,17 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
                                     static_cast<size_t>(e) * (a.K - a.ksplit) * a.N
                               : nullptr;
     const int ncol = min(n0, a.N - BN);  // N >= BN; the last tile may overlap the previous one
+    // BKC: rows ncol + r0 + 64 i of the transposed block, as the A loads
+    const uint16_t *bt_src[BKC ? BN / 64 : 1];
+    if constexpr (BKC) {
+        const int r0 = tid / CHUNKS;
+#pragma unroll
+        for (int i = 0; i < BN / 64; i++) {
+            const int ch = (tid % CHUNKS) ^ (((r0 + 64 * i) >> 1) & (CHUNKS - 1));
+            bt_src[i] = static_cast<const uint16_t *>(a.B1) +
+                        (static_cast<size_t>(e) * a.N + ncol + r0 + 64 * i) * a.K + 8 * ch;
+        }
+    }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
     const int nk = a.K / BK;
 
@@ -283,7 +300,7 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
                 wait_all_loads();
                 __syncthreads();
             }
-            launder(adB);
+            if constexpr (!BKC) launder(adB);
             if (kt < nk) {
                 const uint32_t st = lds0 + static_cast<uint32_t>((kt % NSTAGE) * STAGED * 2);
                 const int k0 = kt * BK;
@@ -291,14 +308,22 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
                 for (int i = 0; i < A_LDD; i++)
                     if (i < na)
                         dma16(a_src[i] + k0, __builtin_amdgcn_readfirstlane(st + (8 * i + w) * 1024));
-                const uint16_t *brow[4];
+                if constexpr (BKC) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int kk = k0 + kmajor_row(i, w);
-                    brow[i] = (kk < a.ksplit ? B1 + static_cast<size_t>(kk) * a.N
-                                             : B2 + static_cast<size_t>(kk - a.ksplit) * a.N) + ncol;
+                    for (int i = 0; i < BN / 64; i++)
+                        dma16(bt_src[i] + k0,
+                              __builtin_amdgcn_readfirstlane(st + OPA * 2 + (8 * i + w) * 1024));
+                } else {
+                    const uint16_t *brow[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int kk = k0 + kmajor_row(i, w);
+                        brow[i] = (kk < a.ksplit ? B1 + static_cast<size_t>(kk) * a.N
+                                                 : B2 + static_cast<size_t>(kk - a.ksplit) * a.N) +
+                                  ncol;
+                    }
+                    issue_kmajor(st + OPA * 2, brow, w);
                 }
-                issue_kmajor(st + OPA * 2, brow, w);
             }
             if (kt == 0 || NV == 0) continue;
             const uint16_t *sA = smem + ((kt - 1) % NSTAGE) * STAGED, *sB = sA + OPA;
@@ -308,7 +333,9 @@ __global__ __launch_bounds__(NT, 2) void k_bwd_dgrad(BwdDgradArgs a) {
 #pragma unroll
                 for (int mi = 0; mi < NV; mi++) fa[mi] = rows_frag(sA, block_row(wm, mi) + (l & 15), ks);
 #pragma unroll
-                for (int ni = 0; ni < NI; ni++) fb[ni] = kmaj_frag(sB, adB, ks, ni);
+                for (int ni = 0; ni < NI; ni++)
+                    fb[ni] = BKC ? rows_frag(sB, wn * WN + ni * 16 + (l & 15), ks)
+                                 : kmaj_frag(sB, adB, ks, ni);
                 mfma_tile<EPI == BWD_EPI_SWIGLU, NV, MID>(fa, fb, acc);
             }
         }
@@ -620,8 +647,14 @@ int wgrad_k_chunk(int rows, int parts) {
 hipError_t launch_bwd_dgrad(const BwdDgradArgs &a, size_t max_m_tiles, hipStream_t s) {
     const unsigned grid = grid_for(max_m_tiles * ((a.N + BN - 1) / BN));
     if (grid == 0) return hipSuccess;
-    if (a.epilogue == BWD_EPI_SWIGLU) k_bwd_dgrad<BWD_EPI_SWIGLU><<<grid, NT, 0, s>>>(a);
-    else k_bwd_dgrad<BWD_EPI_MERGE><<<grid, NT, 0, s>>>(a);
+    if (a.b_kcontig && (a.epilogue != BWD_EPI_SWIGLU || a.B2 || a.ksplit != a.K))
+        return hipErrorInvalidValue;
+    if (a.epilogue == BWD_EPI_SWIGLU) {
+        if (a.b_kcontig) k_bwd_dgrad<BWD_EPI_SWIGLU, true><<<grid, NT, 0, s>>>(a);
+        else k_bwd_dgrad<BWD_EPI_SWIGLU, false><<<grid, NT, 0, s>>>(a);
+    } else {
+        k_bwd_dgrad<BWD_EPI_MERGE, false><<<grid, NT, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

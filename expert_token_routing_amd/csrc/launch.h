@@ -145,7 +145,9 @@ hipError_t launch_gemm_down_f32(const DownArgs &a, size_t max_m_tiles, hipStream
 // DownArgs):  C[pos, :] = A_row . B_e, K contracted, with A_row the K values
 // at column a_col of row a_rows[pos] (or pos) of A (rows lda apart), and row
 // k of B_e = B1[e] row k for k < ksplit, else B2[e] row k - ksplit (both N
-// wide, so B is read K-major; e = tab.expert[p]).  N >= 256.
+// wide, so B is read K-major; e = tab.expert[p]).  N >= 256.  With b_kcontig
+// (SWIGLU only, no B2, ksplit = K) B1 holds the weights transposed instead:
+// expert e's block of N rows of K contiguous values, B_e[k][n] = B1[(e N + n) K + k].
 // Epilogue SWIGLU: C is dh; with g = gu[pos*gu_ld + gu_col + f], u at
 // + gu_uoff, and w = row_w[pos] (1 if NULL), writes bf16 dg, du to
 // out[pos*out_ld + out_col + f] and + out_uoff, and (dw_part non-NULL)
@@ -171,7 +173,7 @@ struct BwdDgradArgs {
     float *dw_part;
     float *merge_out;
     float *epd_out;
-    int N, K, ksplit, Ne, phase, epilogue, dw_stride, merge_store, split;
+    int N, K, ksplit, Ne, phase, epilogue, dw_stride, merge_store, split, b_kcontig;
     int lda, a_col, gu_ld, gu_col, gu_uoff, out_ld, out_col, out_uoff;
     PlaceTab tab;
 };
