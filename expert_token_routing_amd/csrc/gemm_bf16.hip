@@ -150,18 +150,23 @@ __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int 
 // bytes per 64-deep K slice at 320 x 256 tiles) rather than one row tile x 32
 // column tiles (the row-major order of a dense product: 1.06 MB) or, for an
 // expert of 14 row tiles walked column by column, 14 x 2-3 (650 KB).
-// Measured (bands of 1, 2, 4, 8 and unbounded): 8 is best, though by little
-// -- the Qwen-shaped layer's step -1.5%, the OLMoE- and DeepSeek-shaped ones
-// -0.5% against unbounded bands -- so L2 reuse is not what bounds these
-// GEMMs.  Local index `local` -> (row tile lm, column tn).
+// Measured (bands of 1, 2, 4, 8 and unbounded): 8 is best for the
+// up-projection, though by little -- the Qwen-shaped layer's step -1.5%, the
+// OLMoE- and DeepSeek-shaped ones -0.5% against unbounded bands -- so L2
+// reuse is not what bounds these GEMMs.  The down-projection (8 column tiles
+// of d = 2048) takes bands of 16, which for these batches' experts of at
+// most 14 row tiles is column by column over the whole expert: against 8,
+// 2% faster on the Qwen-shaped and pruned OLMoE batches, even on the others
+// (bands of 2 and 4 slower).  Local index `local` -> (row tile lm, column tn).
 #ifndef OCC_GEMM_BAND
 #define OCC_GEMM_BAND 8
 #endif
-__device__ __forceinline__ void band_order(int local, int r, int c, int &lm, int &tn) {
-    const int band = local / (OCC_GEMM_BAND * c);
-    const int rb0 = band * OCC_GEMM_BAND;
-    const int rb = min(OCC_GEMM_BAND, r - rb0);
-    const int idx = local - band * OCC_GEMM_BAND * c;
+constexpr int kBandDown = 16;
+__device__ __forceinline__ void band_order(int local, int r, int c, int &lm, int &tn, int B = OCC_GEMM_BAND) {
+    const int band = local / (B * c);
+    const int rb0 = band * B;
+    const int rb = min(B, r - rb0);
+    const int idx = local - band * B * c;
     tn = idx / rb;
     lm = rb0 + idx - tn * rb;
 }
@@ -193,7 +198,8 @@ __device__ __forceinline__ void split_rows(int len, int n, int j, int &m0, int &
 __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *tile_off, int M,
                                         int m_tiles_dense, int Ne, const PlaceTab &tab,
                                         int n_tiles, int n_step, Tile &t,
-                                        const int32_t *first_cnt = nullptr, int phase = 0) {
+                                        const int32_t *first_cnt = nullptr, int phase = 0,
+                                        int band = OCC_GEMM_BAND) {
     int tm, tn;
     if (seg_off) {
         const int m_tiles = tile_off[Ne];
@@ -208,7 +214,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
             // the atomic phase is faster in row order.
             int lm;
             band_order((tm - tile_off[p]) * n_tiles + tn, tile_off[p + 1] - tile_off[p], n_tiles,
-                       lm, tn);
+                       lm, tn, band);
             tm = tile_off[p] + lm;
         }
         const int seg0 = seg_off[p], len = seg_off[p + 1] - seg0;
@@ -221,7 +227,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     } else {
         const int m_tiles = m_tiles_dense;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
-        band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn);
+        band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn, band);
         t.e = 0;
         t.seg = 0;
         split_rows(M, m_tiles, tm, t.m0, t.rows);
@@ -663,7 +669,7 @@ __global__ __launch_bounds__(NT, OCC_GEMM_WG_PER_CU * NT / 256) void OCC_NAMED(k
     __shared__ int s_dst[BM];
     Tile t;
     if (!tile_of(a.seg_off, a.tile_off, a.M, a.m_tiles, a.Ne, a.tab, (a.N + BN - 1) / BN, BN, t,
-                 a.first_cnt, a.phase))
+                 a.first_cnt, a.phase, kBandDown))
         return;
 
     const int tid = threadIdx.x, r0 = tid / CHUNKS;
