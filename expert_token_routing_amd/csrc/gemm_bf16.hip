@@ -153,11 +153,13 @@ __device__ __forceinline__ bool map_tile(int m_tiles, int n_tiles, int &tm, int 
 // Measured (bands of 1, 2, 4, 8 and unbounded): 8 is best for the
 // up-projection, though by little -- the Qwen-shaped layer's step -1.5%, the
 // OLMoE- and DeepSeek-shaped ones -0.5% against unbounded bands -- so L2
-// reuse is not what bounds these GEMMs.  The down-projection (8 column tiles
-// of d = 2048) takes bands of 16, which for these batches' experts of at
-// most 14 row tiles is column by column over the whole expert: against 8,
-// 2% faster on the Qwen-shaped and pruned OLMoE batches, even on the others
-// (bands of 2 and 4 slower).  Local index `local` -> (row tile lm, column tn).
+// reuse is not what bounds these GEMMs.  The routed down-projection (8
+// column tiles of d = 2048) takes bands of 16, which for these batches'
+// experts of at most 14 row tiles is column by column over the whole expert:
+// against 8, 2% faster on the Qwen-shaped and pruned OLMoE batches, even on
+// the others (bands of 2 and 4 slower); dense launches keep 8 (the
+// Qwen-shaped shared down-projection measured 8% slower with 16).  Local
+// index `local` -> (row tile lm, column tn).
 #ifndef OCC_GEMM_BAND
 #define OCC_GEMM_BAND 8
 #endif
@@ -199,7 +201,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
                                         int m_tiles_dense, int Ne, const PlaceTab &tab,
                                         int n_tiles, int n_step, Tile &t,
                                         const int32_t *first_cnt = nullptr, int phase = 0,
-                                        int band = OCC_GEMM_BAND) {
+                                        int band = OCC_GEMM_BAND) {  // routed launches
     int tm, tn;
     if (seg_off) {
         const int m_tiles = tile_off[Ne];
@@ -227,7 +229,7 @@ __device__ __forceinline__ bool tile_of(const int32_t *seg_off, const int32_t *t
     } else {
         const int m_tiles = m_tiles_dense;
         if (!map_tile(m_tiles, n_tiles, tm, tn)) return false;
-        band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn, band);
+        band_order(tm * n_tiles + tn, m_tiles, n_tiles, tm, tn);
         t.e = 0;
         t.seg = 0;
         split_rows(M, m_tiles, tm, t.m0, t.rows);
