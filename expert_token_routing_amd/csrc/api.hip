@@ -152,7 +152,7 @@ Layout layout(const occ_layer_desc &D) {
         L.bt_first = take((Ne + 1) * 4);
         L.bt_rest = take((Ne + 1) * 4);
         L.dense_seg = take(2 * 4);
-        L.dense_tile = take(4 * 4);
+        L.dense_tile = take(2 * 4);
         if (D.n_shared > 0) {
             L.gu_sh = take(T * 2 * Nsh * es);
             L.dgu_sh = take(T * 2 * Nsh * es);
@@ -790,8 +790,8 @@ occ_status occ_moe_backward(const occ_layer_desc *desc, const void *dy, const vo
     if (D.n_shared > 0) {
         int32_t *dseg = at<int32_t>(workspace, L.dense_seg);
         int32_t *dtile = at<int32_t>(workspace, L.dense_tile);
-        // one row-tile schedule per product: dg, du against F_shared columns,
-        // dx against d columns, each balanced over the CUs' rounds
+        // the row-tile schedule of dh -> dg, du against F_shared columns,
+        // balanced over the CUs' rounds (dx_sh below schedules its own)
         const int m_gu = dense_row_tiles_bwd(D.T, ceil_div(D.F_shared, kBwdTile));
         OCC_HIP(launch_dense_sched(D.T, m_gu, dseg, dtile, s));
         PlaceTab one{};
