@@ -139,3 +139,58 @@ def test_large_dense_training():
             den = np.linalg.norm(q[key][i])
             assert np.linalg.norm(g[i] - q[key][i]) / (den if den > 0 else 1.0) <= NORM_TOL, (key, sel[i])
             assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max(), (key, sel[i])
+
+
+def test_large_dense_training_two_shared_experts():
+    """Two shared experts and a batch long enough that their input gradient
+    dx_sh = sum of dg W_g + du W_u (one product over both experts' blocks of
+    transposed weights, K = 2 x 2 x 256) runs on the pipelined build
+    (257 x 4 tiles); sampled dx rows, including the ragged last row tile,
+    and sampled rows of both experts' weight gradients."""
+    wl = shape("dense_train_2sh", 35, d=1024, F_shared=256, n_shared=2)
+    assert pipelined(wl.T, wl.d)
+    inp = synth.make_all(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    torch.cuda.synchronize()
+    ids, w = oracle.route(inp["logits"].numpy(), wl.k, L, wl.prune_rule, wl.prune_groups)
+    rows = sample(wl.T, wl.index)
+    err = row_err(y.float().cpu().numpy().astype(np.float64)[rows], oracle_rows(wl, inp, rows, ids, w))
+    assert err.max() <= TOL[wl.dtype], f"training forward: max per-row rel err {err.max():.3e}"
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(wl.index)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    nsh, Fs = wl.n_shared, wl.F_shared
+    dWsg = torch.empty(nsh, Fs, wl.d, **f32)
+    dWsu = torch.empty_like(dWsg)
+    dWsd = torch.empty(nsh, wl.d, Fs, **f32)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                         dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], dx, dWg, dWu,
+                         dWd, dWsg, dWsu, dWsd, None, None, ws)
+    torch.cuda.synchronize()
+    dyd = dy.double().numpy()
+    r = oracle.moe_backward_rows(rows, bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                 bits(inp["w_up"]), bits(inp["w_down"]), bits(inp["ws_gate"]),
+                                 bits(inp["ws_up"]), bits(inp["ws_down"]))
+    assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
+    fs, ns = np.array([0, 100, Fs - 1]), np.array([0, 517, wl.d - 1])
+    for sx in range(nsh):
+        q = oracle.moe_wgrad_rows(bits(inp["x"]), np.zeros((wl.T, 1), np.int32),
+                                  np.ones((wl.T, 1)), dyd, bits(inp["ws_gate"][sx:sx + 1]),
+                                  bits(inp["ws_up"][sx:sx + 1]), bits(inp["ws_down"][sx:sx + 1]),
+                                  0, fs, ns)
+        for key, got, sel in (("dW_gate", dWsg, fs), ("dW_up", dWsu, fs), ("dW_down", dWsd, ns)):
+            g = got[sx].cpu().numpy()[sel]
+            for i in range(len(sel)):
+                den = np.linalg.norm(q[key][i])
+                assert np.linalg.norm(g[i] - q[key][i]) / (den if den > 0 else 1.0) <= NORM_TOL, \
+                    (key, sx, sel[i])
