@@ -338,3 +338,62 @@ def test_backward_shared_input_gradient_pipelined_build():
                                  bits(inp["w_gate"]), bits(inp["w_up"]), bits(inp["w_down"]),
                                  bits(inp["ws_gate"]), bits(inp["ws_up"]), bits(inp["ws_down"]))
     assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
+
+
+def test_backward_full_size_qwen_sampled():
+    """The Qwen-shaped layer at the size bench.py times its training step
+    (T = 65536, 60 experts of F = 1408, top-4, one shared expert of
+    F = 5632), deterministic merge: sampled dx, dw and dlogits rows, sampled
+    rows of two routed experts' weight gradients, against the oracle
+    computed one by one.  (The shared expert's weight gradients sum over all
+    65536 tokens, each needing the expert's full 5632-feature backward in
+    fp64: they are checked at T = 16384 and on the long dense shapes.)"""
+    from gpu_common import inputs
+    wl = W.QWEN
+    inp = inputs(wl)
+    dev = to_dev(inp)
+    L = inp["placement"]
+    desc = occ.desc_of(wl, flags=occ.OCC_FLAG_TRAIN | occ.OCC_FLAG_DETERMINISTIC)
+    ws = occ.alloc_workspace(desc)
+    dt = torch.bfloat16
+    y = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    occ.occ_moe_forward(desc, dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                        dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], y, ws)
+    ids, w = check_train_forward(wl, inp, L, desc, ws, y, rows=synth.sample_rows(wl.T, 32, seed=27))
+    dy = (torch.randn(wl.T, wl.d, generator=torch.Generator().manual_seed(11)) * 0.5).to(dt)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dx = torch.empty(wl.T, wl.d, dtype=dt, device="cuda")
+    dWg = torch.empty(wl.Ne, wl.F, wl.d, **f32)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(wl.Ne, wl.d, wl.F, **f32)
+    Fs = wl.F_shared
+    dWsg = torch.empty(1, Fs, wl.d, **f32)
+    dWsu = torch.empty_like(dWsg)
+    dWsd = torch.empty(1, wl.d, Fs, **f32)
+    dw = torch.empty(wl.T, wl.k, **f32)
+    dl = torch.empty(wl.T, wl.Ne, **f32)
+    occ.occ_moe_backward(desc, dy.cuda(), dev["x"], dev["logits"], L, dev["w_gate"], dev["w_up"],
+                         dev["w_down"], dev["ws_gate"], dev["ws_up"], dev["ws_down"], dx, dWg, dWu,
+                         dWd, dWsg, dWsu, dWsd, dw, dl, ws)
+    torch.cuda.synchronize()
+    del ws
+    dyd = dy.double().numpy()
+    rows = synth.sample_rows(wl.T, 24, seed=28)
+    r = oracle.moe_backward_rows(rows, bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                 bits(inp["w_up"]), bits(inp["w_down"]), bits(inp["ws_gate"]),
+                                 bits(inp["ws_up"]), bits(inp["ws_down"]),
+                                 logits=inp["logits"].numpy())
+    assert row_err(dx.float().cpu().numpy()[rows], r["dx"]).max() <= NORM_TOL
+    for key, got in (("dw", dw), ("dlogits", dl)):
+        g = got.cpu().numpy()[rows]
+        assert normwise(g, r[key]) <= NORM_TOL, key
+        assert np.abs(g - r[key]).max() <= ELEM_TOL * np.abs(r[key]).max(), key
+    fs, ns = np.array([0, 703, wl.F - 1]), np.array([0, 1001, wl.d - 1])
+    for e in (7, 52):
+        q = oracle.moe_wgrad_rows(bits(inp["x"]), ids, w, dyd, bits(inp["w_gate"]),
+                                  bits(inp["w_up"]), bits(inp["w_down"]), e, fs, ns)
+        for key, got, sel in (("dW_gate", dWg, fs), ("dW_up", dWu, fs), ("dW_down", dWd, ns)):
+            g = got[e].cpu().numpy()[sel]
+            for i in range(len(sel)):
+                assert normwise(g[i], q[key][i]) <= NORM_TOL, (key, e, sel[i])
+                assert np.abs(g[i] - q[key][i]).max() <= ELEM_TOL * np.abs(q[key][i]).max()
