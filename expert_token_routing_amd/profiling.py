@@ -251,6 +251,7 @@ def _main(argv=None):
         sources = {"k_gemm_up": "gemm_bf16.hip", "k_gemm_down": "gemm_bf16.hip",
                    "k_gemm_up_m128": "gemm_bf16.hip", "k_gemm_down_m128": "gemm_bf16.hip",
                    "k_gemm_up_dense": "gemm_bf16.hip", "k_gemm_down_dense": "gemm_bf16.hip",
+                   "k_gemm_up_f32": "gemm_f32.hip", "k_gemm_down_f32": "gemm_f32.hip",
                    "k_gate_bf16": "gate.hip", "k_sim_gram": "similarity.hip",
                    "k_dispatch": "rows.hip", "k_combine": "rows.hip",
                    "k_merge_slots": "rows.hip",

@@ -94,3 +94,9 @@ def scaled(w: Workload, T: int, name: str | None = None, **over) -> Workload:
     kw.update(T=T, name=name or f"{w.name}_T{T}")
     kw.update(over)
     return Workload(**kw)
+
+
+# The pruned OLMoE batch again under the TRAVERSE rule (same inputs).
+OLMOE_PRUNED_TRAVERSE = scaled(OLMOE_PRUNED, OLMOE_PRUNED.T, name=OLMOE_PRUNED.name + "_traverse",
+                               prune_rule=PRUNE_TRAVERSE)
+BY_NAME[OLMOE_PRUNED_TRAVERSE.name] = OLMOE_PRUNED_TRAVERSE
